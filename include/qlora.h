@@ -1,0 +1,190 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA quantized linear layer.
+ *
+ * The layer keeps a frozen weight W [rows = N = out_features, cols = K =
+ * in_features] in NF4 form and adds a trainable low-rank bypass:
+ *
+ *     y = x W^T + (alpha / r) (x A^T) B^T
+ *
+ * (26. QLoRA and 4bit Quantization, datawhalechina, Step 3; same formula in
+ * 22. QLoRA and 4bit Quantization, Step 4).  W is stored as 4-bit indices into
+ * a fixed 16-entry NF4 codebook (26. ..., Step 4 lookup table), one fp32
+ * absmax per block of 64 consecutive elements of the row-major flattened
+ * weight (Gemma lesson 09, sec. 9.2.1: each block is normalised to [-1, 1];
+ * 22. ..., engineering notes: 64 parameters share one scale), two indices per
+ * byte (22. ..., Step 4).  Optionally the block constants are quantised again
+ * to 8-bit integers (Gemma lesson 09, sec. 9.2.2 "double quantization";
+ * gufacode ch. 4: ~4.5 -> ~4.127 bits per parameter).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers (HIP memory on the current
+ *    device) unless a parameter says "host".  Row-major, densely packed.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Every call only enqueues work on that stream and returns; it never
+ *    synchronises.  Outputs are valid once the stream reaches the work.
+ *  - The caller owns and allocates every buffer, including the workspace.
+ *    The library never allocates or frees device memory and keeps no state
+ *    between calls apart from read-only kernel code.
+ *  - Outputs are overwritten (never accumulated into).
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a non-zero status and enqueues nothing.  A launch error
+ *    reported by the runtime returns QL_EHIP.  No C++ exception crosses the
+ *    ABI.  Inputs must be finite; NaN/Inf inputs give unspecified values.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QL_OK 0
+#define QL_EINVAL 1       /* null pointer, bad enum value, non-positive size */
+#define QL_ESHAPE 2       /* shapes inconsistent or unsupported (e.g. K % 64) */
+#define QL_EALIGN 3       /* a pointer lacks the 16-byte alignment required */
+#define QL_EUNSUPPORTED 4 /* valid request this build does not implement */
+#define QL_EWORKSPACE 5   /* workspace smaller than ql_workspace_bytes() */
+#define QL_EHIP 6         /* the HIP runtime reported an error */
+
+/* Element types of activations, weights to quantise, LoRA factors, outputs. */
+#define QL_F32 0
+#define QL_BF16 1
+
+/* Workspace queries (ql_workspace_bytes `op`). */
+#define QL_OP_QUANTIZE 0
+#define QL_OP_FWD 1
+#define QL_OP_BWD 2
+
+/* Fixed format parameters: 64 weights per NF4 block, 256 block constants per
+ * double-quantisation block. */
+#define QL_NF4_BLOCK 64
+#define QL_DQ_BLOCK 256
+
+/*
+ * An NF4-quantised weight.  n = rows * cols elements, nb = ceil(n / block)
+ * block constants, nb2 = ceil(nb / block2) second-level scales.
+ *
+ *  packed        uint8 [ceil(n/2)]: indices of the row-major flattened weight;
+ *                element 2j in bits 7..4 of byte j, element 2j+1 in bits 3..0;
+ *                for odd n the last low nibble is 0.
+ *  absmax        fp32 [nb]: per-block absolute maximum (double_quant == 0).
+ *  absmax_q      int8 [nb]: codes of the centred constants (double_quant == 1).
+ *  absmax_scale  fp32 [nb2]: one scale per block2 codes (double_quant == 1).
+ *  absmax_mean   fp32 [1]: per-tensor mean of the constants (double_quant == 1).
+ *  block, block2 must be QL_NF4_BLOCK and QL_DQ_BLOCK in this build.
+ *
+ * Dequantised element i (block b = i / block):
+ *   a'  = absmax[b]                                         (no double quant)
+ *   a'  = fmaf((float)absmax_q[b], absmax_scale[b / block2], absmax_mean[0])
+ *   w^_i = fp32 product codebook[index_i] * a'
+ * The struct itself lives in host memory; the pointers it holds are device
+ * pointers.  Unused pointers may be NULL.
+ */
+typedef struct ql_nf4 {
+  uint8_t *packed;
+  float *absmax;
+  int8_t *absmax_q;
+  float *absmax_scale;
+  float *absmax_mean;
+  int64_t rows;
+  int64_t cols;
+  int32_t block;
+  int32_t block2;
+  int32_t double_quant;
+  int32_t reserved; /* must be 0 */
+} ql_nf4;
+
+/*
+ * Host only.  Byte sizes of the five buffers of a rows x cols weight:
+ * bytes_out[0..4] = packed, absmax, absmax_q, absmax_scale, absmax_mean
+ * (entries a format does not use are 0).  Returns QL_OK or QL_EINVAL.
+ */
+int ql_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t bytes_out[5]);
+
+/*
+ * Host only.  Workspace bytes an operation needs (a multiple of 256).
+ *   QL_OP_QUANTIZE: M and r ignored, N x K is the weight (double-quant form;
+ *                   the single-level form needs none).
+ *   QL_OP_FWD / QL_OP_BWD: M tokens, N = out_features, K = in_features, rank r.
+ * Returns 0 for invalid sizes.  The workspace never scales with N * K.
+ */
+size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
+
+/*
+ * NF4-quantise a weight (Gemma lesson 09, sec. 9.2.1 and 9.2.2; 26. ...,
+ * Step 2 nearest codepoint).
+ *   w         device, q->rows * q->cols elements of w_dtype (QL_F32/QL_BF16),
+ *             16-byte aligned.
+ *   q         host struct describing device outputs: packed and either absmax
+ *             (double_quant 0) or absmax_q, absmax_scale, absmax_mean (1).
+ * Per block: a = max |w|; v = w / a (correctly rounded fp32 division); the
+ * index is the nearest codepoint of v, ties to the lower index; a zero block
+ * codes every element as index 7 (the exact zero).  Double quantisation:
+ * mu = mean of all a (exact sum, fp64 division, rounded to fp32);
+ * per 256 constants sigma = max|a - mu| / 127 (fp32), code =
+ * clamp(round-half-even((a - mu) / sigma), -127, 127), 0 when sigma == 0.
+ *   ws, ws_bytes  device workspace of ql_workspace_bytes(QL_OP_QUANTIZE, ...)
+ *                 bytes, 256-byte aligned (may be NULL/0 without double quant).
+ * Errors: QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP.
+ */
+int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/*
+ * Dequantise a whole NF4 weight to out (device, rows * cols elements of
+ * out_dtype; bf16 is the round-to-nearest-even of the fp32 product)
+ * (26. ..., Step 4: table[index] * scale; 22. ..., Step 3: restored to a
+ * 16-bit float for the matrix product).  out must be 16-byte aligned.
+ * Errors: QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
+ */
+int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream);
+
+/*
+ * Forward of the layer (26. ..., Step 3):
+ *     u = x A^T,   y = x W^^T + s u B^T,   s = fp32(alpha / r)
+ * with W^ dequantised on the fly, never stored.
+ *   x       device [M, K] act_dtype (QL_BF16, or QL_F32 for the fp32 path)
+ *   W       host struct, rows = N, cols = K, K % 64 == 0
+ *   A, B    device [r, K] and [N, r] of lora_dtype (QL_BF16 or QL_F32)
+ *   r       1..128;  alpha any finite value
+ *   y       device [M, N] act_dtype (overwritten)
+ *   u_save  device [M, r] fp32 receiving u, or NULL
+ *   ws      device workspace of ql_workspace_bytes(QL_OP_FWD, M, N, K, r)
+ * bf16 activations multiply in bf16 on the matrix cores with fp32
+ * accumulation; fp32 activations compute entirely in fp32.
+ * All device pointers 16-byte aligned.
+ */
+int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                     const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
+                     void *y, float *u_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the layer (22. QLoRA and 4bit Quantization, Step 1: the
+ * gradient reaches x and the LoRA factors; the frozen base gets none):
+ *     u = x A^T (or u_saved),  g = s dy B
+ *     dB = s dy^T u   [N, r] fp32
+ *     dA = g^T x      [r, K] fp32
+ *     dx = dy W^ + g A [M, K] act_dtype   (skipped when dx == NULL)
+ * dy [M, N] act_dtype.  Other arguments as for qlora_linear_fwd.  No
+ * gradient buffer of size N x K exists anywhere.
+ */
+int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                     const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                     int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                     float *dB, void *ws, size_t ws_bytes, void *stream);
+
+/* Host only: a static string describing a status code. */
+const char *ql_strerror(int status);
+
+/* Host only: ABI version (major * 100 + minor). */
+int ql_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,260 @@
+// api.hip -- the C ABI declared in include/qlora.h: argument checks on the
+// host, workspace carve-up, and the choice of kernels.  No allocation, no
+// synchronisation, no state.
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dtype(int32_t d) { return (d == QL_F32 || d == QL_BF16) ? QL_OK : QL_EINVAL; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validates the quantised-weight descriptor (pointers it must hold for its
+// format, fixed block sizes, alignment of the packed array).
+int check_nf4(const ql_nf4 *q) {
+  if (!q) return QL_EINVAL;
+  if (q->rows <= 0 || q->cols <= 0) return QL_EINVAL;
+  if (q->double_quant != 0 && q->double_quant != 1) return QL_EINVAL;
+  if (q->reserved != 0) return QL_EINVAL;
+  if (q->block != QL_NF4_BLOCK || q->block2 != QL_DQ_BLOCK) return QL_EUNSUPPORTED;
+  if (!q->packed) return QL_EINVAL;
+  if (q->double_quant) {
+    if (!q->absmax_q || !q->absmax_scale || !q->absmax_mean) return QL_EINVAL;
+  } else if (!q->absmax) {
+    return QL_EINVAL;
+  }
+  if (!aligned16(q->packed)) return QL_EALIGN;
+  return QL_OK;
+}
+
+BlockScales scales_of(const ql_nf4 *q) {
+  BlockScales sc;
+  sc.absmax = q->double_quant ? nullptr : q->absmax;
+  sc.q = q->absmax_q;
+  sc.sigma = q->absmax_scale;
+  sc.mu = q->absmax_mean;
+  return sc;
+}
+
+// Workspace layouts (offsets are multiples of 256 bytes).
+struct QuantWs {
+  size_t absmax, partial, total;
+};
+QuantWs quant_ws(int64_t n) {
+  const int64_t nb = ceil_div(n, QL_NF4_BLOCK);
+  QuantWs w;
+  w.absmax = 0;
+  w.partial = round_up((size_t)nb * 4);
+  w.total = w.partial + round_up(dq_partial_count(nb) * 8);
+  return w;
+}
+
+struct FwdWs {
+  size_t u, rows, total;
+};
+FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  (void)N;
+  FwdWs w;
+  w.u = 0;
+  w.rows = round_up((size_t)M * r * 4);
+  w.total = w.rows + round_up(lora_rows_partial_floats(M, K, r) * 4);
+  return w;
+}
+
+struct BwdWs {
+  size_t u, g, rows, cols, total;
+};
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdWs w;
+  w.u = 0;
+  w.g = round_up((size_t)M * r * 4);
+  w.rows = w.g + round_up((size_t)M * r * 4);
+  size_t rows_f = lora_rows_partial_floats(M, K, r);
+  size_t rows_f2 = lora_rows_partial_floats(M, N, r);
+  if (rows_f2 > rows_f) rows_f = rows_f2;
+  w.cols = w.rows + round_up(rows_f * 4);
+  size_t cols_f = lora_cols_partial_floats(M, K, r);
+  size_t cols_f2 = lora_cols_partial_floats(M, N, r);
+  if (cols_f2 > cols_f) cols_f = cols_f2;
+  w.total = w.cols + round_up(cols_f * 4);
+  return w;
+}
+
+int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const void *A,
+                        const void *B, int32_t lora_dtype, int32_t r, float alpha) {
+  int st = check_nf4(W);
+  if (st) return st;
+  if (check_dtype(act_dtype) || check_dtype(lora_dtype)) return QL_EINVAL;
+  if (M <= 0 || r <= 0) return QL_EINVAL;
+  if (r > 128) return QL_EUNSUPPORTED;
+  if (W->cols % QL_NF4_BLOCK != 0) return QL_ESHAPE;
+  if (!A || !B) return QL_EINVAL;
+  if (!aligned16(A) || !aligned16(B)) return QL_EALIGN;
+  if (!(alpha == alpha) || alpha - alpha != 0.0f) return QL_EINVAL;  // not finite
+  return QL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ql_abi_version(void) { return 100; }
+
+const char *ql_strerror(int status) {
+  switch (status) {
+    case QL_OK: return "ok";
+    case QL_EINVAL: return "invalid argument (null pointer, bad enum or non-positive size)";
+    case QL_ESHAPE: return "unsupported or inconsistent shape";
+    case QL_EALIGN: return "pointer not 16-byte aligned";
+    case QL_EUNSUPPORTED: return "unsupported configuration";
+    case QL_EWORKSPACE: return "workspace too small";
+    case QL_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ql_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t bytes_out[5]) {
+  if (!bytes_out || rows <= 0 || cols <= 0 || (double_quant != 0 && double_quant != 1))
+    return QL_EINVAL;
+  const int64_t n = rows * cols;
+  const int64_t nb = ceil_div(n, QL_NF4_BLOCK);
+  const int64_t nb2 = ceil_div(nb, QL_DQ_BLOCK);
+  bytes_out[0] = (size_t)((n + 1) / 2);
+  bytes_out[1] = double_quant ? 0 : (size_t)nb * 4;
+  bytes_out[2] = double_quant ? (size_t)nb : 0;
+  bytes_out[3] = double_quant ? (size_t)nb2 * 4 : 0;
+  bytes_out[4] = double_quant ? 4 : 0;
+  return QL_OK;
+}
+
+size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
+  switch (op) {
+    case QL_OP_QUANTIZE:
+      if (N <= 0 || K <= 0) return 0;
+      return quant_ws(N * K).total;
+    case QL_OP_FWD:
+      if (M <= 0 || N <= 0 || K <= 0 || r <= 0 || r > 128) return 0;
+      return fwd_ws(M, N, K, r).total;
+    case QL_OP_BWD:
+      if (M <= 0 || N <= 0 || K <= 0 || r <= 0 || r > 128) return 0;
+      return bwd_ws(M, N, K, r).total;
+    default:
+      return 0;
+  }
+}
+
+int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size_t ws_bytes,
+                 void *stream) {
+  int st = check_nf4(q);
+  if (st) return st;
+  if (!w || check_dtype(w_dtype)) return QL_EINVAL;
+  if (!aligned16(w)) return QL_EALIGN;
+  const int64_t n = q->rows * q->cols;
+  const int64_t nb = ceil_div(n, QL_NF4_BLOCK);
+  hipStream_t s = (hipStream_t)stream;
+  if (!q->double_quant) return launch_nf4_quantize(w, w_dtype, n, q->packed, q->absmax, s);
+  const QuantWs L = quant_ws(n);
+  if (!ws || ws_bytes < L.total) return QL_EWORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
+  uint8_t *base = (uint8_t *)ws;
+  float *absmax = (float *)(base + L.absmax);
+  double *partial = (double *)(base + L.partial);
+  st = launch_nf4_quantize(w, w_dtype, n, q->packed, absmax, s);
+  if (st) return st;
+  return launch_double_quant(absmax, nb, partial, q->absmax_q, q->absmax_scale, q->absmax_mean, s);
+}
+
+int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) {
+  int st = check_nf4(q);
+  if (st) return st;
+  if (!out || check_dtype(out_dtype)) return QL_EINVAL;
+  if (!aligned16(out)) return QL_EALIGN;
+  return launch_nf4_dequantize(q->packed, q->rows * q->cols, scales_of(q), out, out_dtype,
+                               (hipStream_t)stream);
+}
+
+int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                     const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
+                     void *y, float *u_save, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
+  if (st) return st;
+  if (!x || !y) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || (u_save && !aligned16(u_save))) return QL_EALIGN;
+  const int64_t N = W->rows, K = W->cols;
+  const FwdWs L = fwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < L.total) return QL_EWORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
+  uint8_t *base = (uint8_t *)ws;
+  float *u = u_save ? u_save : (float *)(base + L.u);
+  float *rows_partial = (float *)(base + L.rows);
+  hipStream_t s = (hipStream_t)stream;
+  const float sc_lora = alpha / (float)r;
+  const BlockScales sc = scales_of(W);
+  st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
+  if (st) return st;
+  if (act_dtype == QL_BF16) {
+    if (M <= 16)
+      return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
+                             sc_lora, (uint16_t *)y, s);
+    return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
+                           sc_lora, (uint16_t *)y, s);
+  }
+  return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
+                           s);
+}
+
+int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                     const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                     int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                     float *dB, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
+  if (st) return st;
+  if (!dy || !x || !dA || !dB) return QL_EINVAL;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(dA) || !aligned16(dB) ||
+      (dx && !aligned16(dx)) || (u_saved && !aligned16(u_saved)))
+    return QL_EALIGN;
+  const int64_t N = W->rows, K = W->cols;
+  const BwdWs L = bwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < L.total) return QL_EWORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
+  uint8_t *base = (uint8_t *)ws;
+  float *u = (float *)(base + L.u);
+  float *g = (float *)(base + L.g);
+  float *rows_partial = (float *)(base + L.rows);
+  float *cols_partial = (float *)(base + L.cols);
+  hipStream_t s = (hipStream_t)stream;
+  const float sc_lora = alpha / (float)r;
+  const BlockScales sc = scales_of(W);
+  if (u_saved) {
+    u = const_cast<float *>(u_saved);
+  } else {
+    st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
+    if (st) return st;
+  }
+  // g = s dy B: Q(j, c) = B[c][j]
+  st = launch_lora_rows_ws(dy, act_dtype, M, N, B, lora_dtype, 1, r, r, sc_lora, g, rows_partial, s);
+  if (st) return st;
+  // dB[n][j] = s sum_m dy[m][n] u[m][j]
+  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s);
+  if (st) return st;
+  // dA[j][k] = sum_m g[m][j] x[m][k]
+  st = launch_lora_cols(g, M, r, x, act_dtype, K, 1.0f, false, dA, cols_partial, s);
+  if (st) return st;
+  if (!dx) return QL_OK;
+  if (act_dtype == QL_BF16 && N % 64 == 0 && K % 128 == 0)
+    return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
+                          (uint16_t *)dx, s);
+  return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
+}
+
+}  // extern "C"

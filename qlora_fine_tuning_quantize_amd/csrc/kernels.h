@@ -1,0 +1,54 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (one per .hip file).
+// Each launcher enqueues on `stream`, never synchronises, and returns a
+// QL_* status.  Shapes and pointers are validated by the C ABI layer before
+// a launcher is called.
+#pragma once
+
+#include "common.h"
+
+namespace qlora {
+
+// quant.hip
+int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, uint8_t *packed, float *absmax,
+                        hipStream_t stream);
+size_t dq_partial_count(int64_t nb);
+int launch_double_quant(const float *absmax, int64_t nb, double *partial, int8_t *q, float *sigma,
+                        float *mean_out, hipStream_t stream);
+int launch_nf4_dequantize(const uint8_t *packed, int64_t n, BlockScales sc, void *out,
+                          int out_dtype, hipStream_t stream);
+
+// lora.hip: the rank-r products around the base matrix product.
+//   rows:  out[m][j] = scale * sum_c P[m][c] * Q(j, c)   (u = x A^T, g = s dy B)
+//          Q(j, c) = Q[j*ldq_j + c*ldq_c]
+//   cols:  out(j, c) = scale * sum_m R[m][j] * P[m][c]    (dA = g^T x, dB = s dy^T u)
+size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r);
+int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const void *Q,
+                        int q_dtype, int64_t ldq_j, int64_t ldq_c, int32_t r, float scale,
+                        float *out, float *partial, hipStream_t stream);
+size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r);
+int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
+                     float scale, bool out_c_major, float *out, float *partial,
+                     hipStream_t stream);
+
+// simple.hip: fp32-accumulating tiled kernels for any activation dtype.
+int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
+                      BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,
+                      int lora_dtype, int32_t r, float s, void *y, hipStream_t stream);
+int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *packed,
+                     BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
+                     int lora_dtype, int32_t r, void *dx, hipStream_t stream);
+
+// gemv.hip: decode-sized forward (M <= 16, bf16 activations).
+int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
+                    int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
+                    float s, uint16_t *y, hipStream_t stream);
+
+// gemm.hip: matrix-core forward and input-gradient products (bf16).
+int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
+                    int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
+                    float s, uint16_t *y, hipStream_t stream);
+int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
+                   int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
+                   uint16_t *dx, hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,35 @@
+"""Small helpers shared by the tests (no arithmetic of the layer itself)."""
+import numpy as np
+import torch
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 tensor -> numpy uint16 bit patterns (host copy)."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Host numpy view of a tensor; bf16 becomes uint16 bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.contiguous().cpu().numpy()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max(max |ref|, rms(ref)): the bf16 tolerance measure
+    (plain relative error is ill-posed where ref cancels to ~0)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    denom = max(float(np.max(np.abs(ref))), float(np.sqrt(np.mean(ref ** 2))), 1e-30)
+    return float(np.max(np.abs(got - ref))) / denom
+
+
+BF16_TOL = 2e-2        # bf16 activations: max rel error against the fp64 oracle
+F32_ATOL = 1e-5        # fp32 activations: |d| <= atol + rtol |ref| (allclose defaults)
+F32_RTOL = 1e-5
+
+
+def assert_f32_close(got: np.ndarray, ref: np.ndarray, what: str):
+    excess = np.abs(np.asarray(got, np.float64) - ref) - (F32_ATOL + F32_RTOL * np.abs(ref))
+    assert np.all(excess <= 0), f"{what}: max excess over atol+rtol|ref| = {excess.max():.3e}"

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact for packed indices, block constants, double-quantisation codes,
+scales, mean and dequantised values; within the stated tolerance for the
+layer's outputs and gradients (bf16: max |d| / max(max|ref|, rms ref) <=
+2e-2 against the fp64 oracle; fp32: |d| <= 1e-5 + 1e-5 |ref|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import qlora_fine_tuning_quantize_amd as q
+import synth_inputs as si
+from tests.helpers import BF16_TOL, assert_f32_close, host, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# quantisation / double quantisation / dequantisation: bit-exact
+# ---------------------------------------------------------------------------
+def _check_quant(orc, w_cpu: torch.Tensor, dq: bool):
+    Wq = q.nf4_quantize(w_cpu.to(DEV).contiguous(), double_quant=dq)
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(w_cpu).reshape(-1), double_quant=dq)
+    np.testing.assert_array_equal(host(Wq.packed)[:st["packed"].size], st["packed"])
+    if dq:
+        np.testing.assert_array_equal(host(Wq.absmax_q)[:st["absmax_q"].size], st["absmax_q"])
+        np.testing.assert_array_equal(host(Wq.absmax_scale)[:st["absmax_scale"].size].view(np.uint32),
+                                      st["absmax_scale"].view(np.uint32))
+        assert host(Wq.absmax_mean)[:1].view(np.uint32)[0] == np.float32(st["absmax_mean"]).view(np.uint32)
+    else:
+        np.testing.assert_array_equal(host(Wq.absmax)[:st["absmax"].size].view(np.uint32),
+                                      st["absmax"].view(np.uint32))
+    ref32 = orc.dequantize(st)
+    got32 = host(q.nf4_dequantize(Wq, torch.float32)).reshape(-1)
+    np.testing.assert_array_equal(got32.view(np.uint32), ref32.view(np.uint32))
+    got16 = host(q.nf4_dequantize(Wq, torch.bfloat16)).reshape(-1)
+    np.testing.assert_array_equal(got16, orc.round_bf16(ref32))
+    return Wq, st
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 7), (3, 5), (1, 63), (1, 64), (1, 65), (7, 129),
+                                       (64, 64), (256, 256), (300, 1000), (33, 64 * 257)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dq", [False, True])
+def test_quant_dequant_bit_exact(orc, rows, cols, dtype, dq):
+    _say(f"quant rows={rows} cols={cols} dtype={dtype} dq={dq}")
+    w = si.normal((rows, cols), 0.02, seed=rows * 131 + cols, dtype=dtype)
+    flat = w.view(-1)
+    if flat.numel() >= 256:
+        flat[64:128] = 0                       # an all-zero block
+        flat[5] = 0.4                          # 20-sigma outliers
+        flat[200] = -0.4
+    _check_quant(orc, w, dq)
+
+
+def test_quant_subnormal_and_signed_zero_blocks(orc):
+    w = torch.zeros(4 * 64, dtype=torch.float32)
+    w[0:64] = torch.linspace(-1e-39, 1e-39, 64)        # fp32 subnormals only
+    w[64:128] = -0.0
+    w[128:192] = torch.linspace(-3.0, 3.0, 64)
+    w[192] = 1e-30
+    for dq in (False, True):
+        _check_quant(orc, w.view(4, 64), dq)
+        _check_quant(orc, w.to(torch.bfloat16).view(4, 64), dq)
+
+
+def _bf16_sweep_weights(a_scale_exp: int) -> torch.Tensor:
+    """Blocks of 64 bf16 values: element 0 is the block maximum a (128 bf16
+    mantissas times 2**a_scale_exp), the other 63 run through every finite
+    bf16 value w with |w| <= a, both signs.  Covers every (w, a) ratio class
+    of bf16 inputs."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)  # all finite non-negative bf16 patterns
+    vals = (bits << 16).view(np.float32)
+    blocks = []
+    for m in range(128):
+        a = np.float32((1 + m / 128) * 2.0 ** a_scale_exp)
+        ws = vals[vals <= a]
+        ws = np.concatenate([ws, -ws[ws > 0]])
+        n_blk = (ws.size + 62) // 63
+        pad = np.zeros(n_blk * 63, dtype=np.float32)
+        pad[:ws.size] = ws
+        blk = np.concatenate([np.full((n_blk, 1), a, dtype=np.float32), pad.reshape(n_blk, 63)], 1)
+        blocks.append(blk)
+    allw = np.concatenate(blocks).reshape(-1)
+    return torch.from_numpy(allw).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("a_exp", [0, -20, 7])
+def test_quant_exhaustive_bf16_ratios(orc, a_exp):
+    w = _bf16_sweep_weights(a_exp)
+    _say(f"bf16 sweep a_exp={a_exp}: {w.numel()} elements")
+    Wq = q.nf4_quantize(w.to(DEV).view(1, -1), double_quant=False)
+    torch.cuda.synchronize()
+    packed, absmax = orc.quantize(host(w))
+    np.testing.assert_array_equal(host(Wq.packed)[:packed.size], packed)
+    np.testing.assert_array_equal(host(Wq.absmax)[:absmax.size], absmax)
+
+
+# ---------------------------------------------------------------------------
+# the layer: forward and backward
+# ---------------------------------------------------------------------------
+def _layer_case(orc, M, N, K, r, dq, act, lora, alpha=32.0, seed_cfg=90, dy_ones=False,
+                rows=None):
+    t = si.linear_inputs(seed_cfg, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora,
+                         sub=M + N + K + r)
+    if dy_ones:
+        t["dy"] = torch.ones((M, N), dtype=act)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=dq)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], alpha, u_save=u)
+    dx, dA, dB = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], alpha)
+    dx2, dA2, dB2 = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], alpha, u_saved=u)
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(t["W"]), double_quant=dq)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    xs = host(t["x"]) if rows is None else host(t["x"])[rows]
+    y_ref, u_ref = orc.linear_fwd(xs, w_hat, host(t["A"]), host(t["B"]), alpha, r)
+    dx_ref, dA_ref, dB_ref = orc.linear_bwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]),
+                                            host(t["dy"]), alpha, r, rows=rows)
+    sel = slice(None) if rows is None else rows
+    got = {"y": y.float().cpu().numpy()[sel], "u": u.cpu().numpy()[sel],
+           "dx": dx.float().cpu().numpy()[sel], "dA": dA.cpu().numpy(), "dB": dB.cpu().numpy()}
+    ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": dA_ref, "dB": dB_ref}
+    # the saved-u backward is the same computation
+    np.testing.assert_array_equal(dA2.cpu().numpy(), got["dA"])
+    np.testing.assert_array_equal(dB2.cpu().numpy(), got["dB"])
+    np.testing.assert_array_equal(dx2.float().cpu().numpy()[sel], got["dx"])
+    return got, ref
+
+
+@pytest.mark.parametrize("dy_ones", [False, True])
+def test_layer_fp32_small_config(orc, dy_ones):
+    """fp32 compute: W 256x256, x 4x256, r 8, alpha 16, no double quant."""
+    c = si.SMALL_FP32
+    got, ref = _layer_case(orc, c["M"], c["N"], c["K"], c["r"], False, torch.float32,
+                           torch.float32, alpha=c["alpha"], seed_cfg=c["config"], dy_ones=dy_ones)
+    for k in ("y", "u", "dx", "dA", "dB"):
+        assert_f32_close(got[k], ref[k], k)
+    if dy_ones:  # the pages' .sum().backward(): identical dx rows and dB rows
+        assert np.all(got["dx"] == got["dx"][0:1])
+
+
+BF16_CASES = [
+    # M, N, K, r, dq, lora dtype         (path exercised)
+    (1, 256, 256, 8, True, torch.bfloat16),     # decode GEMV
+    (3, 200, 320, 16, False, torch.float32),    # GEMV, ragged N, fp32 LoRA
+    (16, 384, 1024, 16, True, torch.bfloat16),  # GEMV at M = 16
+    (17, 128, 128, 16, True, torch.bfloat16),   # smallest matrix-core GEMM
+    (300, 384, 384, 16, True, torch.bfloat16),  # ragged M over two token tiles
+    (300, 200, 320, 8, False, torch.float32),   # ragged N: guarded fwd tile, tiled dx
+    (512, 256, 640, 64, True, torch.bfloat16),  # r = 64
+    (257, 128, 128, 128, True, torch.bfloat16), # r = 128
+    (64, 64, 64, 5, True, torch.bfloat16),      # rank not a multiple of 8
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,dq,lora", BF16_CASES)
+def test_layer_bf16_parity(orc, M, N, K, r, dq, lora):
+    _say(f"layer bf16 M={M} N={N} K={K} r={r} dq={dq} lora={lora}")
+    got, ref = _layer_case(orc, M, N, K, r, dq, torch.bfloat16, lora)
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_config_full_size(orc, M):
+    """Llama-3-8B attention projection: W 4096x4096 NF4 + double quant,
+    r 16, alpha 32, bf16; forward only, every output checked."""
+    c = si.DECODE
+    N, K, r = c["N"], c["K"], c["r"]
+    t = si.linear_inputs(c["config"], M, N, K, r, with_dy=False)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=True)
+    y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], c["alpha"])
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(t["W"]), double_quant=True)
+    np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
+    np.testing.assert_array_equal(host(W.absmax_q)[:st["absmax_q"].size], st["absmax_q"])
+    y_ref, _ = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
+                              host(t["B"]), c["alpha"], r)
+    e = rel_err(y.float().cpu().numpy(), y_ref)
+    _say(f"decode M={M}: rel err {e:.2e}")
+    assert e <= BF16_TOL
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_mlp8b_config_full_size_sampled(orc, proj):
+    """8B-shaped MLP projection at M = 2048 tokens, r 16, alpha 32, NF4 +
+    double quant: y and dx on 64 sampled token rows, dA and dB in full."""
+    c = si.MLP_8B
+    N, K = c["projs"][proj]
+    M, r = c["M"], c["r"]
+    rows = np.sort(np.random.default_rng(3).choice(M, 64, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    _say(f"mlp8b {proj}: M={M} N={N} K={K}")
+    got, ref = _layer_case(orc, M, N, K, r, True, torch.bfloat16, torch.bfloat16,
+                           alpha=c["alpha"], seed_cfg=c["config"], rows=rows)
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
