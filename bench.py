@@ -1,0 +1,287 @@
+"""Benchmark of the QLoRA quantized linear layer on one MI355X.
+
+Step = one training pass of an 8B-shaped MLP's three QLoRA projections
+(gate and up 14336x4096, down 4096x14336; NF4 + double quantisation),
+2048 tokens, LoRA r=16 alpha=32: forward (u, y) and backward (dx, dA, dB)
+for each projection, inputs resident in HBM.  The headline value is the
+step's algorithmic TFLOP/s (4MNK + 6Mr(K+N) per projection).
+
+In the same run (reported beside the step):
+  roofline     the forward GEMM timed alone in a loop with HIP events
+  decode_gemv  Llama-3-8B attention projection (4096x4096) at M = 1, 4, 16,
+               packed-weight GB/s, rotating over 64 weight copies so the
+               256 MB Infinity Cache cannot hold them
+  quantize     NF4 + double quantisation and full dequantisation of an
+               8B-shaped weight set, GB/s and bits/param
+  cpu_baseline the CPU oracle on a bounded sample of the step (host cores)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s (%MFMA peak); decode GEMV packed-weight GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ROOFLINE_KERNEL = "k_gemm_fwd"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_fwd_mlp8b_gate.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def layer_flops(M, N, K, r):
+    return 4 * M * N * K + 6 * M * r * (K + N)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "qlora_fine_tuning_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, iters, warmup):
+    """Average ms per call of fn() over `iters` calls, HIP events on the
+    current stream, synchronised on both sides."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="only the training step")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's data-parallel sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import qlora_fine_tuning_quantize_amd as q
+    import synth_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = si.MLP_8B
+    M, r, alpha = c["M"], c["r"], c["alpha"]
+
+    # ---------------- training step: gate, up, down -----------------------
+    projs = []
+    for pi, (name, (N, K)) in enumerate(c["projs"].items()):
+        t = si.linear_inputs(c["config"], M, N, K, r, sub=pi, device=dev)
+        W = q.nf4_quantize(t["W"], double_quant=True)
+        del t["W"]
+        p = dict(name=name, N=N, K=K, W=W, x=t["x"], dy=t["dy"], A=t["A"], B=t["B"],
+                 y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 u=torch.empty((M, r), dtype=torch.float32, device=dev),
+                 dx=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                 dA=torch.empty((r, K), dtype=torch.float32, device=dev),
+                 dB=torch.empty((N, r), dtype=torch.float32, device=dev),
+                 wsf=q.workspace(q.QL_OP_FWD, M, N, K, r, dev),
+                 wsb=q.workspace(q.QL_OP_BWD, M, N, K, r, dev))
+        projs.append(p)
+    torch.cuda.synchronize()
+    log("inputs ready")
+
+    def step():
+        for p in projs:
+            q.qlora_linear_fwd(p["x"], p["W"], p["A"], p["B"], alpha, y=p["y"], u_save=p["u"],
+                               ws=p["wsf"])
+            q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha, u_saved=p["u"],
+                               dx=p["dx"], dA=p["dA"], dB=p["dB"], ws=p["wsb"])
+
+    flops_step = sum(layer_flops(M, p["N"], p["K"], r) for p in projs)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms  {tflops:.1f} TFLOP/s  (wall {wall:.2f} s for {args.steps} steps)")
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "8B-shaped MLP QLoRA training step: gate+up 14336x4096, down "
+                               "4096x14336, NF4 block 64 + 8-bit double quant, 2048 tokens, "
+                               "LoRA r=16 alpha=32, forward + backward (dx, dA, dB)",
+                   "tokens": M, "rank": r, "alpha": alpha, "flop_per_step": flops_step},
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+    }
+
+    # ---------------- roofline: the forward GEMM alone ------------------------
+    g = projs[0]
+    fwd_ms = timed(lambda: q.qlora_linear_fwd(g["x"], g["W"], g["A"], g["B"], alpha, y=g["y"],
+                                              u_save=g["u"], ws=g["wsf"]), 50, 5)
+    fwd_flops = 2 * M * g["N"] * g["K"] + 2 * M * r * (g["K"] + g["N"])
+    ach = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha") == kernel_source_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+    result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                          "traffic": traffic, "kernel": ROOFLINE_KERNEL,
+                          "launch": "qlora_linear_fwd gate 2048x14336x4096 (u pre-pass + GEMM)",
+                          "ms_per_launch": round(fwd_ms, 4), "flop_per_launch": fwd_flops}
+    log(f"fwd gate {fwd_ms:.3f} ms {ach:.1f} TFLOP/s")
+    del projs, g
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        result["decode_gemv"] = bench_decode(q, si, dev)
+        result["quantize"] = bench_quantize(q, si, dev)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(si, M, r, alpha)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(q, si, dev, copies=64, iters=1000):
+    c = si.DECODE
+    N, K, r, alpha = c["N"], c["K"], c["r"], c["alpha"]
+    t = si.linear_inputs(c["config"], 16, N, K, r, with_dy=False, device=dev)
+    Ws = []
+    for i in range(copies):
+        w = t["W"] if i == 0 else si.normal((N, K), 0.02, si.seed_of(2, 1, i), device=dev)
+        Ws.append(q.nf4_quantize(w, double_quant=True))
+    del w
+    packed_bytes = sum(q.nf4_sizes(N, K, True))
+    out = {"workload": "Llama-3-8B attention projection 4096x4096 NF4 + double quant, r=16, "
+                       "alpha=32, bf16, forward only; 64 rotating weight copies",
+           "unit": "GB/s", "packed_weight_bytes": packed_bytes}
+    for M in c["Ms"]:
+        x = t["x"][:M].contiguous()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
+        state = {"i": 0}
+
+        def call():
+            W = Ws[state["i"] % copies]
+            state["i"] += 1
+            q.qlora_linear_fwd(x, W, t["A"], t["B"], alpha, y=y, ws=ws)
+
+        ms = timed(call, iters, 50)
+        gbs = packed_bytes / (ms * 1e-3) / 1e9
+        out[f"M{M}"] = {"us_per_call": round(ms * 1e3, 3), "packed_GBps": round(gbs, 1),
+                        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s packed")
+    del Ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_quantize(q, si, dev):
+    """8B-shaped weight set (32 layers x q,k,v,o,gate,up,down), bf16 N(0,0.02)
+    with 0.1% outliers at 20 sigma: quantise (+ double quant) and dequantise
+    every tensor once per pass."""
+    cfg = si.WEIGHTSET_8B
+    ws_list, q_list, out_list = [], [], []
+    n_total = 0
+    for layer in range(cfg["layers"]):
+        for name in cfg["shapes"]:
+            w = si.weightset_tensor(layer, name, device=dev)
+            ws_list.append(w)
+            q_list.append(q.NF4Weight.empty(w.shape[0], w.shape[1], True, dev))
+            n_total += w.numel()
+    maxn = max(w.numel() for w in ws_list)
+    wsq = q.workspace(q.QL_OP_QUANTIZE, 0, 1, maxn, 0, dev)
+    deq = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"weight set ready: {n_total} params")
+
+    def quant_all():
+        for w, qq in zip(ws_list, q_list):
+            q.nf4_quantize(w, double_quant=True, out=qq, ws=wsq)
+
+    def dequant_all():
+        for qq in q_list:
+            q.nf4_dequantize(qq, out=deq[:qq.rows * qq.cols].view(qq.rows, qq.cols))
+
+    qms = timed(quant_all, 3, 1)
+    dms = timed(dequant_all, 3, 1)
+    stored = sum(qq.storage_bytes() for qq in q_list)
+    q_bytes = 2 * n_total + stored
+    d_bytes = stored + 2 * n_total
+    out = {"workload": "8B-shaped weight set, 32 layers x {q,k,v,o,gate,up,down}, bf16 "
+                       "N(0,0.02) + 0.1% outliers at 20 sigma, NF4 + double quant",
+           "params": n_total, "bits_per_param": round(8 * stored / n_total, 5),
+           "quantize_ms": round(qms, 3), "quantize_GBps": round(q_bytes / (qms * 1e-3) / 1e9, 1),
+           "dequantize_ms": round(dms, 3),
+           "dequantize_GBps": round(d_bytes / (dms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+    out["quantize_hbm_frac"] = round(out["quantize_GBps"] / PEAK_HBM_GBS, 4)
+    out["dequantize_hbm_frac"] = round(out["dequantize_GBps"] / PEAK_HBM_GBS, 4)
+    log(f"quantize {qms:.2f} ms ({out['quantize_GBps']} GB/s), dequantize {dms:.2f} ms "
+        f"({out['dequantize_GBps']} GB/s), {out['bits_per_param']} bits/param")
+    del ws_list, q_list, deq
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(si, M, r, alpha, target_s=10.0):
+    """The CPU oracle on a bounded sample: the gate projection's forward and
+    backward (dequantisation included) for a slice of the token batch sized
+    so that the run takes about target_s seconds on this host; TFLOP/s."""
+    from oracle import oracle as orc
+    c = si.MLP_8B
+    N, K = c["projs"]["gate"]
+    bits = lambda v: v.contiguous().view(torch.int16).numpy().view("uint16")
+
+    def run(rows):
+        t = si.linear_inputs(c["config"], rows, N, K, r, sub=0)
+        Wh, xh, Ah, Bh, dyh = (bits(t[k]) for k in ("W", "x", "A", "B", "dy"))
+        st = orc.quantize_nf4(Wh, double_quant=True)
+        t0 = time.perf_counter()
+        w_hat = orc.dequantize(st).reshape(N, K)
+        orc.linear_fwd(xh, w_hat, Ah, Bh, alpha, r)
+        orc.linear_bwd(xh, w_hat, Ah, Bh, dyh, alpha, r)
+        return time.perf_counter() - t0
+
+    dt = run(64)
+    rows = int(min(M, max(64, 64 * target_s / max(dt, 1e-3))) // 64 * 64)
+    if rows > 64:
+        dt = run(rows)
+    flops = layer_flops(rows, N, K, r)
+    log(f"cpu oracle: {dt:.2f} s for {flops / 1e9:.1f} GFLOP ({rows} tokens)")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"gate projection 14336x4096, {rows} of the {M} tokens, forward + backward "
+                      f"including dequantisation, fp64 accumulation, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
