@@ -200,15 +200,21 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
+  if (act_dtype == QL_BF16 && M <= 16) {
+    // decode: the GEMV sums the slice partials of u itself; u is reduced
+    // separately only when the caller wants it saved
+    int S = 0;
+    st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u_save,
+                             rows_partial, s, &S);
+    if (st) return st;
+    return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, rows_partial, S, B,
+                           lora_dtype, r, sc_lora, (uint16_t *)y, s);
+  }
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
   if (st) return st;
-  if (act_dtype == QL_BF16) {
-    if (M <= 16)
-      return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
-                             sc_lora, (uint16_t *)y, s);
+  if (act_dtype == QL_BF16)
     return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
                            sc_lora, (uint16_t *)y, s);
-  }
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
 }
@@ -251,7 +257,7 @@ int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M
   st = launch_lora_cols(g, M, r, x, act_dtype, K, 1.0f, false, dA, cols_partial, s);
   if (st) return st;
   if (!dx) return QL_OK;
-  if (act_dtype == QL_BF16 && N % 64 == 0 && K % 128 == 0)
+  if (act_dtype == QL_BF16 && gemm_dx_supported(N, K))
     return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
                           (uint16_t *)dx, s);
   return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);

@@ -46,13 +46,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Two fp32 -> packed bf16x2 (low half = a), round to nearest even
-// (v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even, as one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 ha = (__bf16)a;
-  __bf16 hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {

@@ -12,11 +12,18 @@
 // as extra 16-deep MFMA steps (u and g are fp32 in memory and are rounded to
 // bf16 for those steps).
 //
-// Tiles: 256 (tokens) x 128 (outputs) per workgroup, contraction step 64
-// (= one NF4 block of every weight row in the forward), 8 waves of 64 x 64.
-// LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r is stored at
-// position c ^ (r & 7) so that 8 consecutive rows read at the same logical
-// chunk hit 8 different bank groups.
+// Tiles: 256 tokens x BN outputs per workgroup (BN = 256 or 128), contraction
+// step 64 (= one NF4 block of every weight row in the forward), 8 waves laid
+// out 2 (tokens) x 4 (outputs), each owning a 128 x BN/4 block of 32x32
+// accumulator tiles.  LDS is double-buffered: while the matrix cores work on
+// step k, the registers loaded during step k-1 (step k+1's tiles) are written
+// to the other buffer and step k+2's global loads are issued; one barrier
+// per step.  LDS rows are 64 bf16 = 8 chunks of 16 bytes.  gfx950 serves a
+// 16-byte-per-lane LDS read 16 lanes per pass over 64 banks (256 bytes), so
+// the 16 rows one pass touches must land on 16 distinct 16-byte bank slots:
+// chunk c of row r is stored at position c ^ ((r >> 1) & 7); with the row
+// parity choosing the bank half this spreads any 16 consecutive rows read at
+// the same logical chunk over all 64 banks.
 //
 // v_mfma_f32_32x32x16_bf16 layout (gfx950): A lane l holds A[l % 32][8*(l/32)
 // .. +8], B lane l holds B[8*(l/32) .. +8][l % 32], result register v of lane
@@ -26,11 +33,13 @@
 namespace qlora {
 
 constexpr int kBM = 256;
-constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kThreads = 512;
+constexpr int kRowBytes = 128;  // 64 bf16 per LDS row
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -41,38 +50,16 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
 // the 8 XCDs; remap so that each XCD receives a contiguous range of logical
 // tiles, ordered output-column fastest: an XCD then keeps the same token tile
 // (activations) in its L2 while it walks across the weight.
-__device__ __forceinline__ void tile_of(int64_t mt_count, int64_t nt_count, int64_t &mt, int64_t &nt) {
+__device__ __forceinline__ void tile_of(int64_t mt_count, int64_t nt_count, int64_t &mt,
+                                        int64_t &nt) {
   const int64_t G = mt_count * nt_count;
-  int64_t bid = blockIdx.x;
-  int64_t L = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int64_t bid = blockIdx.x;
+  const int64_t L = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
   mt = L / nt_count;
   nt = L % nt_count;
 }
 
-template <typename T>
-__device__ __forceinline__ void load8_as_bf16(const T *p, int64_t i, bool ok, u32x4 &out);
-template <>
-__device__ __forceinline__ void load8_as_bf16<uint16_t>(const uint16_t *p, int64_t i, bool ok,
-                                                        u32x4 &out) {
-  if (ok) {
-    out = *reinterpret_cast<const u32x4 *>(p + i);
-  } else {
-    out = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-template <>
-__device__ __forceinline__ void load8_as_bf16<float>(const float *p, int64_t i, bool ok, u32x4 &out) {
-  if (ok) {
-    const float4 a = *reinterpret_cast<const float4 *>(p + i);
-    const float4 b = *reinterpret_cast<const float4 *>(p + i + 4);
-    out = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                pack_bf16x2(b.z, b.w)};
-  } else {
-    out = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// Eight consecutive entries j0..j0+7 of a length-r row (zero past r), as bf16.
+// Eight consecutive entries j0..j0+7 of a length-r row (zero past r), scaled, as bf16.
 template <typename T>
 __device__ __forceinline__ u32x4 lora_row8(const T *row, int j0, int r, float scale) {
   float v[8];
@@ -82,132 +69,213 @@ __device__ __forceinline__ u32x4 lora_row8(const T *row, int j0, int r, float sc
                pack_bf16x2(v[6], v[7])};
 }
 
+// 256 rows x 64 bf16 activation tile: 4 chunks of 16 B per lane.
+struct ActStage {
+  u32x4 v[4];
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ src, int64_t ld, int64_t r0,
+                                       int64_t rows, int64_t c0, int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = t + kThreads * i;
+      const int row = id >> 3, c = id & 7;
+      const int64_t rr = r0 + row;
+      if (rr < rows)
+        v[i] = *reinterpret_cast<const u32x4 *>(src + rr * ld + c0 + 8 * c);
+      else
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t *lds, int t) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = t + kThreads * i;
+      *reinterpret_cast<u32x4 *>(lds + swz(id >> 3, id & 7)) = v[i];
+    }
+  }
+};
+
+__device__ __forceinline__ void zero_acc(f32x16 *acc, int n) {
+  for (int i = 0; i < n; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+}
+
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <typename LT>
+template <int BN, typename LT, bool DQ>
 __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restrict__ x, int64_t M,
                                                        const uint8_t *__restrict__ packed,
                                                        BlockScales sc, int64_t N, int64_t K,
                                                        const float *__restrict__ u,
                                                        const LT *__restrict__ B, int32_t r,
                                                        float s, uint16_t *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t ws[kBN * 128];
+  constexpr int TN = BN / 4;           // outputs per wave
+  constexpr int NJ = TN / 32;          // 32-wide tiles per wave along outputs
+  constexpr int WBYTES = BN * 32 / kThreads;  // packed bytes per lane per step (16 or 8)
+  constexpr int LPR = 32 / WBYTES;            // lanes per weight row
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ws[2][BN * kRowBytes];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, nt;
-  tile_of((M + kBM - 1) / kBM, (N + kBN - 1) / kBN, mt, nt);
-  const int64_t m0 = mt * kBM, n0 = nt * kBN;
+  tile_of((M + kBM - 1) / kBM, (N + BN - 1) / BN, mt, nt);
+  const int64_t m0 = mt * kBM, n0 = nt * BN;
   const int64_t KB = K >> 6;
+  const int nsteps = (int)KB;
 
-  // global -> register staging
-  u32x4 xr[4];
-  u32x2 wr;
-  float wa;
-  const int w_row = t >> 2, w_part = t & 3;
-  const int64_t w_n = n0 + w_row;
-  const bool w_ok = w_n < N;
+  // weight staging: lane -> (row, part) of the packed tile.  Rows past N
+  // (and token rows past M below) are clamped to the last valid row instead
+  // of predicated: they only feed outputs that are never stored, and
+  // branch-free loads let the compiler count outstanding loads exactly.
+  const int w_row = t / LPR, w_part = t % LPR;
+  const int64_t w_n = n0 + w_row < N ? n0 + w_row : N - 1;
+  const uint8_t *w_src = packed + ((w_n * K) >> 1) + WBYTES * w_part;
+  const int64_t w_sc = w_n * KB;
 
-  auto load_stage = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      const int row = id >> 3, c = id & 7;
-      const int64_t m = m0 + row;
-      load8_as_bf16<uint16_t>(x, m * K + k0 + 8 * c, m < M, xr[i]);
-    }
-    if (w_ok) {
-      wr = *reinterpret_cast<const u32x2 *>(packed + ((w_n * K + k0) >> 1) + 8 * w_part);
-      wa = sc(w_n * KB + (k0 >> 6));
+  const float mu = DQ ? sc.mu[0] : 0.0f;
+
+  ActStage xr;
+  uint32_t wr[WBYTES / 4];
+  // the block constant travels as its raw parts (code and sigma, or the fp32
+  // absmax) and is combined only when the tile is staged, so that no wait
+  // for the just-issued prefetch is needed
+  int wq = 0;
+  float wsig = 0.0f;
+  auto load_w = [&](int step) {
+    if constexpr (WBYTES == 16) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(w_src + 32 * (int64_t)step);
+      wr[0] = v.x; wr[1] = v.y; wr[2] = v.z; wr[3] = v.w;
     } else {
-      wr = u32x2{0u, 0u};
-      wa = 0.0f;
+      const u32x2 v = *reinterpret_cast<const u32x2 *>(w_src + 32 * (int64_t)step);
+      wr[0] = v.x; wr[1] = v.y;
+    }
+    const int64_t b = w_sc + step;
+    if constexpr (DQ) {
+      wq = sc.q[b];
+      wsig = sc.sigma[b >> 8];
+    } else {
+      wsig = sc.absmax[b];
     }
   };
-  auto store_stage = [&]() {
+  const uint16_t *x_src[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      const int row = id >> 3, c = id & 7;
-      *reinterpret_cast<u32x4 *>(xs + swz(row, c)) = xr[i];
-    }
-    uint32_t d[8];
+  for (int i = 0; i < 4; ++i) {
+    const int id = t + kThreads * i;
+    const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
+    x_src[i] = x + rr * K + 8 * (id & 7);
+  }
+  auto load_x_chunk = [&](int step, int i) {
+    xr.v[i] = *reinterpret_cast<const u32x4 *>(x_src[i] + (int64_t)step * kBK);
+  };
+  // quarter q of the staging of one step into LDS buffer buf: activation
+  // chunk q and the q-th quarter of this lane's dequantised weight bytes
+  auto store_quarter = [&](int buf, int qq) {
+    const int id = t + kThreads * qq;
+    *reinterpret_cast<u32x4 *>(xs[buf] + swz(id >> 3, id & 7)) = xr.v[qq];
+    const float wa = DQ ? __builtin_fmaf((float)wq, wsig, mu) : wsig;
+    constexpr int BPQ = WBYTES / 4;  // packed bytes per quarter: 4 or 2
+    uint32_t d[BPQ];
 #pragma unroll
-    for (int bi = 0; bi < 8; ++bi) {
-      const uint32_t word = bi < 4 ? wr.x : wr.y;
-      const float2 p = lut[(word >> (8 * (bi & 3))) & 0xFF];
-      d[bi] = pack_bf16x2(p.x * wa, p.y * wa);
+    for (int e = 0; e < BPQ; ++e) {
+      const int bi = BPQ * qq + e;
+      const float2 p = lut[(wr[bi >> 2] >> (8 * (bi & 3))) & 0xFF];
+      d[e] = pack_bf16x2(p.x * wa, p.y * wa);
     }
-    *reinterpret_cast<u32x4 *>(ws + swz(w_row, 2 * w_part)) = u32x4{d[0], d[1], d[2], d[3]};
-    *reinterpret_cast<u32x4 *>(ws + swz(w_row, 2 * w_part + 1)) = u32x4{d[4], d[5], d[6], d[7]};
+    if constexpr (BPQ == 4) {
+      *reinterpret_cast<u32x4 *>(ws[buf] + swz(w_row, 4 * w_part + qq)) =
+          u32x4{d[0], d[1], d[2], d[3]};
+    } else {
+      // 8-byte halves of the lane's two 16-byte chunks
+      *reinterpret_cast<u32x2 *>(ws[buf] + swz(w_row, 2 * w_part + (qq >> 1)) + 8 * (qq & 1)) =
+          u32x2{d[0], d[1]};
+    }
   };
 
   const int wave = t >> 6, lane = t & 63;
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lk = lane >> 5;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  f32x16 acc[4][NJ];
+  zero_acc(&acc[0][0], 4 * NJ);
 
   __syncthreads();  // lut
-  load_stage(0);
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    store_stage();
-    __syncthreads();
-    if (k0 + kBK < K) load_stage(k0 + kBK);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_x_chunk(0, i);
+  load_w(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_quarter(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_x_chunk(nsteps > 1 ? 1 : 0, i);
+  load_w(nsteps > 1 ? 1 : 0);
+  __syncthreads();
+  // The staging of step k+1 and the prefetch of step k+2 run unconditionally
+  // (clamped to the last step): the extra work in the last two iterations
+  // writes a buffer no one reads again and keeps the loop free of branches.
+  for (int k = 0; k < nsteps; ++k) {
+    const int cur = k & 1;
+    const int pf = k + 2 < nsteps ? k + 2 : nsteps - 1;
+    const uint8_t *xb = xs[cur];
+    const uint8_t *wb = ws[cur];
+    u32x4 a[2][4], b[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[0][i] = *reinterpret_cast<const u32x4 *>(xb + swz(128 * wm + 32 * i + lr, lk));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      b[0][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TN * wn + 32 * j + lr, lk));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = 2 * kk + lk;
-      u32x4 a[2], b[2];
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk < 3) {
+        const int chunk = 2 * (kk + 1) + lk;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const u32x4 *>(xs + swz(64 * wm + 32 * i + lr, chunk));
+        for (int i = 0; i < 4; ++i)
+          a[nb][i] = *reinterpret_cast<const u32x4 *>(xb + swz(128 * wm + 32 * i + lr, chunk));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const u32x4 *>(ws + swz(64 * wn + 32 * j + lr, chunk));
+        for (int j = 0; j < NJ; ++j)
+          b[nb][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TN * wn + 32 * j + lr, chunk));
+      }
+      store_quarter(cur ^ 1, kk);
+      load_x_chunk(pf, kk);
+      if (kk == 3) load_w(pf);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[cb][i], b[cb][j], acc[i][j]);
     }
     __syncthreads();
   }
 
   // LoRA bypass: acc += (s u) B^T, 16 ranks per MFMA step.
   for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 a[2], b[2];
+    u32x4 a[4], b[NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + 64 * wm + 32 * i + lr;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 128 * wm + 32 * i + lr;
       a[i] = (m < M) ? lora_row8(u + m * r, j0 + 8 * lk, r, s) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + 64 * wn + 32 * j + lr;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t n = n0 + TN * wn + 32 * j + lr;
       b[j] = (n < N) ? lora_row8(B + n * r, j0 + 8 * lk, r, 1.0f) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + 64 * wn + 32 * j + lr;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t n = n0 + TN * wn + 32 * j + lr;
       if (n >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
+        const int64_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
         if (m < M) y[m * N + n] = f32_to_bf16_bits(acc[i][j][v]);
       }
     }
@@ -215,175 +283,237 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 
 // ===========================================================================
 // Input gradient.  Contraction over the N outputs in steps of 64; the
-// workgroup's output tile is 256 tokens x 128 input features.  The weight
-// tile (64 rows n x 128 columns k, two NF4 blocks per row) is staged raw in
-// LDS, then every lane dequantises a 2 (n) x 8 (k) patch and writes it
-// transposed ([k][n], n contiguous) so the matrix cores read 8 consecutive n
-// per lane.
+// workgroup's output tile is 256 tokens x BX input features.  Every lane
+// dequantises 2 (n) x 8 (k) patches of the weight tile (loaded straight
+// from global memory, 4 bytes per row) and writes them transposed ([k][n],
+// n contiguous) so the matrix cores read 8 consecutive n per lane.
 // ===========================================================================
-constexpr int kDxBX = 128;
 constexpr int kDxBC = 64;
 
-template <typename LT>
+template <int BX, typename LT, bool DQ>
 __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
                                                       const uint8_t *__restrict__ packed,
                                                       BlockScales sc, int64_t N, int64_t K,
                                                       const float *__restrict__ g,
                                                       const LT *__restrict__ A, int32_t r,
                                                       uint16_t *__restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) uint8_t ds[kBM * 128];      // [m][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t wt[kDxBX * 128];    // [k][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t wraw[kDxBC * 64];   // [n][64 bytes]
+  constexpr int TX = BX / 4;
+  constexpr int NJ = TX / 32;
+  constexpr int NP = BX / 128;  // 2x8 patches per lane per step
+  __shared__ __attribute__((aligned(16))) uint8_t ds[2][kBM * kRowBytes];  // [m][n] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2][BX * kRowBytes];   // [k][n] bf16
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, kt;
-  tile_of((M + kBM - 1) / kBM, K / kDxBX, mt, kt);
-  const int64_t m0 = mt * kBM, k0 = kt * kDxBX;
+  tile_of((M + kBM - 1) / kBM, K / BX, mt, kt);
+  const int64_t m0 = mt * kBM, k0 = kt * BX;
   const int64_t KB = K >> 6;
+  const int nsteps = (int)(N / kDxBC);
 
-  u32x4 dr[4];
-  u32x2 wr;
-  float wa0, wa1;
-  const int raw_row = t >> 3, raw_part = t & 7;  // staging of the packed tile
-  const int pp = t & 31, kg = t >> 5;            // transposing dequant: rows 2pp, 2pp+1; k 8kg..+8
-
-  auto load_stage = [&](int64_t n0) {
+  const int pp = t & 31, kg = t >> 5;  // rows 2pp, 2pp+1; k-groups kg + 16 p
+  const float mu = DQ ? sc.mu[0] : 0.0f;
+  ActStage dr;
+  uint32_t wr[NP][2];
+  int wq[NP][2];
+  float wsig[NP][2];
+  auto load_w = [&](int step) {
+    const int64_t n0 = (int64_t)step * kDxBC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      const int row = id >> 3, c = id & 7;
-      const int64_t m = m0 + row;
-      load8_as_bf16<uint16_t>(dy, m * N + n0 + 8 * c, m < M, dr[i]);
+    for (int p = 0; p < NP; ++p) {
+      const int kl = 8 * (kg + 16 * p);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t n = n0 + 2 * pp + h;
+        wr[p][h] = *reinterpret_cast<const uint32_t *>(packed + ((n * K + k0 + kl) >> 1));
+        const int64_t b = n * KB + ((k0 + kl) >> 6);
+        if constexpr (DQ) {
+          wq[p][h] = sc.q[b];
+          wsig[p][h] = sc.sigma[b >> 8];
+        } else {
+          wq[p][h] = 0;
+          wsig[p][h] = sc.absmax[b];
+        }
+      }
     }
-    const int64_t n = n0 + raw_row;
-    wr = *reinterpret_cast<const u32x2 *>(packed + ((n * K + k0) >> 1) + 8 * raw_part);
-    const int64_t blk = (k0 >> 6) + (kg >> 3);
-    wa0 = sc((n0 + 2 * pp) * KB + blk);
-    wa1 = sc((n0 + 2 * pp + 1) * KB + blk);
+  };
+  // token rows past M are clamped (their outputs are never stored)
+  const uint16_t *dy_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = t + kThreads * i;
+    const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
+    dy_src[i] = dy + rr * N + 8 * (id & 7);
+  }
+  auto load_dy_chunk = [&](int step, int i) {
+    dr.v[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (int64_t)step * kDxBC);
+  };
+  // quarter q of one step's staging: dy chunk q, and byte q of every 2x8
+  // weight patch (columns kl + 2q, kl + 2q + 1 of rows 2pp, 2pp + 1)
+  auto store_quarter = [&](int buf, int qq) {
+    const int id = t + kThreads * qq;
+    *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) = dr.v[qq];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int kl = 8 * (kg + 16 * p);
+      const float wa0 = DQ ? __builtin_fmaf((float)wq[p][0], wsig[p][0], mu) : wsig[p][0];
+      const float wa1 = DQ ? __builtin_fmaf((float)wq[p][1], wsig[p][1], mu) : wsig[p][1];
+      const float2 p0 = lut[(wr[p][0] >> (8 * qq)) & 0xFF];
+      const float2 p1 = lut[(wr[p][1] >> (8 * qq)) & 0xFF];
+      const int kr = kl + 2 * qq;
+      *reinterpret_cast<uint32_t *>(wt[buf] + swz(kr, pp >> 2) + (pp & 3) * 4) =
+          pack_bf16x2(p0.x * wa0, p1.x * wa1);
+      *reinterpret_cast<uint32_t *>(wt[buf] + swz(kr + 1, pp >> 2) + (pp & 3) * 4) =
+          pack_bf16x2(p0.y * wa0, p1.y * wa1);
+    }
   };
 
   const int wave = t >> 6, lane = t & 63;
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lk = lane >> 5;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  f32x16 acc[4][NJ];
+  zero_acc(&acc[0][0], 4 * NJ);
 
   __syncthreads();  // lut
-  load_stage(0);
-  for (int64_t n0 = 0; n0 < N; n0 += kDxBC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      *reinterpret_cast<u32x4 *>(ds + swz(id >> 3, id & 7)) = dr[i];
-    }
-    *reinterpret_cast<u32x2 *>(wraw + raw_row * 64 + 8 * raw_part) = wr;
-    __syncthreads();
-    {
-      // rows 2pp and 2pp+1, columns 8kg..8kg+7 (4 bytes of each row)
-      const uint32_t w0 = *reinterpret_cast<const uint32_t *>(wraw + (2 * pp) * 64 + 4 * kg);
-      const uint32_t w1 = *reinterpret_cast<const uint32_t *>(wraw + (2 * pp + 1) * 64 + 4 * kg);
+  for (int i = 0; i < 4; ++i) load_dy_chunk(0, i);
+  load_w(0);
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const float2 p0 = lut[(w0 >> (8 * bi)) & 0xFF];
-        const float2 p1 = lut[(w1 >> (8 * bi)) & 0xFF];
-        const int kr = 8 * kg + 2 * bi;
-        const int off = ((pp >> 2) ^ (kr & 7)) * 16 + (pp & 3) * 4;
-        const int off1 = ((pp >> 2) ^ ((kr + 1) & 7)) * 16 + (pp & 3) * 4;
-        *reinterpret_cast<uint32_t *>(wt + kr * 128 + off) = pack_bf16x2(p0.x * wa0, p1.x * wa1);
-        *reinterpret_cast<uint32_t *>(wt + (kr + 1) * 128 + off1) =
-            pack_bf16x2(p0.y * wa0, p1.y * wa1);
-      }
-    }
-    __syncthreads();
-    if (n0 + kDxBC < N) load_stage(n0 + kDxBC);
+  for (int i = 0; i < 4; ++i) store_quarter(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_dy_chunk(nsteps > 1 ? 1 : 0, i);
+  load_w(nsteps > 1 ? 1 : 0);
+  __syncthreads();
+  for (int k = 0; k < nsteps; ++k) {
+    const int cur = k & 1;
+    const int pf = k + 2 < nsteps ? k + 2 : nsteps - 1;
+    const uint8_t *db = ds[cur];
+    const uint8_t *wb = wt[cur];
+    u32x4 a[2][4], b[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[0][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, lk));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      b[0][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TX * wn + 32 * j + lr, lk));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = 2 * kk + lk;
-      u32x4 a[2], b[2];
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk < 3) {
+        const int chunk = 2 * (kk + 1) + lk;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const u32x4 *>(ds + swz(64 * wm + 32 * i + lr, chunk));
+        for (int i = 0; i < 4; ++i)
+          a[nb][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, chunk));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const u32x4 *>(wt + swz(64 * wn + 32 * j + lr, chunk));
+        for (int j = 0; j < NJ; ++j)
+          b[nb][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TX * wn + 32 * j + lr, chunk));
+      }
+      store_quarter(cur ^ 1, kk);
+      load_dy_chunk(pf, kk);
+      if (kk == 3) load_w(pf);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[cb][i], b[cb][j], acc[i][j]);
     }
     __syncthreads();
   }
 
   // LoRA bypass: acc += g A, 16 ranks per MFMA step (g already holds s).
   for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 a[2], b[2];
+    u32x4 a[4], b[NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + 64 * wm + 32 * i + lr;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 128 * wm + 32 * i + lr;
       a[i] = (m < M) ? lora_row8(g + m * r, j0 + 8 * lk, r, 1.0f) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t k = k0 + 64 * wn + 32 * j + lr;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t kc = k0 + TX * wn + 32 * j + lr;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int jj = j0 + 8 * lk + e;
-        v[e] = (jj < r) ? load_as_f32(A, (int64_t)jj * K + k) : 0.0f;
+        v[e] = (jj < r) ? load_as_f32(A, (int64_t)jj * K + kc) : 0.0f;
       }
       b[j] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                    pack_bf16x2(v[6], v[7])};
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t k = k0 + 64 * wn + 32 * j + lr;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t kc = k0 + TX * wn + 32 * j + lr;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (m < M) dx[m * K + k] = f32_to_bf16_bits(acc[i][j][v]);
+        const int64_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
+        if (m < M) dx[m * K + kc] = f32_to_bf16_bits(acc[i][j][v]);
       }
     }
+}
+
+// Output tile width: 256 when that still gives at least ~1.5 workgroups per
+// compute unit, else 128.
+static int pick_width(int64_t M, int64_t cols, int64_t divisor_ok) {
+  const int64_t mt = (M + kBM - 1) / kBM;
+  const int64_t tiles256 = mt * ((cols + 255) / 256);
+  if (divisor_ok && tiles256 >= 384) return 256;
+  return 128;
 }
 
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
                     int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
                     float s, uint16_t *y, hipStream_t stream) {
-  const int64_t G = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  if (lora_dtype == QL_BF16)
-    hipLaunchKernelGGL(k_gemm_fwd<uint16_t>, dim3((unsigned)G), dim3(kThreads), 0, stream, x, M,
-                       packed, sc, N, K, u, (const uint16_t *)B, r, s, y);
-  else
-    hipLaunchKernelGGL(k_gemm_fwd<float>, dim3((unsigned)G), dim3(kThreads), 0, stream, x, M,
-                       packed, sc, N, K, u, (const float *)B, r, s, y);
+  const int bn = pick_width(M, N, 1);
+  const int64_t G = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
+  const bool dq = sc.absmax == nullptr;
+#define QL_FWD(BNV, LT, DQV)                                                                    \
+  hipLaunchKernelGGL((k_gemm_fwd<BNV, LT, DQV>), dim3((unsigned)G), dim3(kThreads), 0, stream, \
+                     x, M, packed, sc, N, K, u, (const LT *)B, r, s, y)
+#define QL_FWD_DQ(BNV, LT) \
+  do { if (dq) QL_FWD(BNV, LT, true); else QL_FWD(BNV, LT, false); } while (0)
+  if (bn == 256) {
+    if (lora_dtype == QL_BF16) QL_FWD_DQ(256, uint16_t);
+    else QL_FWD_DQ(256, float);
+  } else {
+    if (lora_dtype == QL_BF16) QL_FWD_DQ(128, uint16_t);
+    else QL_FWD_DQ(128, float);
+  }
+#undef QL_FWD_DQ
+#undef QL_FWD
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }
 
+bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 == 0; }
+
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
                    uint16_t *dx, hipStream_t stream) {
-  const int64_t G = ((M + kBM - 1) / kBM) * (K / kDxBX);
-  if (lora_dtype == QL_BF16)
-    hipLaunchKernelGGL(k_gemm_dx<uint16_t>, dim3((unsigned)G), dim3(kThreads), 0, stream, dy, M,
-                       packed, sc, N, K, g, (const uint16_t *)A, r, dx);
-  else
-    hipLaunchKernelGGL(k_gemm_dx<float>, dim3((unsigned)G), dim3(kThreads), 0, stream, dy, M,
-                       packed, sc, N, K, g, (const float *)A, r, dx);
+  const int bx = pick_width(M, K, K % 256 == 0);
+  const int64_t G = ((M + kBM - 1) / kBM) * (K / bx);
+  const bool dq = sc.absmax == nullptr;
+#define QL_DX(BXV, LT, DQV)                                                                      \
+  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV>), dim3((unsigned)G), dim3(kThreads), 0, stream,   \
+                     dy, M, packed, sc, N, K, g, (const LT *)A, r, dx)
+#define QL_DX_DQ(BXV, LT) \
+  do { if (dq) QL_DX(BXV, LT, true); else QL_DX(BXV, LT, false); } while (0)
+  if (bx == 256) {
+    if (lora_dtype == QL_BF16) QL_DX_DQ(256, uint16_t);
+    else QL_DX_DQ(256, float);
+  } else {
+    if (lora_dtype == QL_BF16) QL_DX_DQ(128, uint16_t);
+    else QL_DX_DQ(128, float);
+  }
+#undef QL_DX_DQ
+#undef QL_DX
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

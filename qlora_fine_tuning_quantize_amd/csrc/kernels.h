@@ -22,9 +22,11 @@ int launch_nf4_dequantize(const uint8_t *packed, int64_t n, BlockScales sc, void
 //          Q(j, c) = Q[j*ldq_j + c*ldq_c]
 //   cols:  out(j, c) = scale * sum_m R[m][j] * P[m][c]    (dA = g^T x, dB = s dy^T u)
 size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r);
+// out may be NULL: then only the partials are produced and the number of
+// slices is returned through *slices (the caller reduces them).
 int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const void *Q,
                         int q_dtype, int64_t ldq_j, int64_t ldq_c, int32_t r, float scale,
-                        float *out, float *partial, hipStream_t stream);
+                        float *out, float *partial, hipStream_t stream, int *slices = nullptr);
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r);
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
@@ -39,14 +41,16 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
                      int lora_dtype, int32_t r, void *dx, hipStream_t stream);
 
 // gemv.hip: decode-sized forward (M <= 16, bf16 activations).
+// u_part: S slice partials [S][M][r] of x A^T, summed in the epilogue.
 int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, hipStream_t stream);
+                    int64_t N, int64_t K, const float *u_part, int S, const void *B,
+                    int lora_dtype, int32_t r, float s, uint16_t *y, hipStream_t stream);
 
 // gemm.hip: matrix-core forward and input-gradient products (bf16).
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
                     int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
                     float s, uint16_t *y, hipStream_t stream);
+bool gemm_dx_supported(int64_t N, int64_t K);
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
                    uint16_t *dx, hipStream_t stream);
