@@ -209,3 +209,41 @@ def test_mlp8b_config_full_size_sampled(orc, proj):
     _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e <= BF16_TOL, (k, e)
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_mlp70b_config_full_size_sampled(orc, proj):
+    """70B-shaped MLP projection at M = 4096 tokens, r 64, alpha 16 (s = 0.25),
+    NF4 + double quant: y and dx on 32 sampled token rows, dA and dB in full."""
+    c = si.MLP_70B
+    N, K = c["projs"][proj]
+    M, r = c["M"], c["r"]
+    rows = np.sort(np.random.default_rng(4).choice(M, 32, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    _say(f"mlp70b {proj}: M={M} N={N} K={K}")
+    got, ref = _layer_case(orc, M, N, K, r, True, torch.bfloat16, torch.bfloat16,
+                           alpha=c["alpha"], seed_cfg=c["config"], rows=rows)
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_weightset_layer_bit_exact(orc, layer):
+    """8B-shaped weight set (N(0, 0.02) with 0.1% outliers at 20 sigma): every
+    tensor of one layer quantised (+ double quant) and dequantised bit-exactly;
+    bits/param as the pages' arithmetic says."""
+    for name in si.WEIGHTSET_8B["shapes"]:
+        w = si.weightset_tensor(layer, name, device=DEV)
+        _say(f"weight set layer {layer} {name} {tuple(w.shape)}")
+        Wq = q.nf4_quantize(w, double_quant=True)
+        deq = q.nf4_dequantize(Wq, torch.bfloat16)
+        torch.cuda.synchronize()
+        st = orc.quantize_nf4(host(w).reshape(-1), double_quant=True)
+        np.testing.assert_array_equal(host(Wq.packed)[:st["packed"].size], st["packed"])
+        np.testing.assert_array_equal(host(Wq.absmax_q)[:st["absmax_q"].size], st["absmax_q"])
+        np.testing.assert_array_equal(host(Wq.absmax_scale)[:st["absmax_scale"].size], st["absmax_scale"])
+        assert host(Wq.absmax_mean)[0] == st["absmax_mean"]
+        np.testing.assert_array_equal(host(deq).reshape(-1), orc.round_bf16(orc.dequantize(st)))
+        assert abs(orc.bits_per_param(st) - (4 + 8 / 64 + 32 / 16384 + 32 / w.numel())) < 1e-12
