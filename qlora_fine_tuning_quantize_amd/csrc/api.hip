@@ -200,16 +200,9 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype == QL_BF16 && M <= 16) {
-    // decode: the GEMV sums the slice partials of u itself; u is reduced
-    // separately only when the caller wants it saved
-    int S = 0;
-    st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u_save,
-                             rows_partial, s, &S);
-    if (st) return st;
-    return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, rows_partial, S, B,
-                           lora_dtype, r, sc_lora, (uint16_t *)y, s);
-  }
+  if (act_dtype == QL_BF16 && M <= 16)  // decode: one launch computes u and y
+    return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, A, B, lora_dtype, r,
+                           sc_lora, (uint16_t *)y, u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
   if (st) return st;
   if (act_dtype == QL_BF16)

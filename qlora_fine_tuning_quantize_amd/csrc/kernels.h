@@ -40,11 +40,11 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
                      int lora_dtype, int32_t r, void *dx, hipStream_t stream);
 
-// gemv.hip: decode-sized forward (M <= 16, bf16 activations).
-// u_part: S slice partials [S][M][r] of x A^T, summed in the epilogue.
+// gemv.hip: decode-sized forward (M <= 16, bf16 activations), one launch:
+// computes u = x A^T itself and writes it to u_save when non-null.
 int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const float *u_part, int S, const void *B,
-                    int lora_dtype, int32_t r, float s, uint16_t *y, hipStream_t stream);
+                    int64_t N, int64_t K, const void *A, const void *B, int lora_dtype, int32_t r,
+                    float s, uint16_t *y, float *u_save, hipStream_t stream);
 
 // gemm.hip: matrix-core forward and input-gradient products (bf16).
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
