@@ -283,12 +283,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 
 // ===========================================================================
 // Input gradient.  Contraction over the N outputs in steps of 64; the
-// workgroup's output tile is 256 tokens x BX input features.  Every lane
-// dequantises 2 (n) x 8 (k) patches of the weight tile (loaded straight
-// from global memory, 4 bytes per row) and writes them transposed ([k][n],
-// n contiguous) so the matrix cores read 8 consecutive n per lane.
+// workgroup's output tile is 256 tokens x BX input features.  The weight
+// tile (64 rows n x BX columns k) is loaded with wide coalesced reads (each
+// lane takes BX/8 consecutive codes of one row), dequantised and stored in
+// LDS in its natural [n][k] order; the matrix cores need 8 consecutive n of
+// one column k per lane, which gfx950's transposing LDS read provides: for
+// a group of 16 lanes whose 64-bit addresses name rows n0..n0+3 (lanes
+// 4e..4e+3 -> row n0+e, columns c..c+15 in four 4-column pieces), output
+// lane i receives column c+i of the four rows.  Two such reads give the 8
+// rows of one operand.
 // ===========================================================================
 constexpr int kDxBC = 64;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Byte offset of 16-byte chunk c (8 columns) of weight-tile row n.  Chunks
+// are permuted within each 256-byte bank span so that (a) the 16 lanes of a
+// chunk store (two rows, eight lanes each) and (b) the 32 lanes of a
+// transposing read (four rows x four chunks) touch 16 distinct bank slots.
+template <int BX>
+__device__ __forceinline__ int wswz(int n, int c) {
+  const int p = c ^ (((n & 3) << 2) | (n & 1)) ^ (((c >> 4) & 1) << 1);
+  return n * (2 * BX) + (p << 4);
+}
 
 template <int BX, typename LT, bool DQ>
 __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
@@ -299,9 +322,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
                                                       uint16_t *__restrict__ dx) {
   constexpr int TX = BX / 4;
   constexpr int NJ = TX / 32;
-  constexpr int NP = BX / 128;  // 2x8 patches per lane per step
-  __shared__ __attribute__((aligned(16))) uint8_t ds[2][kBM * kRowBytes];  // [m][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t wt[2][BX * kRowBytes];   // [k][n] bf16
+  constexpr int NU = BX / 64;  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
+  __shared__ __attribute__((aligned(16))) uint8_t ds[2][kBM * kRowBytes];  // dy [m][n] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];   // W^ [n][k] bf16
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
@@ -309,33 +332,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   int64_t mt, kt;
   tile_of((M + kBM - 1) / kBM, K / BX, mt, kt);
   const int64_t m0 = mt * kBM, k0 = kt * BX;
-  const int64_t KB = K >> 6;
   const int nsteps = (int)(N / kDxBC);
 
-  const int pp = t & 31, kg = t >> 5;  // rows 2pp, 2pp+1; k-groups kg + 16 p
+  // weight staging: lane -> row wrow of the step, 8 * NU codes from column wk
+  const int wrow = t >> 3, wk = (t & 7) * 8 * NU;
   const float mu = DQ ? sc.mu[0] : 0.0f;
   ActStage dr;
-  uint32_t wr[NP][2];
-  int wq[NP][2];
-  float wsig[NP][2];
+  uint32_t wr[NU];
+  int wq;
+  float wsig;
   auto load_w = [&](int step) {
-    const int64_t n0 = (int64_t)step * kDxBC;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int kl = 8 * (kg + 16 * p);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t n = n0 + 2 * pp + h;
-        wr[p][h] = *reinterpret_cast<const uint32_t *>(packed + ((n * K + k0 + kl) >> 1));
-        const int64_t b = n * KB + ((k0 + kl) >> 6);
-        if constexpr (DQ) {
-          wq[p][h] = sc.q[b];
-          wsig[p][h] = sc.sigma[b >> 8];
-        } else {
-          wq[p][h] = 0;
-          wsig[p][h] = sc.absmax[b];
-        }
-      }
+    const int64_t e = ((int64_t)step * kDxBC + wrow) * K + k0 + wk;
+    if constexpr (NU == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2 *>(packed + (e >> 1));
+      wr[0] = v[0];
+      wr[1] = v[1];
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(packed + (e >> 1));
+      wr[0] = v[0];
+      wr[1] = v[1];
+      wr[2] = v[2];
+      wr[3] = v[3];
+    }
+    const int64_t b = e >> 6;  // the lane's codes lie inside one 64-block
+    if constexpr (DQ) {
+      wq = sc.q[b];
+      wsig = sc.sigma[b >> 8];
+    } else {
+      wq = 0;
+      wsig = sc.absmax[b];
     }
   };
   // token rows past M are clamped (their outputs are never stored)
@@ -349,29 +374,42 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   auto load_dy_chunk = [&](int step, int i) {
     dr.v[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (int64_t)step * kDxBC);
   };
-  // quarter q of one step's staging: dy chunk q, and byte q of every 2x8
-  // weight patch (columns kl + 2q, kl + 2q + 1 of rows 2pp, 2pp + 1)
+  // quarter q of one step's staging: dy chunk q, and the weight words
+  // assigned to that quarter (one word = 8 codes = one 16-byte chunk)
   auto store_quarter = [&](int buf, int qq) {
     const int id = t + kThreads * qq;
     *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) = dr.v[qq];
+    constexpr int every = 4 / NU;
+    if (qq % every == 0) {
+      const int u = qq / every;
+      const float wa = DQ ? __builtin_fmaf((float)wq, wsig, mu) : wsig;
+      u32x4 o;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int kl = 8 * (kg + 16 * p);
-      const float wa0 = DQ ? __builtin_fmaf((float)wq[p][0], wsig[p][0], mu) : wsig[p][0];
-      const float wa1 = DQ ? __builtin_fmaf((float)wq[p][1], wsig[p][1], mu) : wsig[p][1];
-      const float2 p0 = lut[(wr[p][0] >> (8 * qq)) & 0xFF];
-      const float2 p1 = lut[(wr[p][1] >> (8 * qq)) & 0xFF];
-      const int kr = kl + 2 * qq;
-      *reinterpret_cast<uint32_t *>(wt[buf] + swz(kr, pp >> 2) + (pp & 3) * 4) =
-          pack_bf16x2(p0.x * wa0, p1.x * wa1);
-      *reinterpret_cast<uint32_t *>(wt[buf] + swz(kr + 1, pp >> 2) + (pp & 3) * 4) =
-          pack_bf16x2(p0.y * wa0, p1.y * wa1);
+      for (int bb = 0; bb < 4; ++bb) {
+        // byte bb holds codes 2bb (high nibble) and 2bb+1 of the word
+        const float2 pv = lut[(wr[u] >> (8 * bb)) & 0xFF];
+        o[bb] = pack_bf16x2(pv.x * wa, pv.y * wa);
+      }
+      *reinterpret_cast<u32x4 *>(wt[buf] + wswz<BX>(wrow, (wk >> 3) + u)) = o;
     }
   };
 
   const int wave = t >> 6, lane = t & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lk = lane >> 5;
+  // transposing-read address of this lane within a 16-lane group:
+  // row offset e = (lane & 15) / 4, column piece 4 * (lane & 3); groups
+  // 1 and 3 take columns +16, groups 2 and 3 take rows +8
+  const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto read_b = [&](const uint8_t *wb, int kk, int j) {
+    const int col = TX * wn + 32 * j + tr_col;
+    const int n = 16 * kk + tr_row;
+    const int off = (col & 7) * 2;
+    const u32x2 lo = lds_read_tr16(wb + wswz<BX>(n, col >> 3) + off);
+    const u32x2 hi = lds_read_tr16(wb + wswz<BX>(n + 4, col >> 3) + off);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
   f32x16 acc[4][NJ];
   zero_acc(&acc[0][0], 4 * NJ);
 
@@ -395,8 +433,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     for (int i = 0; i < 4; ++i)
       a[0][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, lk));
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[0][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TX * wn + 32 * j + lr, lk));
+    for (int j = 0; j < NJ; ++j) b[0][j] = read_b(wb, 0, j);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cb = kk & 1, nb = cb ^ 1;
@@ -406,8 +443,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
         for (int i = 0; i < 4; ++i)
           a[nb][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, chunk));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          b[nb][j] = *reinterpret_cast<const u32x4 *>(wb + swz(TX * wn + 32 * j + lr, chunk));
+        for (int j = 0; j < NJ; ++j) b[nb][j] = read_b(wb, kk + 1, j);
       }
       store_quarter(cur ^ 1, kk);
       load_dy_chunk(pf, kk);
