@@ -28,6 +28,12 @@
 // v_mfma_f32_32x32x16_bf16 layout (gfx950): A lane l holds A[l % 32][8*(l/32)
 // .. +8], B lane l holds B[8*(l/32) .. +8][l % 32], result register v of lane
 // l is D[8*(v/4) + 4*(l/32) + v%4][l % 32].
+//
+// The matrix cores compute the transposed output tile (weight operand as A,
+// activation operand as B), so that each lane ends with runs of 4
+// consecutive output columns of one row and stores them as 8-byte words.
+// The rank-r bypass is accumulated first, before the main loop, so the loads
+// of its operands overlap the loads of the first tiles.
 #include "kernels.h"
 
 namespace qlora {
@@ -100,6 +106,112 @@ __device__ __forceinline__ void zero_acc(f32x16 *acc, int n) {
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 }
 
+// Store a wave's transposed accumulators as bf16: register v of
+// accumulator (i, j) in lane l is out[row][col], row = row_base + 32 i +
+// l % 32, col = col_base + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4.  Full
+// tiles use 8-byte stores; a tile crossing the last column stores element
+// by element.
+template <int NJ>
+__device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t ld, int64_t rows,
+                                             int64_t cols, int64_t row_base, int64_t col_base,
+                                             const f32x16 (&acc)[4][NJ], int lane) {
+  const int lr = lane & 31, lk = lane >> 5;
+  const bool full = col_base + 32 * NJ <= cols && ld % 4 == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = row_base + 32 * i + lr;
+    if (m >= rows) continue;
+    uint16_t *p = out + m * ld + col_base + 4 * lk;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2 *>(p + 32 * j + 8 * q) =
+              u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                    pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+    } else {
+      for (int j = 0; j < NJ; ++j)
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * j + 8 * (v >> 2) + (v & 3);
+          if (col_base + 4 * lk + c < cols) p[c] = f32_to_bf16_bits(acc[i][j][v]);
+        }
+    }
+  }
+}
+
+// Rank-r operand tiles are staged once per 16-rank chunk into LDS as bf16
+// rows of 16 values with a 48-byte stride (the 16 rows one 16-byte-per-lane
+// read pass touches then start on 16 distinct 4-bank groups).
+constexpr int kLoraStride = 48;
+
+// rows x 16 slice [j0, j0 + 16) of a row-major [*, r] factor, times scale,
+// rounded to bf16; rows past `valid` and ranks past r are zero.
+template <typename T>
+__device__ __forceinline__ void stage_lora(uint8_t *dst, int rows, const T *__restrict__ src,
+                                           int64_t row0, int64_t valid, int32_t r, int j0,
+                                           float scale, int t, int nthreads) {
+  for (int e = t; e < rows * 16; e += nthreads) {
+    const int row = e >> 4, jj = e & 15;
+    const int64_t gr = row0 + row;
+    float v = 0.0f;
+    if (gr < valid && j0 + jj < r) v = scale * load_as_f32(src, gr * r + j0 + jj);
+    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = f32_to_bf16_bits(v);
+  }
+}
+
+// rows x 16 slice of the transpose of a row-major [r, ld] factor: staged
+// row `row` holds src[(j0 + jj) * ld + col0 + row], jj = 0..15 (lanes walk
+// along a source row, so the loads are coalesced).
+template <typename T>
+__device__ __forceinline__ void stage_lora_t(uint8_t *dst, int rows, const T *__restrict__ src,
+                                             int64_t ld, int64_t col0, int32_t r, int j0, int t,
+                                             int nthreads) {
+  for (int e = t; e < rows * 16; e += nthreads) {
+    const int jj = e / rows, row = e % rows;
+    float v = 0.0f;
+    if (j0 + jj < r) v = load_as_f32(src, (int64_t)(j0 + jj) * ld + col0 + row);
+    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = f32_to_bf16_bits(v);
+  }
+}
+
+__device__ __forceinline__ u32x4 lora_frag(const uint8_t *src, int row, int lk) {
+  return *reinterpret_cast<const u32x4 *>(src + row * kLoraStride + 16 * lk);
+}
+
+// Write a wave's transposed accumulators (see store_tile_t) through a
+// wave-private LDS slice of 32 rows, so every global store instruction
+// writes whole 16-byte pieces of 64 / (TN / 8) consecutive rows.  Needs a
+// full tile in the column direction and ld % 8 == 0.
+template <int NJ>
+__device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64_t ld,
+                                               int64_t rows, int64_t row_base, int64_t col_base,
+                                               const f32x16 (&acc)[4][NJ], uint8_t *slice,
+                                               int lane) {
+  constexpr int TN = 32 * NJ;
+  constexpr int OS = 2 * TN + 16;   // bytes per staged row
+  constexpr int CPR = TN / 8;       // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;     // rows per store instruction
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2 *>(slice + lr * OS + 2 * (32 * j + 8 * q + 4 * lk)) =
+            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = it * RPI + lane / CPR, c = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(slice + row * OS + 16 * c);
+      const int64_t m = row_base + 32 * i + row;
+      if (m < rows) *reinterpret_cast<u32x4 *>(out + m * ld + col_base + 8 * c) = v;
+    }
+  }
+}
+
 // ===========================================================================
 // Forward
 // ===========================================================================
@@ -116,6 +228,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   constexpr int LPR = 32 / WBYTES;            // lanes per weight row
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ws[2][BN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_u[kBM * kLoraStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_b[BN * kLoraStride];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
@@ -204,6 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) load_x_chunk(0, i);
   load_w(0);
+  // first 16-rank chunk of the bypass operands (s u and B), used after the
+  // main loop; staged here so that its loads overlap the first tile loads
+  stage_lora(ls_u, kBM, u, m0, M, r, 0, s, t, kThreads);
+  stage_lora(ls_b, BN, B, n0, N, r, 0, 1.0f, t, kThreads);
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
@@ -243,42 +361,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[cb][i], b[cb][j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(b[cb][j], a[cb][i], acc[i][j]);
     }
     __syncthreads();
   }
 
-  // LoRA bypass: acc += (s u) B^T, 16 ranks per MFMA step.
+  // LoRA bypass: acc += B (s u)^T, 16 ranks per MFMA step (the main loop's
+  // last barrier orders the staged chunk 0 before these reads).
   for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 a[4], b[NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + 128 * wm + 32 * i + lr;
-      a[i] = (m < M) ? lora_row8(u + m * r, j0 + 8 * lk, r, s) : u32x4{0u, 0u, 0u, 0u};
+    if (j0 > 0) {
+      __syncthreads();
+      stage_lora(ls_u, kBM, u, m0, M, r, j0, s, t, kThreads);
+      stage_lora(ls_b, BN, B, n0, N, r, j0, 1.0f, t, kThreads);
+      __syncthreads();
     }
+    u32x4 ua[4], bb[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t n = n0 + TN * wn + 32 * j + lr;
-      b[j] = (n < N) ? lora_row8(B + n * r, j0 + 8 * lk, r, 1.0f) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) ua[i] = lora_frag(ls_u, 128 * wm + 32 * i + lr, lk);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bb[j] = lora_frag(ls_b, TN * wn + 32 * j + lr, lk);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(bb[j], ua[i], acc[i][j]);
   }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t n = n0 + TN * wn + 32 * j + lr;
-      if (n >= N) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (m < M) y[m * N + n] = f32_to_bf16_bits(acc[i][j][v]);
-      }
-    }
+  if (n0 + BN <= N && N % 8 == 0)
+    store_tile_lds<NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
+                       &xs[0][0] + wave * 32 * (2 * TN + 16), lane);
+  else
+    store_tile_t<NJ>(y, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc, lane);
 }
 
 // ===========================================================================
@@ -325,6 +436,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   constexpr int NU = BX / 64;  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
   __shared__ __attribute__((aligned(16))) uint8_t ds[2][kBM * kRowBytes];  // dy [m][n] bf16
   __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];   // W^ [n][k] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t ls_g[kBM * kLoraStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_a[BX * kLoraStride];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
@@ -417,6 +530,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
 #pragma unroll
   for (int i = 0; i < 4; ++i) load_dy_chunk(0, i);
   load_w(0);
+  // first 16-rank chunk of the bypass operands (g, which already holds s,
+  // and A^T), used after the main loop; staged here so that its loads
+  // overlap the first tile loads
+  stage_lora(ls_g, kBM, g, m0, M, r, 0, 1.0f, t, kThreads);
+  stage_lora_t(ls_a, BX, A, K, k0, r, 0, t, kThreads);
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
@@ -451,48 +569,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[cb][i], b[cb][j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(b[cb][j], a[cb][i], acc[i][j]);
     }
     __syncthreads();
   }
 
-  // LoRA bypass: acc += g A, 16 ranks per MFMA step (g already holds s).
+  // LoRA bypass: acc += A^T g^T, 16 ranks per MFMA step.
   for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 a[4], b[NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + 128 * wm + 32 * i + lr;
-      a[i] = (m < M) ? lora_row8(g + m * r, j0 + 8 * lk, r, 1.0f) : u32x4{0u, 0u, 0u, 0u};
+    if (j0 > 0) {
+      __syncthreads();
+      stage_lora(ls_g, kBM, g, m0, M, r, j0, 1.0f, t, kThreads);
+      stage_lora_t(ls_a, BX, A, K, k0, r, j0, t, kThreads);
+      __syncthreads();
     }
+    u32x4 ga[4], ab[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t kc = k0 + TX * wn + 32 * j + lr;
-      float v[8];
+    for (int i = 0; i < 4; ++i) ga[i] = lora_frag(ls_g, 128 * wm + 32 * i + lr, lk);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = j0 + 8 * lk + e;
-        v[e] = (jj < r) ? load_as_f32(A, (int64_t)jj * K + kc) : 0.0f;
-      }
-      b[j] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                   pack_bf16x2(v[6], v[7])};
-    }
+    for (int j = 0; j < NJ; ++j) ab[j] = lora_frag(ls_a, TX * wn + 32 * j + lr, lk);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
   }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t kc = k0 + TX * wn + 32 * j + lr;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (m < M) dx[m * K + kc] = f32_to_bf16_bits(acc[i][j][v]);
-      }
-    }
+  // K % 128 == 0 here, so every tile is full in the column direction
+  store_tile_lds<NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
+                     &ds[0][0] + wave * 32 * (2 * TX + 16), lane);
 }
 
 // Output tile width: 256 when that still gives at least ~1.5 workgroups per
