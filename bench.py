@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s (%MFMA peak); decode GEMV packed-weight GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ROOFLINE_KERNEL = "k_gemm_fwd"
+ROOFLINE_KERNEL = "k_gemm_fwd<256, unsigned short, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_fwd_mlp8b_gate.json")
 
 
@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="only the training step")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of the step instead of direct launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -118,17 +120,53 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ms_eager = timed(step, args.steps, 0)
+    log(f"eager step {ms_eager:.3f} ms")
+
+    # With --graph the step's ~27 launches are captured once into a HIP graph
+    # and replayed: every kernel still runs each step, only host launch gaps
+    # go away (the GPU is the bottleneck here, so the two timings agree).
+    # The first replay must reproduce the eager outputs bit for bit.
+    outs = ("y", "u", "dx", "dA", "dB")
+    eager_out = [{k: p[k].clone() for k in outs} for p in projs]
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for p in projs:
+            for k in outs:
+                p[k].zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, e in zip(projs, eager_out):
+            for k in outs:
+                if not torch.equal(p[k], e[k]):
+                    raise RuntimeError(f"graph replay differs from the eager step ({p['name']} {k})")
+        log("graph replay reproduces the eager step")
+    run = graph.replay if graph is not None else step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     tflops = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms  {tflops:.1f} TFLOP/s  (wall {wall:.2f} s for {args.steps} steps)")
+    log(f"step {ms_step:.3f} ms  {tflops:.1f} TFLOP/s  (wall {wall:.2f} s for {args.steps} steps"
+        f", {'graph replay' if graph is not None else 'eager'})")
+    del graph, eager_out
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -140,13 +178,17 @@ def main():
                                "LoRA r=16 alpha=32, forward + backward (dx, dA, dB)",
                    "tokens": M, "rank": r, "alpha": alpha, "flop_per_step": flops_step},
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "launch": "HIP graph replay of the whole step" if args.graph else "direct launches",
+        "ms_per_step_eager": round(ms_eager, 4),
     }
 
     # ---------------- roofline: the forward GEMM alone ------------------------
+    # qlora_linear_fwd_u is one launch of the matrix-core forward kernel (u is
+    # the u_save of the step), so events on this stream bracket exactly it.
     g = projs[0]
-    fwd_ms = timed(lambda: q.qlora_linear_fwd(g["x"], g["W"], g["A"], g["B"], alpha, y=g["y"],
-                                              u_save=g["u"], ws=g["wsf"]), 50, 5)
-    fwd_flops = 2 * M * g["N"] * g["K"] + 2 * M * r * (g["K"] + g["N"])
+    fwd_ms = timed(lambda: q.qlora_linear_fwd_u(g["x"], g["W"], g["u"], g["B"], alpha,
+                                                y=g["y"]), 50, 5)
+    fwd_flops = 2 * M * g["N"] * g["K"] + 2 * M * r * g["N"]
     ach = fwd_flops / (fwd_ms * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -157,7 +199,7 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                           "traffic": traffic, "kernel": ROOFLINE_KERNEL,
-                          "launch": "qlora_linear_fwd gate 2048x14336x4096 (u pre-pass + GEMM)",
+                          "launch": "qlora_linear_fwd_u gate 2048x14336x4096 (one GEMM launch)",
                           "ms_per_launch": round(fwd_ms, 4), "flop_per_launch": fwd_flops}
     log(f"fwd gate {fwd_ms:.3f} ms {ach:.1f} TFLOP/s")
     del projs, g

@@ -163,6 +163,23 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
                      void *y, float *u_save, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Forward given the rank-r projection (26. ..., Step 3, with the first
+ * bypass product x A^T already at hand, e.g. the u_save of an earlier
+ * qlora_linear_fwd on the same x when a forward is recomputed):
+ *     y = x W^^T + s u B^T,   s = fp32(alpha / r)
+ *   u       device [M, r] fp32, 16-byte aligned
+ * Other arguments as for qlora_linear_fwd; no workspace.  With bf16
+ * activations this is a single matrix-core launch, bit-identical to the
+ * y of qlora_linear_fwd for M > 16 (for M <= 16 qlora_linear_fwd takes the
+ * single-launch decode path, which rounds u to bf16 in registers instead of
+ * reading it, so the two agree to within bf16 rounding).
+ * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
+ */
+int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                       const float *u, const void *B, int32_t lora_dtype, int32_t r,
+                       float alpha, void *y, void *stream);
+
+/*
  * Backward of the layer (22. QLoRA and 4bit Quantization, Step 1: the
  * gradient reaches x and the LoRA factors; the frozen base gets none):
  *     u = x A^T (or u_saved),  g = s dy B

@@ -23,7 +23,8 @@ NF4_BLOCK, DQ_BLOCK = 64, 256
 
 # every extern "C" symbol declared in include/qlora.h
 EXPORTED = ("ql_nf4_sizes", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
-            "qlora_linear_fwd", "qlora_linear_bwd", "ql_strerror", "ql_abi_version")
+            "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "ql_strerror",
+            "ql_abi_version")
 
 
 class QlNf4(ctypes.Structure):
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.nf4_dequantize.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, sz, p]
     L.qlora_linear_fwd.restype = ctypes.c_int
+    L.qlora_linear_fwd_u.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p]
+    L.qlora_linear_fwd_u.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [p, p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, p, p, sz, p]
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.ql_strerror.argtypes = [ctypes.c_int]
@@ -200,6 +203,23 @@ def qlora_linear_fwd(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Te
                                   _ptr(B), _dtype_code(A.dtype), r, float(alpha), _ptr(y),
                                   _ptr(u_save), _ptr(ws), ws.numel(), _stream(x.device)),
            "qlora_linear_fwd")
+    return y
+
+
+def qlora_linear_fwd_u(x: torch.Tensor, W: NF4Weight, u: torch.Tensor, B: torch.Tensor,
+                       alpha: float, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x W^T + (alpha/r) u B^T with u = x A^T given (fp32 [M, r])."""
+    assert x.dim() == 2 and x.is_contiguous() and u.is_contiguous() and B.is_contiguous()
+    M, K = x.shape
+    r = u.shape[1]
+    assert K == W.cols and u.shape == (M, r) and u.dtype == torch.float32
+    assert B.shape == (W.rows, r)
+    if y is None:
+        y = torch.empty((M, W.rows), dtype=x.dtype, device=x.device)
+    st = W.struct()
+    _check(lib().qlora_linear_fwd_u(_ptr(x), _dtype_code(x.dtype), M, ctypes.byref(st), _ptr(u),
+                                    _ptr(B), _dtype_code(B.dtype), r, float(alpha), _ptr(y),
+                                    _stream(x.device)), "qlora_linear_fwd_u")
     return y
 
 

@@ -108,7 +108,7 @@ int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const voi
 
 extern "C" {
 
-int ql_abi_version(void) { return 100; }
+int ql_abi_version(void) { return 101; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -205,6 +205,25 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
                            sc_lora, (uint16_t *)y, u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
   if (st) return st;
+  if (act_dtype == QL_BF16)
+    return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
+                           sc_lora, (uint16_t *)y, s);
+  return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
+                           s);
+}
+
+int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                       const float *u, const void *B, int32_t lora_dtype, int32_t r,
+                       float alpha, void *y, void *stream) {
+  // A is not read; B stands in for it in the shared argument check
+  int st = check_linear_common(act_dtype, M, W, B, B, lora_dtype, r, alpha);
+  if (st) return st;
+  if (!x || !y || !u) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(u)) return QL_EALIGN;
+  const int64_t N = W->rows, K = W->cols;
+  hipStream_t s = (hipStream_t)stream;
+  const float sc_lora = alpha / (float)r;
+  const BlockScales sc = scales_of(W);
   if (act_dtype == QL_BF16)
     return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
                            sc_lora, (uint16_t *)y, s);

@@ -147,11 +147,10 @@ constexpr int kLoraStride = 48;
 
 // rows x 16 slice [j0, j0 + 16) of a row-major [*, r] factor, times scale,
 // rounded to bf16; rows past `valid` and ranks past r are zero.
-template <typename T>
-__device__ __forceinline__ void stage_lora(uint8_t *dst, int rows, const T *__restrict__ src,
-                                           int64_t row0, int64_t valid, int32_t r, int j0,
-                                           float scale, int t, int nthreads) {
-  for (int e = t; e < rows * 16; e += nthreads) {
+template <int ROWS, int NT, typename T>
+__device__ __forceinline__ void stage_lora(uint8_t *dst, const T *__restrict__ src, int64_t row0,
+                                           int64_t valid, int32_t r, int j0, float scale, int t) {
+  for (int e = t; e < ROWS * 16; e += NT) {
     const int row = e >> 4, jj = e & 15;
     const int64_t gr = row0 + row;
     float v = 0.0f;
@@ -160,15 +159,14 @@ __device__ __forceinline__ void stage_lora(uint8_t *dst, int rows, const T *__re
   }
 }
 
-// rows x 16 slice of the transpose of a row-major [r, ld] factor: staged
+// ROWS x 16 slice of the transpose of a row-major [r, ld] factor: staged
 // row `row` holds src[(j0 + jj) * ld + col0 + row], jj = 0..15 (lanes walk
 // along a source row, so the loads are coalesced).
-template <typename T>
-__device__ __forceinline__ void stage_lora_t(uint8_t *dst, int rows, const T *__restrict__ src,
-                                             int64_t ld, int64_t col0, int32_t r, int j0, int t,
-                                             int nthreads) {
-  for (int e = t; e < rows * 16; e += nthreads) {
-    const int jj = e / rows, row = e % rows;
+template <int ROWS, int NT, typename T>
+__device__ __forceinline__ void stage_lora_t(uint8_t *dst, const T *__restrict__ src, int64_t ld,
+                                             int64_t col0, int32_t r, int j0, int t) {
+  for (int e = t; e < ROWS * 16; e += NT) {
+    const int jj = e / ROWS, row = e % ROWS;
     float v = 0.0f;
     if (j0 + jj < r) v = load_as_f32(src, (int64_t)(j0 + jj) * ld + col0 + row);
     *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = f32_to_bf16_bits(v);
@@ -320,8 +318,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   load_w(0);
   // first 16-rank chunk of the bypass operands (s u and B), used after the
   // main loop; staged here so that its loads overlap the first tile loads
-  stage_lora(ls_u, kBM, u, m0, M, r, 0, s, t, kThreads);
-  stage_lora(ls_b, BN, B, n0, N, r, 0, 1.0f, t, kThreads);
+  stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, 0, s, t);
+  stage_lora<BN, kThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
@@ -371,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   for (int j0 = 0; j0 < r; j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora(ls_u, kBM, u, m0, M, r, j0, s, t, kThreads);
-      stage_lora(ls_b, BN, B, n0, N, r, j0, 1.0f, t, kThreads);
+      stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, j0, s, t);
+      stage_lora<BN, kThreads>(ls_b, B, n0, N, r, j0, 1.0f, t);
       __syncthreads();
     }
     u32x4 ua[4], bb[NJ];
@@ -533,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   // first 16-rank chunk of the bypass operands (g, which already holds s,
   // and A^T), used after the main loop; staged here so that its loads
   // overlap the first tile loads
-  stage_lora(ls_g, kBM, g, m0, M, r, 0, 1.0f, t, kThreads);
-  stage_lora_t(ls_a, BX, A, K, k0, r, 0, t, kThreads);
+  stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, 0, 1.0f, t);
+  stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, 0, t);
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
@@ -578,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   for (int j0 = 0; j0 < r; j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora(ls_g, kBM, g, m0, M, r, j0, 1.0f, t, kThreads);
-      stage_lora_t(ls_a, BX, A, K, k0, r, j0, t, kThreads);
+      stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
+      stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, j0, t);
       __syncthreads();
     }
     u32x4 ga[4], ab[NJ];

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 100
+    assert L.ql_abi_version() == 101
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -131,6 +131,25 @@ def test_linear_fwd_rejects_bad_arguments():
     assert _fwd(L, ws=0) == b.QL_EWORKSPACE
     assert _fwd(L, ws_bytes=255) == b.QL_EWORKSPACE
     assert _fwd(L, ws=FAKE + 16) == b.QL_EALIGN
+
+
+@no_gpu
+def test_linear_fwd_u_rejects_bad_arguments():
+    L = q.lib()
+    d = _desc(rows=128, cols=256)
+
+    def fwd_u(M=16, r=8, u=FAKE, x=FAKE, y=FAKE, alpha=16.0, desc=d):
+        return L.qlora_linear_fwd_u(ctypes.c_void_p(x) if x else None, b.QL_BF16, M,
+                                    ctypes.byref(desc), ctypes.c_void_p(u) if u else None,
+                                    ctypes.c_void_p(FAKE), b.QL_BF16, r, alpha,
+                                    ctypes.c_void_p(y) if y else None, None)
+    assert fwd_u(u=0) == b.QL_EINVAL
+    assert fwd_u(x=0) == b.QL_EINVAL
+    assert fwd_u(M=0) == b.QL_EINVAL
+    assert fwd_u(r=129) == b.QL_EUNSUPPORTED
+    assert fwd_u(alpha=float("inf")) == b.QL_EINVAL
+    assert fwd_u(u=FAKE + 4) == b.QL_EALIGN
+    assert fwd_u(desc=_desc(rows=128, cols=100)) == b.QL_ESHAPE
 
 
 @no_gpu

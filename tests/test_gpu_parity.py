@@ -172,6 +172,35 @@ def test_layer_bf16_parity(orc, M, N, K, r, dq, lora):
         assert e <= BF16_TOL, (k, e)
 
 
+@pytest.mark.parametrize("M,N,K,r,act,lora", [
+    (300, 384, 384, 16, torch.bfloat16, torch.bfloat16),  # ragged M, two token tiles
+    (300, 200, 320, 8, torch.bfloat16, torch.float32),    # ragged N, guarded store path
+    (257, 128, 128, 128, torch.bfloat16, torch.bfloat16), # r = 128 (8 rank chunks)
+    (4, 256, 256, 8, torch.float32, torch.float32),       # fp32 path
+    (16, 384, 1024, 16, torch.bfloat16, torch.bfloat16),  # M <= 16: forward took the GEMV
+])
+def test_forward_given_u(orc, M, N, K, r, act, lora):
+    """qlora_linear_fwd_u with the u_save of qlora_linear_fwd reproduces its y
+    (bit for bit where both run the same kernel) and the oracle's y."""
+    _say(f"fwd_u M={M} N={N} K={K} r={r} act={act} lora={lora}")
+    t = si.linear_inputs(91, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora, sub=M + r)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=True)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], 32.0, u_save=u)
+    y_u = q.qlora_linear_fwd_u(d["x"], W, u, d["B"], 32.0)
+    torch.cuda.synchronize()
+    if M > 16 or act == torch.float32:
+        np.testing.assert_array_equal(y_u.float().cpu().numpy(), y.float().cpu().numpy())
+    st = orc.quantize_nf4(host(t["W"]), double_quant=True)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    y_ref, _ = orc.linear_fwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), 32.0, r)
+    if act == torch.float32:
+        assert_f32_close(y_u.cpu().numpy(), y_ref, "y")
+    else:
+        assert rel_err(y_u.float().cpu().numpy(), y_ref) <= BF16_TOL
+
+
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_config_full_size(orc, M):
     """Llama-3-8B attention projection: W 4096x4096 NF4 + double quant,
