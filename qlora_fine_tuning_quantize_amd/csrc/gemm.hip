@@ -54,15 +54,25 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
 
 // Workgroup -> tile.  Consecutive workgroup ids are spread round-robin over
 // the 8 XCDs; remap so that each XCD receives a contiguous range of logical
-// tiles, ordered output-column fastest: an XCD then keeps the same token tile
-// (activations) in its L2 while it walks across the weight.
+// tiles.  Logical tiles go in groups of two token tiles: within a group the
+// token tile alternates fastest, then the output column.  An XCD thus works
+// on a 2 x (its share of columns) block: its two activation strips stay in
+// its L2, and each weight tile is read by two workgroups at about the same
+// time (one L2 miss instead of two), which halves the weight traffic
+// compared with giving each XCD whole rows of tiles.
 __device__ __forceinline__ void tile_of(int64_t mt_count, int64_t nt_count, int64_t &mt,
                                         int64_t &nt) {
   const int64_t G = mt_count * nt_count;
   const int64_t bid = blockIdx.x;
   const int64_t L = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  mt = L / nt_count;
-  nt = L % nt_count;
+  if (mt_count % 2 == 0) {
+    const int64_t grp = L / (2 * nt_count), i = L % (2 * nt_count);
+    mt = grp * 2 + (i & 1);
+    nt = i >> 1;
+  } else {
+    mt = L / nt_count;
+    nt = L % nt_count;
+  }
 }
 
 // Eight consecutive entries j0..j0+7 of a length-r row (zero past r), scaled, as bf16.
