@@ -74,66 +74,172 @@ __global__ __launch_bounds__(256) void k_lora_rows(const void *__restrict__ P, i
 // ---------------------------------------------------------------------------
 // rows on the matrix cores (bf16 P): v_mfma_f32_16x16x32_bf16 with
 // A = 16 rows of P x 32 contraction values (read straight from global, 16 B
-// per lane) and B = the LoRA factor staged in LDS as bf16 [j][c].  Wave w of
-// the workgroup owns rows 16w..16w+15 of a 64-row tile and every 16-wide
-// rank tile; the workgroup covers one slice of the contraction.
+// per lane) and B = the LoRA factor slice staged in LDS as bf16 [j][c].
+// Wave w of the workgroup owns rows 16w..16w+15 of a 64-row tile and all JT
+// 16-wide rank tiles; the workgroup covers one CS-wide slice of the
+// contraction in a single round trip, with every trip count fixed at
+// compile time: the factor loads are issued first (8 values per load along
+// the factor's contiguous dimension, or single values for ranks / shapes
+// that are not 8-aligned), then all CS/32 loads of P, then the factor is
+// written to LDS (only its loads are waited for), one barrier, the MFMAs,
+// and the fp32 partial sums of the slice.  Rows past M and contraction
+// positions past C load clamped addresses and use zeros instead.
 // Operand layout (gfx950): A lane l holds A[l % 16][8*(l/16) .. +8]; B lane l
 // holds B[8*(l/16) .. +8][l % 16]; result lane l holds D[4*(l/16) .. +4][l % 16].
 // ---------------------------------------------------------------------------
 constexpr int kMRowsTile = 64;
-constexpr int kMRowsChunk = 256;
-constexpr int kQsStride = kMRowsChunk * 2 + 16;  // bytes per staged rank row (bank-shifted)
+
+// factor layouts: rows j contiguous in c (Q(j, c) = Q[j * ldq_j + c]), rows c
+// contiguous in j (Q(j, c) = Q[c * ldq_c + j]), or element-wise
+enum { kQRowJ = 0, kQRowC = 1, kQElem = 2 };
 
 template <typename QT>
+constexpr int rows_cs_of(int jt) {
+  // bounds the staged factor to 8 (bf16) or 4 (fp32) 8-value loads per lane
+  return (sizeof(QT) == 2 ? 1024 : 512) / jt > 512 ? 512 : (sizeof(QT) == 2 ? 1024 : 512) / jt;
+}
+
+static int rows_jt(int32_t r) {
+  const int jt = (r + 15) / 16;
+  return jt <= 1 ? 1 : jt <= 2 ? 2 : jt <= 4 ? 4 : 8;
+}
+static int rows_cs(int32_t r, int q_dtype) {
+  const int jt = rows_jt(r);
+  return q_dtype == QL_BF16 ? rows_cs_of<uint16_t>(jt) : rows_cs_of<float>(jt);
+}
+
+// 8 consecutive values of a factor row as fp32 (zero where !ok)
+template <typename QT>
+struct Vec8;
+template <>
+struct Vec8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ float get(int e, bool ok) const {
+    const uint32_t h = w[e >> 1];
+    return ok ? __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16)) : 0.0f;
+  }
+};
+template <>
+struct Vec8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const f32x4 *>(p);
+    b = *reinterpret_cast<const f32x4 *>(p + 4);
+  }
+  __device__ __forceinline__ float get(int e, bool ok) const {
+    return ok ? (e < 4 ? a[e] : b[e - 4]) : 0.0f;
+  }
+};
+
+template <int CS, int JT, typename QT, int QMODE>
 __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ P, int64_t M,
                                                    int64_t C, const QT *__restrict__ Q,
                                                    int64_t ldq_j, int64_t ldq_c, int32_t r,
-                                                   int64_t slice, float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint8_t qs[128 * kQsStride];
+                                                   float *__restrict__ partial) {
+  constexpr int QST = 2 * CS + 16;   // bytes per staged rank row
+  constexpr int JW = JT * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t qs[JW * QST];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int li = lane & 15, q = lane >> 4;
-  const int JT = (r + 15) >> 4;
-  const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + li;
-  const int64_t cb = (int64_t)blockIdx.y * slice;
-  const int64_t ce = cb + slice < C ? cb + slice : C;
-  f32x4 acc[8];
+  const int64_t c0 = (int64_t)blockIdx.y * CS;
+
+  // ---- factor loads (issued first) ----
+  constexpr int NV = JW * CS / 8 / 256;          // 8-value loads per lane
+  constexpr int NE = (QMODE == kQElem) ? JW * CS / 256 : 1;
+  Vec8<QT> qv[QMODE == kQElem ? 1 : NV];
+  float qe[NE];
+  if constexpr (QMODE == kQRowJ) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t *prow = P + mrow * C;
-  for (int64_t c0 = cb; c0 < ce; c0 += kMRowsChunk) {
-    for (int e = t; e < JT * 16 * kMRowsChunk; e += 256) {
-      const int j = e / kMRowsChunk, cc = e % kMRowsChunk;
+    for (int b = 0; b < NV; ++b) {
+      const int e = t + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
+      const int64_t c = c0 + 8 * c8;
+      const int jc = j < r ? j : r - 1;
+      const int64_t cc = c + 8 <= C ? c : C - 8;
+      qv[b].load(Q + (int64_t)jc * ldq_j + cc);
+    }
+  } else if constexpr (QMODE == kQRowC) {
+#pragma unroll
+    for (int b = 0; b < NV; ++b) {
+      const int e = t + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
+      const int64_t c = c0 + cc < C ? c0 + cc : C - 1;
+      const int jc = 8 * j8 + 8 <= r ? 8 * j8 : r - 8;
+      qv[b].load(Q + c * ldq_c + jc);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NE; ++b) {
+      const int e = t + 256 * b;
+      int j, cc;
+      if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
       const int64_t c = c0 + cc;
-      const float v = (j < r && c < ce) ? load_as_f32(Q, j * ldq_j + c * ldq_c) : 0.0f;
-      *reinterpret_cast<uint16_t *>(qs + j * kQsStride + 2 * cc) = f32_to_bf16_bits(v);
+      qe[b] = (j < r && c < C) ? load_as_f32(Q, j * ldq_j + c * ldq_c) : 0.0f;
     }
-    __syncthreads();
-    // all eight 16-byte loads of the chunk in flight before the matrix ops
-    u32x4 a[kMRowsChunk / 32];
+  }
+
+  // ---- P loads: row mrow, contraction c0 + 32 i + 8 q ----
+  const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + li;
+  const uint16_t *prow = P + (mrow < M ? mrow : M - 1) * C;
+  u32x4 a[CS / 32];
 #pragma unroll
-    for (int i = 0; i < kMRowsChunk / 32; ++i) {
-      const int64_t c = c0 + 32 * i + 8 * q;
-      a[i] = u32x4{0u, 0u, 0u, 0u};
-      if (mrow < M && c + 8 <= ce) a[i] = *reinterpret_cast<const u32x4 *>(prow + c);
-    }
+  for (int i = 0; i < CS / 32; ++i) {
+    const int64_t c = c0 + 32 * i + 8 * q;
+    a[i] = *reinterpret_cast<const u32x4 *>(prow + (c + 8 <= C ? c : C - 8));
+    if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- factor slice to LDS, bf16 [j][c] ----
+  if constexpr (QMODE == kQRowJ) {
 #pragma unroll
-    for (int i = 0; i < kMRowsChunk / 32; ++i) {
-#pragma unroll 1
-      for (int jt = 0; jt < JT; ++jt) {
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(qs + (16 * jt + li) * kQsStride +
-                                                         2 * (32 * i + 8 * q));
-        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                          __builtin_bit_cast(bf16x8, b), acc[jt],
-                                                          0, 0, 0);
-      }
+    for (int b = 0; b < NV; ++b) {
+      const int e = t + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
+      const bool ok = j < r && c0 + 8 * c8 + 8 <= C;
+      *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) =
+          u32x4{pack_bf16x2(qv[b].get(0, ok), qv[b].get(1, ok)),
+                pack_bf16x2(qv[b].get(2, ok), qv[b].get(3, ok)),
+                pack_bf16x2(qv[b].get(4, ok), qv[b].get(5, ok)),
+                pack_bf16x2(qv[b].get(6, ok), qv[b].get(7, ok))};
     }
-    __syncthreads();
+  } else if constexpr (QMODE == kQRowC) {
+#pragma unroll
+    for (int b = 0; b < NV; ++b) {
+      const int e = t + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
+      const bool ok = c0 + cc < C && 8 * j8 + 8 <= r;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        *reinterpret_cast<uint16_t *>(qs + (8 * j8 + jj) * QST + 2 * cc) =
+            f32_to_bf16_bits(qv[b].get(jj, ok));
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NE; ++b) {
+      const int e = t + 256 * b;
+      int j, cc;
+      if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
+      *reinterpret_cast<uint16_t *>(qs + j * QST + 2 * cc) = f32_to_bf16_bits(qe[b]);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[JT];
+#pragma unroll
+  for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CS / 32; ++i) {
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(qs + (16 * jt + li) * QST +
+                                                       2 * (32 * i + 8 * q));
+      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                        __builtin_bit_cast(bf16x8, b), acc[jt],
+                                                        0, 0, 0);
+    }
   }
   const int64_t mbase = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + 4 * q;
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
+  for (int jt = 0; jt < JT; ++jt) {
     const int j = 16 * jt + li;
-    if (jt >= JT || j >= r) continue;
+    if (j >= r) continue;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t m = mbase + v;
@@ -142,14 +248,22 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
   }
 }
 
-// out[e] = scale * sum_s partial[s][e], s in increasing order.
+// out[e] = scale * sum_s partial[s][e], s in increasing order (8 slices per
+// batch are loaded before they are added).
 __global__ __launch_bounds__(256) void k_reduce_slices(const float *__restrict__ partial, int S,
                                                        int64_t count, float scale,
                                                        float *__restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= count) return;
   float s = 0.0f;
-  for (int i = 0; i < S; ++i) s += partial[(int64_t)i * count + e];
+  for (int i0 = 0; i0 < S; i0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) v[b] = i0 + b < S ? partial[(int64_t)(i0 + b) * count + e] : 0.0f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      if (i0 + b < S) s += v[b];
+  }
   out[e] = scale * s;
 }
 
@@ -163,21 +277,17 @@ static int rows_slices(int64_t M, int64_t C) {
   return (int)s;
 }
 
-// Slices of the matrix-core rows kernel: about 512 workgroups, slices a
-// multiple of the 256-wide LDS chunk.
-static int mrows_slices(int64_t M, int64_t C) {
-  const int64_t mt = (M + kMRowsTile - 1) / kMRowsTile;
-  int64_t s = 512 / mt;
-  const int64_t max_s = (C + kMRowsChunk - 1) / kMRowsChunk;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return (int)s;
+// Slices of the matrix-core rows kernel: one per CS-wide piece of the
+// contraction (the partial buffer is sized for the fp32-factor case, which
+// has the narrower slices).
+static int mrows_slices(int64_t C, int32_t r, int q_dtype) {
+  return (int)((C + rows_cs(r, q_dtype) - 1) / rows_cs(r, q_dtype));
 }
 
 static bool rows_use_mfma(int p_dtype, int64_t C) { return p_dtype == QL_BF16 && C % 8 == 0; }
 
 size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r) {
-  const int64_t s1 = rows_slices(M, C), s2 = mrows_slices(M, C);
+  const int64_t s1 = rows_slices(M, C), s2 = mrows_slices(C, r, QL_F32);
   return (size_t)(s1 > s2 ? s1 : s2) * (size_t)M * (size_t)r;
 }
 
@@ -187,16 +297,32 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
   if (M <= 0) return QL_OK;
   int S;
   if (rows_use_mfma(p_dtype, C)) {
-    S = mrows_slices(M, C);
-    int64_t slice = (C + S - 1) / S;
-    slice = (slice + kMRowsChunk - 1) / kMRowsChunk * kMRowsChunk;
+    S = mrows_slices(C, r, q_dtype);
     const dim3 grid((unsigned)((M + kMRowsTile - 1) / kMRowsTile), (unsigned)S);
-    if (q_dtype == QL_BF16)
-      hipLaunchKernelGGL(k_rows_mfma<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t *)P, M,
-                         C, (const uint16_t *)Q, ldq_j, ldq_c, r, slice, partial);
-    else
-      hipLaunchKernelGGL(k_rows_mfma<float>, grid, dim3(256), 0, stream, (const uint16_t *)P, M, C,
-                         (const float *)Q, ldq_j, ldq_c, r, slice, partial);
+    const int jt = rows_jt(r);
+    // 8-value loads need the loaded factor rows 8-aligned (the factor base
+    // pointer is 16-byte aligned) and at least 8 long
+    int mode = kQElem;
+    if (ldq_c == 1 && C % 8 == 0 && ldq_j % 8 == 0 && C >= 8) mode = kQRowJ;
+    else if (ldq_j == 1 && r % 8 == 0 && ldq_c % 8 == 0) mode = kQRowC;
+#define QL_ROWS_M(JTV, QT, MODEV)                                                                \
+  hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, QT, MODEV>), grid, dim3(256), 0,     \
+                     stream, (const uint16_t *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r, partial)
+#define QL_ROWS_Q(JTV, QT)                                                                       \
+  do {                                                                                           \
+    if (mode == kQRowJ) QL_ROWS_M(JTV, QT, kQRowJ);                                              \
+    else if (mode == kQRowC) QL_ROWS_M(JTV, QT, kQRowC);                                         \
+    else QL_ROWS_M(JTV, QT, kQElem);                                                             \
+  } while (0)
+#define QL_ROWS_JT(JTV) \
+  do { if (q_dtype == QL_BF16) QL_ROWS_Q(JTV, uint16_t); else QL_ROWS_Q(JTV, float); } while (0)
+    if (jt == 1) QL_ROWS_JT(1);
+    else if (jt == 2) QL_ROWS_JT(2);
+    else if (jt == 4) QL_ROWS_JT(4);
+    else QL_ROWS_JT(8);
+#undef QL_ROWS_JT
+#undef QL_ROWS_Q
+#undef QL_ROWS_M
   } else {
     S = rows_slices(M, C);
     int64_t slice = (C + S - 1) / S;
@@ -272,83 +398,128 @@ __global__ __launch_bounds__(256) void k_lora_cols(const float *__restrict__ R, 
 
 // ---------------------------------------------------------------------------
 // cols on the matrix cores (bf16 P): D[j][c] = sum_m R^T[j][m] P[m][c] with
-// v_mfma_f32_16x16x32_bf16.  Per 64-token chunk the workgroup stages its
-// 64 x 64 tile of P in LDS ([m][c], 132-byte rows so that the column reads
-// below spread over all banks) and R^T as bf16 [j][m].  Wave w owns columns
-// 16w..16w+15 of the tile and every rank tile; its B operand (8 consecutive
-// tokens of one column) is gathered from LDS 16 bits at a time.
+// v_mfma_f32_16x16x32_bf16.  The workgroup owns 64 columns (wave w: columns
+// 16w..16w+15, all JT rank tiles) and one TM-token slice, in one round trip
+// with compile-time trip counts: the loads of R (fp32, 4 ranks per load when
+// r % 4 == 0) and of the P tile (16 bytes per lane) are all issued first,
+// then R^T is written to LDS as bf16 [j][m] and the P tile as [m][c]
+// (128-byte rows), one barrier, the MFMAs, and the fp32 partial sums.  The
+// B operand (8 consecutive tokens of one column) comes from gfx950's
+// transposing LDS read: for a group of 16 lanes naming rows m0..m0+3
+// (lanes 4e..4e+3 -> row m0+e, four columns each), output lane i receives
+// column i of those rows.  Within a row the four 32-byte column groups are
+// rotated by a row-dependent amount, so the 8 rows one read pass touches
+// (and the 2 rows one 16-lane store pass touches) hit distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kMColsTile = 64;
-constexpr int kMColsChunk = 64;
-constexpr int kPsStride = 132;                   // bytes per staged token row
-constexpr int kRsStride = kMColsChunk * 2 + 16;  // bytes per staged rank row
+constexpr int kMColsTM = 256;  // tokens per workgroup
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// byte offset of 16-byte piece h (columns 8h..8h+7) of staged token row m
+__device__ __forceinline__ int ps_off(int m, int h) {
+  const int pcg = ((h >> 1) + (m >> 1) + 2 * ((m >> 3) & 1)) & 3;
+  return m * 128 + ((2 * pcg + (h & 1)) << 4);
+}
+
+__device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int TM, int JT, bool RVEC>
 __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
                                                    int32_t r, const uint16_t *__restrict__ P,
-                                                   int64_t C, int64_t slice,
-                                                   float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint8_t ps[kMColsChunk * kPsStride];
-  __shared__ __attribute__((aligned(16))) uint8_t rs[128 * kRsStride];
+                                                   int64_t C, float *__restrict__ partial) {
+  constexpr int JW = JT * 16;
+  constexpr int RST = 2 * TM + 16;  // bytes per staged rank row
+  __shared__ __attribute__((aligned(16))) uint8_t ps[TM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t rs[JW * RST];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int li = lane & 15, q = lane >> 4;
-  const int JT = (r + 15) >> 4;
   const int64_t ct0 = (int64_t)blockIdx.x * kMColsTile;
-  const int64_t mb = (int64_t)blockIdx.y * slice;
-  const int64_t me = mb + slice < M ? mb + slice : M;
-  f32x4 acc[8];
+  const int64_t m0 = (int64_t)blockIdx.y * TM;
+
+  // ---- R loads: rows m0 .. m0 + TM, ranks 0 .. JW ----
+  constexpr int NR = RVEC ? TM * JW / 4 / 256 : TM * JW / 256;
+  f32x4 rv[RVEC ? NR : 1];
+  float re[RVEC ? 1 : NR];
+  if constexpr (RVEC) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int col = 16 * wave + li;
-  for (int64_t mc = mb; mc < me; mc += kMColsChunk) {
-    // P tile: 64 rows x 8 chunks of 16 B; stored as 4-byte words (132-byte rows)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = t + 256 * i;
-      const int row = id >> 3, ch = id & 7;
-      const int64_t m = mc + row, c = ct0 + 8 * ch;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m < me && c + 8 <= C) v = *reinterpret_cast<const u32x4 *>(P + m * C + c);
-      uint32_t *dst = reinterpret_cast<uint32_t *>(ps + row * kPsStride + 16 * ch);
-      dst[0] = v.x;
-      dst[1] = v.y;
-      dst[2] = v.z;
-      dst[3] = v.w;
+    for (int b = 0; b < NR; ++b) {
+      const int e = t + 256 * b, mm = e / (JW / 4), j4 = e % (JW / 4);
+      const int64_t m = m0 + mm < M ? m0 + mm : M - 1;
+      const int jc = 4 * j4 + 4 <= r ? 4 * j4 : r - 4;
+      rv[b] = *reinterpret_cast<const f32x4 *>(R + m * r + jc);
     }
-    for (int e = t; e < JT * 16 * kMColsChunk; e += 256) {
-      const int j = e / kMColsChunk, mm = e % kMColsChunk;
-      const int64_t m = mc + mm;
-      const float v = (j < r && m < me) ? R[m * r + j] : 0.0f;
-      *reinterpret_cast<uint16_t *>(rs + j * kRsStride + 2 * mm) = f32_to_bf16_bits(v);
+  } else {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      const int e = t + 256 * b, mm = e / JW, j = e % JW;
+      re[b] = (m0 + mm < M && j < r) ? R[(m0 + mm) * r + j] : 0.0f;
     }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kMColsChunk; kk += 32) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t *>(ps + (kk + 8 * q + 2 * e) * kPsStride + 2 * col);
-        const uint32_t hi = *reinterpret_cast<const uint16_t *>(ps + (kk + 8 * q + 2 * e + 1) * kPsStride + 2 * col);
-        bw[e] = lo | (hi << 16);
-      }
-      const u32x4 b = u32x4{bw[0], bw[1], bw[2], bw[3]};
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        if (jt < JT) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4 *>(rs + (16 * jt + li) * kRsStride + 2 * (kk + 8 * q));
-          acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                            __builtin_bit_cast(bf16x8, b), acc[jt],
-                                                            0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
   }
-  const int64_t c = ct0 + col;
+  // ---- P tile loads: rows (t >> 3) + 32 i, piece t & 7 ----
+  const int prow = t >> 3, ph = t & 7;
+  const int64_t pc = ct0 + 8 * ph;
+  const bool cok = pc + 8 <= C;
+  u32x4 pv[TM / 32];
+#pragma unroll
+  for (int i = 0; i < TM / 32; ++i) {
+    const int64_t m = m0 + prow + 32 * i;
+    pv[i] = *reinterpret_cast<const u32x4 *>(P + (m < M ? m : M - 1) * C + (cok ? pc : C - 8));
+    if (m >= M || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // ---- to LDS ----
+  if constexpr (RVEC) {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      const int e = t + 256 * b, mm = e / (JW / 4), j4 = e % (JW / 4);
+      const bool ok = m0 + mm < M && 4 * j4 + 4 <= r;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<uint16_t *>(rs + (4 * j4 + jj) * RST + 2 * mm) =
+            f32_to_bf16_bits(ok ? rv[b][jj] : 0.0f);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      const int e = t + 256 * b, mm = e / JW, j = e % JW;
+      *reinterpret_cast<uint16_t *>(rs + j * RST + 2 * mm) = f32_to_bf16_bits(re[b]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TM / 32; ++i)
+    *reinterpret_cast<u32x4 *>(ps + ps_off(prow + 32 * i, ph)) = pv[i];
+  __syncthreads();
+
+  f32x4 acc[JT];
+#pragma unroll
+  for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read supplier address: rows 8q + (li >> 2) (+4), columns
+  // 16 wave + 4 (li & 3)
+  const int tr_col = 16 * wave + 4 * (li & 3);
+  const int tr_h = tr_col >> 3, tr_b = 2 * (tr_col & 7);
+#pragma unroll
+  for (int kk = 0; kk < TM; kk += 32) {
+    const int row = kk + 8 * q + (li >> 2);
+    const u32x2 lo = lds_tr16(ps + ps_off(row, tr_h) + tr_b);
+    const u32x2 hi = lds_tr16(ps + ps_off(row + 4, tr_h) + tr_b);
+    const u32x4 b = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const u32x4 a =
+          *reinterpret_cast<const u32x4 *>(rs + (16 * jt + li) * RST + 2 * (kk + 8 * q));
+      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), acc[jt],
+                                                        0, 0, 0);
+    }
+  }
+  const int64_t c = ct0 + 16 * wave + li;
   if (c < C) {
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt >= JT) continue;
+    for (int jt = 0; jt < JT; ++jt) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * jt + 4 * q + v;
@@ -358,7 +529,8 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
   }
 }
 
-// out = scale * sum_s partial[s][j][c]; written as [r][C] or transposed [C][r].
+// out = scale * sum_s partial[s][j][c] (s in increasing order, 8 slices per
+// batch loaded before they are added); written as [r][C] or transposed [C][r].
 __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ partial, int S,
                                                      int32_t r, int64_t C, float scale,
                                                      int c_major, float *__restrict__ out) {
@@ -366,7 +538,14 @@ __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ p
   const int64_t count = (int64_t)r * C;
   if (e >= count) return;
   float s = 0.0f;
-  for (int i = 0; i < S; ++i) s += partial[(int64_t)i * count + e];
+  for (int i0 = 0; i0 < S; i0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) v[b] = i0 + b < S ? partial[(int64_t)(i0 + b) * count + e] : 0.0f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      if (i0 + b < S) s += v[b];
+  }
   const int64_t j = e / C, c = e % C;
   if (c_major)
     out[c * r + j] = scale * s;
@@ -384,19 +563,13 @@ static int cols_slices(int64_t M, int64_t C) {
   return (int)s;
 }
 
-static int mcols_slices(int64_t M, int64_t C) {
-  const int64_t ct = (C + kMColsTile - 1) / kMColsTile;
-  int64_t s = 768 / ct;
-  const int64_t max_s = (M + kMColsChunk - 1) / kMColsChunk;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return (int)s;
-}
+// Token slices of the matrix-core cols kernel: one per TM tokens.
+static int mcols_slices(int64_t M) { return (int)((M + kMColsTM - 1) / kMColsTM); }
 
 static bool cols_use_mfma(int p_dtype, int64_t C) { return p_dtype == QL_BF16 && C % 8 == 0; }
 
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
-  const int64_t s1 = cols_slices(M, C), s2 = mcols_slices(M, C);
+  const int64_t s1 = cols_slices(M, C), s2 = mcols_slices(M);
   return (size_t)(s1 > s2 ? s1 : s2) * (size_t)r * (size_t)C;
 }
 
@@ -406,12 +579,20 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   if (C <= 0) return QL_OK;
   int S;
   if (cols_use_mfma(p_dtype, C)) {
-    S = mcols_slices(M, C);
-    int64_t slice = (M + S - 1) / S;
-    slice = (slice + kMColsChunk - 1) / kMColsChunk * kMColsChunk;
+    S = mcols_slices(M);
     const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
-    hipLaunchKernelGGL(k_cols_mfma, grid, dim3(256), 0, stream, R, M, r, (const uint16_t *)P, C,
-                       slice, partial);
+    const bool rvec = r % 4 == 0;
+#define QL_COLS_M(JTV, RV)                                                                       \
+  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, RV>), grid, dim3(256), 0, stream, R, M, r,     \
+                     (const uint16_t *)P, C, partial)
+#define QL_COLS_JT(JTV) do { if (rvec) QL_COLS_M(JTV, true); else QL_COLS_M(JTV, false); } while (0)
+    const int jt = rows_jt(r);
+    if (jt == 1) QL_COLS_JT(1);
+    else if (jt == 2) QL_COLS_JT(2);
+    else if (jt == 4) QL_COLS_JT(4);
+    else QL_COLS_JT(8);
+#undef QL_COLS_JT
+#undef QL_COLS_M
   } else {
     S = cols_slices(M, C);
     const int64_t slice = (M + S - 1) / S;
