@@ -291,3 +291,40 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* One AdamW step over n fp32 parameters, in place.  [gc4] "显存计算实战" and
+ * "分页优化器": the LoRA factors are trained with AdamW (torch.optim.AdamW,
+ * lr 2e-4) holding fp32 moments, 8 bytes per trainable parameter; [L9] 9.4:
+ * two states (momentum and variance) per parameter.  The pages do not write
+ * the update out; it is the published AdamW definition (decoupled weight
+ * decay, bias-corrected moments), every operation an fp32 rounding, none
+ * fused, in this order:
+ *   p  = p * decay                         decay = fp32(1 - lr * wd)
+ *   m  = b1 * m + (1 - b1) * g
+ *   v  = b2 * v + (1 - b2) * (g * g)
+ *   p  = p - step_size * (m / (sqrt(v) / bc2_sqrt + eps))
+ * with the scalars computed once in fp64 and rounded to fp32 by the caller:
+ *   step_size = lr / (1 - b1^t),  bc2_sqrt = sqrt(1 - b2^t).
+ * p_bf16 (optional) receives the round-to-nearest-even bf16 of the new p. */
+void orc_adamw_step(float *p, const float *g, float *m, float *v, uint16_t *p_bf16, int64_t n,
+                    float decay, float b1, float omb1, float b2, float omb2, float eps,
+                    float step_size, float bc2_sqrt) {
+  for (int64_t i = 0; i < n; ++i) {
+    float pi = p[i] * decay;
+    float mi = b1 * m[i] + omb1 * g[i];
+    float gg = g[i] * g[i];
+    float vi = b2 * v[i] + omb2 * gg;
+    float denom = sqrtf(vi) / bc2_sqrt + eps;
+    float upd = mi / denom;
+    pi = pi - step_size * upd;
+    p[i] = pi;
+    m[i] = mi;
+    v[i] = vi;
+    if (p_bf16) { /* round to nearest even, as orc_round_bf16 */
+      uint32_t u;
+      memcpy(&u, &pi, 4);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      p_bf16[i] = (uint16_t)(u >> 16);
+    }
+  }
+}

@@ -58,6 +58,8 @@ def _load():
     lib.orc_linear_fwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p]
     lib.orc_linear_bwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p,
                                    _p, _i64, _p, _p, _p, _p, _p]
+    lib.orc_adamw_step.argtypes = [_p, _p, _p, _p, _p, _i64, _f32, _f32, _f32, _f32, _f32, _f32,
+                                   _f32, _f32]
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -249,3 +251,31 @@ def linear_bwd(x, w_hat: np.ndarray, A, B, dy, alpha: float, r: int, rows=None, 
     _load().orc_linear_bwd(M, N, K, r, s, _ptr(xd), _ptr(wf), _ptr(Ad), _ptr(Bd), _ptr(dyd),
                            _ptr(rows_arr), nr, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ub), _ptr(gb))
     return dx, dA, dB
+
+
+def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                  step: int) -> dict:
+    """The fp32 scalars of one AdamW step, computed in fp64 and rounded once
+    (the bias corrections 1 - beta^t at step t >= 1)."""
+    if step < 1:
+        raise ValueError("step counts from 1")
+    f = np.float32
+    return dict(decay=f(1.0 - lr * weight_decay), b1=f(beta1), omb1=f(1.0 - beta1), b2=f(beta2),
+                omb2=f(1.0 - beta2), eps=f(eps), step_size=f(lr / (1.0 - beta1 ** step)),
+                bc2_sqrt=f(math.sqrt(1.0 - beta2 ** step)))
+
+
+def adamw_step(p, g, m, v, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8, weight_decay: float = 0.01, step: int = 1, want_bf16=False):
+    """[gc4] / [L9] 9.4: one AdamW step with fp32 moments, in fp32 arithmetic,
+    on copies of p, m, v.  Returns (p, m, v, p_bf16 bits or None)."""
+    p = np.array(p, dtype=np.float32, copy=True).reshape(-1)
+    m = np.array(m, dtype=np.float32, copy=True).reshape(-1)
+    v = np.array(v, dtype=np.float32, copy=True).reshape(-1)
+    g = np.ascontiguousarray(g, dtype=np.float32).reshape(-1)
+    sc = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step)
+    pb = np.empty(p.size, dtype=np.uint16) if want_bf16 else None
+    _load().orc_adamw_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(pb), p.size, sc["decay"],
+                           sc["b1"], sc["omb1"], sc["b2"], sc["omb2"], sc["eps"],
+                           sc["step_size"], sc["bc2_sqrt"])
+    return p, m, v, pb

@@ -471,3 +471,74 @@ def test_forward_brute_force_exact_small(orc):
             ref = sum(frac(x[m, k]) * frac(w[n, k]) for k in range(8)) + s * sum(
                 uu[j] * frac(B[n, j]) for j in range(r))
             assert abs(y[m, n] - float(ref)) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# AdamW on the LoRA factors ([gc4] "显存计算实战" / "分页优化器": AdamW with
+# fp32 moments, 8 bytes per trainable parameter; [L9] 9.4: two states each)
+# ---------------------------------------------------------------------------
+def test_adamw_first_step_closed_form(orc):
+    """At t = 1 the bias-corrected moments are exactly g and g^2, so the
+    step is p (1 - lr wd) - lr g / (|g| + eps)."""
+    rng = np.random.default_rng(11)
+    p = rng.standard_normal(4096).astype(np.float32)
+    g = (rng.standard_normal(4096) * 10.0 ** rng.integers(-6, 2, 4096)).astype(np.float32)
+    g[:8] = 0.0
+    lr, wd, eps = 2e-4, 0.01, 1e-8
+    p1, m1, v1, _ = orc.adamw_step(p, g, np.zeros_like(p), np.zeros_like(p), lr, eps=eps,
+                                   weight_decay=wd, step=1)
+    ref = p.astype(np.float64) * (1 - lr * wd) - lr * g / (np.abs(g.astype(np.float64)) + eps)
+    np.testing.assert_allclose(p1, ref, rtol=2e-6, atol=1e-9)
+    assert np.all(p1[:8] == np.float32(p[:8] * np.float32(1 - lr * wd)))  # g = 0: decay only
+    np.testing.assert_allclose(m1, 0.1 * g.astype(np.float64), rtol=2e-7, atol=0)
+    np.testing.assert_allclose(v1, 0.001 * g.astype(np.float64) ** 2, rtol=4e-7, atol=0)
+
+
+def test_adamw_matches_torch_over_steps(orc):
+    """Five steps against torch.optim.AdamW (CPU, fp32, single-tensor path),
+    an independent implementation of the same definition.  Each step starts
+    both from torch's current state, so only that step's roundings differ."""
+    rng = np.random.default_rng(12)
+    n = 1000
+    p0 = rng.standard_normal(n).astype(np.float32)
+    grads = [rng.standard_normal(n).astype(np.float32) * (0.1 ** k) for k in range(5)]
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.AdamW([tp], lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                            foreach=False)
+    for t, g in enumerate(grads, start=1):
+        st = opt.state.get(tp, {})
+        p = tp.detach().numpy().copy()
+        m = st["exp_avg"].numpy().copy() if st else np.zeros(n, np.float32)
+        v = st["exp_avg_sq"].numpy().copy() if st else np.zeros(n, np.float32)
+        tp.grad = torch.from_numpy(g.copy())
+        opt.step()
+        p1, m1, v1, _ = orc.adamw_step(p, g, m, v, 2e-4, step=t)
+        st = opt.state[tp]
+        # torch forms m + (1 - b1)(g - m) (a lerp), the definition b1 m + (1 - b1) g:
+        # equal in exact arithmetic, so they differ by the terms' roundings
+        terms = 0.9 * np.abs(m.astype(np.float64)) + 0.1 * np.abs(g.astype(np.float64))
+        assert np.all(np.abs(m1 - st["exp_avg"].numpy()) <= 3e-7 * terms)
+        np.testing.assert_allclose(v1, st["exp_avg_sq"].numpy(), rtol=4e-7, atol=0)
+        np.testing.assert_allclose(p1, tp.detach().numpy(), rtol=3e-7, atol=0)
+
+
+def test_adamw_special_cases(orc):
+    rng = np.random.default_rng(13)
+    p = rng.standard_normal(257).astype(np.float32)
+    g = rng.standard_normal(257).astype(np.float32)
+    m = rng.standard_normal(257).astype(np.float32)
+    v = np.abs(rng.standard_normal(257)).astype(np.float32)
+    # lr = 0: parameters unchanged, moments still advance
+    p1, m1, v1, _ = orc.adamw_step(p, g, m, v, 0.0, step=3)
+    assert np.array_equal(p1, p)
+    assert not np.array_equal(m1, m) and not np.array_equal(v1, v)
+    # zero moments and zero gradient: only the decoupled weight decay acts
+    z = np.zeros_like(p)
+    p2, m2, v2, _ = orc.adamw_step(p, z, z, z, 1e-3, weight_decay=0.1, step=7)
+    assert np.array_equal(p2, p * np.float32(1 - 1e-3 * 0.1))
+    assert np.all(m2 == 0) and np.all(v2 == 0)
+    # the bf16 copy is the RNE of the new parameters
+    p3, _, _, pb = orc.adamw_step(p, g, m, v, 2e-4, step=2, want_bf16=True)
+    assert np.array_equal(pb, orc.round_bf16(p3))
+    with pytest.raises(ValueError):
+        orc.adamw_step(p, g, m, v, 2e-4, step=0)
