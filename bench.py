@@ -202,12 +202,54 @@ def main():
                           "launch": "qlora_linear_fwd_u gate 2048x14336x4096 (one GEMM launch)",
                           "ms_per_launch": round(fwd_ms, 4), "flop_per_launch": fwd_flops}
     log(f"fwd gate {fwd_ms:.3f} ms {ach:.1f} TFLOP/s")
+
+    # ---------------- every row of the path, per projection -------------------
+    # Each row is timed through the entry points alone (HIP events, 30 calls):
+    #   a5 forward GEMM      = qlora_linear_fwd_u (one launch)
+    #   a4 u = x A^T         = qlora_linear_fwd - qlora_linear_fwd_u
+    #   a6 LoRA gradients    = qlora_linear_bwd(u_saved, dx = NULL)   (g, dB, dA)
+    #   a7 input gradient    = qlora_linear_bwd(u_saved) - the above
+    # against MFMA peak (a5, a7) or HBM peak (a4, a6: bytes of x / dy read).
+    rows = {}
+    for p in projs:
+        N, K = p["N"], p["K"]
+        t_fwd = timed(lambda: q.qlora_linear_fwd(p["x"], p["W"], p["A"], p["B"], alpha, y=p["y"],
+                                                 u_save=p["u"], ws=p["wsf"]), 30, 3)
+        t_fwdu = timed(lambda: q.qlora_linear_fwd_u(p["x"], p["W"], p["u"], p["B"], alpha,
+                                                    y=p["y"]), 30, 3)
+        t_bwd = timed(lambda: q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha,
+                                                 u_saved=p["u"], dx=p["dx"], dA=p["dA"],
+                                                 dB=p["dB"], ws=p["wsb"]), 30, 3)
+        t_lora = timed(lambda: q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha,
+                                                  u_saved=p["u"], need_dx=False, dA=p["dA"],
+                                                  dB=p["dB"], ws=p["wsb"]), 30, 3)
+        a5 = 2 * M * N * K + 2 * M * r * N
+        a7 = 2 * M * N * K + 2 * M * r * K
+        by_x, by_dy = M * K * 2, M * N * 2
+        rec = {
+            "a4_u": {"us": round((t_fwd - t_fwdu) * 1e3, 2), "bytes": by_x},
+            "a5_fwd_gemm": {"us": round(t_fwdu * 1e3, 2), "flop": a5},
+            "a6_lora_grads": {"us": round(t_lora * 1e3, 2), "bytes": by_x + 2 * by_dy},
+            "a7_dx_gemm": {"us": round((t_bwd - t_lora) * 1e3, 2), "flop": a7},
+        }
+        for k, v in rec.items():
+            sec = v["us"] * 1e-6
+            if "flop" in v:
+                v["TFLOPs"] = round(v["flop"] / sec / 1e12, 1)
+                v["frac_mfma"] = round(v["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+            else:
+                v["GBps"] = round(v["bytes"] / sec / 1e9, 1)
+                v["frac_hbm"] = round(v["GBps"] / PEAK_HBM_GBS, 4)
+        rows[p["name"]] = rec
+        log(f"rows {p['name']}: " + ", ".join(f"{k} {v['us']} us" for k, v in rec.items()))
+    result["rows"] = rows
     del projs, g
     torch.cuda.empty_cache()
 
     if not args.no_extras:
         result["decode_gemv"] = bench_decode(q, si, dev)
         result["quantize"] = bench_quantize(q, si, dev)
+        result["optimizer"] = bench_adamw(q, si, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(si, M, r, alpha)
     print(json.dumps(result), flush=True)
@@ -243,6 +285,43 @@ def bench_decode(q, si, dev, copies=64, iters=1000):
                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s packed")
     del Ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_adamw(q, si, dev):
+    """One AdamW step over all LoRA factors of an 8B-shaped model (r = 16 on
+    q, k, v, o, gate, up, down of 32 layers) kept as one flat fp32 buffer
+    with fp32 moments and a bf16 copy for the layers: HBM-bound, 30 bytes per
+    parameter (p, g, m, v read; p, m, v, bf16 p written)."""
+    cfg = si.WEIGHTSET_8B
+    r = 16
+    n = 0
+    for _ in range(cfg["layers"]):
+        for (N, K) in cfg["shapes"].values():
+            n += r * K + N * r
+    n = (n + 3) // 4 * 4
+    gen = torch.Generator(device=dev).manual_seed(7)
+    p = torch.randn(n, device=dev, generator=gen) * 0.01
+    g = torch.randn(n, device=dev, generator=gen) * 1e-3
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    state = {"t": 0}
+
+    def step():
+        state["t"] += 1
+        q.adamw_step(p, g, m, v, lr=2e-4, step=state["t"], param_bf16=pb)
+
+    ms = timed(step, 50, 5)
+    nbytes = 30 * n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"adamw {n} params: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    out = {"workload": "AdamW step over an 8B-shaped model's LoRA factors (r=16 on q,k,v,o,gate,"
+                       "up,down x 32 layers), fp32 params and moments + bf16 copy",
+           "params": n, "us_per_step": round(ms * 1e3, 2), "bytes_per_step": nbytes,
+           "GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    del p, g, m, v, pb
     torch.cuda.empty_cache()
     return out
 

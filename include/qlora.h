@@ -194,6 +194,42 @@ int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M
                      int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
                      float *dB, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Gradient accumulation (Gemma lesson 9, sec. 9.4.1: several forward and
+ * backward passes add their gradients before one optimizer update): as
+ * qlora_linear_bwd, but dA and dB receive dA += g^T x and dB += s dy^T u
+ * (one fp32 addition per element) instead of being overwritten; dx is still
+ * overwritten.  The caller zeroes dA and dB before the first micro-batch.
+ */
+int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                         const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                         int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                         float *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One AdamW step over n fp32 parameters, in place (gufacode fine-tuning
+ * chapter 4, "显存计算实战" and "分页优化器": the LoRA factors train with
+ * AdamW holding fp32 moments, 8 bytes per parameter; Gemma lesson 9, sec.
+ * 9.4: two states per parameter).  The pages do not write the update out;
+ * it is the published AdamW definition, every operation one fp32 rounding,
+ * none fused, in this order:
+ *     p = p * fp32(1 - lr wd)
+ *     m = b1 m + (1 - b1) g,   v = b2 v + (1 - b2) (g g)
+ *     p = p - step_size * (m / (sqrt(v) / bc2_sqrt + eps))
+ * with step_size = fp32(lr / (1 - b1^t)) and bc2_sqrt = fp32(sqrt(1 - b2^t))
+ * computed in fp64 from the arguments (t = step >= 1).
+ *   param, grad, exp_avg, exp_avg_sq  device fp32 [n], 16-byte aligned
+ *   param_bf16  device bf16 [n] receiving the round-to-nearest-even copy of
+ *               the new param (what the layer reads as A or B), 8-byte
+ *               aligned, or NULL
+ * Errors: QL_EINVAL (n < 0, step < 1, a null pointer, b1 or b2 outside
+ * [0, 1), eps <= 0, lr or wd NaN), QL_EALIGN, QL_EHIP.  n == 0 enqueues
+ * nothing.
+ */
+int ql_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq,
+                  uint16_t *param_bf16, int64_t n, double lr, double beta1, double beta2,
+                  double eps, double weight_decay, int64_t step, void *stream);
+
 /* Host only: a static string describing a status code. */
 const char *ql_strerror(int status);
 

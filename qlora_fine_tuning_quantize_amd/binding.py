@@ -23,8 +23,8 @@ NF4_BLOCK, DQ_BLOCK = 64, 256
 
 # every extern "C" symbol declared in include/qlora.h
 EXPORTED = ("ql_nf4_sizes", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
-            "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "ql_strerror",
-            "ql_abi_version")
+            "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "qlora_linear_bwd_acc",
+            "ql_adamw_step", "ql_strerror", "ql_abi_version")
 
 
 class QlNf4(ctypes.Structure):
@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd_u.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [p, p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, p, p, sz, p]
     L.qlora_linear_bwd.restype = ctypes.c_int
+    L.qlora_linear_bwd_acc.argtypes = L.qlora_linear_bwd.argtypes
+    L.qlora_linear_bwd_acc.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    L.ql_adamw_step.argtypes = [p, p, p, p, p, i64, f64, f64, f64, f64, f64, i64, p]
+    L.ql_adamw_step.restype = ctypes.c_int
     L.ql_strerror.argtypes = [ctypes.c_int]
     L.ql_strerror.restype = ctypes.c_char_p
     L.ql_abi_version.restype = ctypes.c_int
@@ -227,8 +232,10 @@ def qlora_linear_bwd(dy: torch.Tensor, x: torch.Tensor, W: NF4Weight, A: torch.T
                      B: torch.Tensor, alpha: float, u_saved: torch.Tensor | None = None,
                      need_dx: bool = True, dx: torch.Tensor | None = None,
                      dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
-                     ws: torch.Tensor | None = None):
-    """Returns (dx | None, dA fp32 [r, K], dB fp32 [N, r]); no base-weight gradient."""
+                     ws: torch.Tensor | None = None, accumulate: bool = False):
+    """Returns (dx | None, dA fp32 [r, K], dB fp32 [N, r]); no base-weight gradient.
+    accumulate: add into the given dA and dB (gradient accumulation) instead of
+    overwriting them."""
     M, K = x.shape
     r = A.shape[0]
     N = W.rows
@@ -238,14 +245,32 @@ def qlora_linear_bwd(dy: torch.Tensor, x: torch.Tensor, W: NF4Weight, A: torch.T
         dx = torch.empty((M, K), dtype=x.dtype, device=dev)
     if not need_dx:
         dx = None
+    if accumulate and (dA is None or dB is None):
+        raise ValueError("accumulate needs the dA and dB to add into")
     dA = dA if dA is not None else torch.empty((r, K), dtype=torch.float32, device=dev)
     dB = dB if dB is not None else torch.empty((N, r), dtype=torch.float32, device=dev)
     if ws is None:
         ws = workspace(QL_OP_BWD, M, N, K, r, dev)
     st = W.struct()
-    _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), _dtype_code(x.dtype), M, ctypes.byref(st),
-                                  _ptr(A), _ptr(B), _dtype_code(A.dtype), r, float(alpha),
-                                  _ptr(u_saved), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
-                                  ws.numel(), _stream(dev)),
-           "qlora_linear_bwd")
+    fn = lib().qlora_linear_bwd_acc if accumulate else lib().qlora_linear_bwd
+    _check(fn(_ptr(dy), _ptr(x), _dtype_code(x.dtype), M, ctypes.byref(st), _ptr(A), _ptr(B),
+              _dtype_code(A.dtype), r, float(alpha), _ptr(u_saved), _ptr(dx), _ptr(dA), _ptr(dB),
+              _ptr(ws), ws.numel(), _stream(dev)),
+           "qlora_linear_bwd_acc" if accumulate else "qlora_linear_bwd")
     return dx, dA, dB
+
+
+def adamw_step(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor,
+               exp_avg_sq: torch.Tensor, lr: float, step: int, beta1: float = 0.9,
+               beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01,
+               param_bf16: torch.Tensor | None = None) -> None:
+    """One AdamW step in place on fp32 param / exp_avg / exp_avg_sq (contiguous,
+    same length as grad); param_bf16, if given, receives the bf16 copy."""
+    for t in (param, grad, exp_avg, exp_avg_sq):
+        assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == param.numel()
+    if param_bf16 is not None:
+        assert param_bf16.dtype == torch.bfloat16 and param_bf16.numel() == param.numel()
+    _check(lib().ql_adamw_step(_ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq),
+                               _ptr(param_bf16), param.numel(), float(lr), float(beta1),
+                               float(beta2), float(eps), float(weight_decay), int(step),
+                               _stream(param.device)), "ql_adamw_step")

@@ -108,7 +108,7 @@ int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const voi
 
 extern "C" {
 
-int ql_abi_version(void) { return 101; }
+int ql_abi_version(void) { return 102; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -231,10 +231,10 @@ int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4
                            s);
 }
 
-int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
-                     const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
-                     int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
-                     float *dB, void *ws, size_t ws_bytes, void *stream) {
+static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                      const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                      int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                      float *dB, void *ws, size_t ws_bytes, void *stream, bool accumulate) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
   if (!dy || !x || !dA || !dB) return QL_EINVAL;
@@ -263,16 +263,48 @@ int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M
   st = launch_lora_rows_ws(dy, act_dtype, M, N, B, lora_dtype, 1, r, r, sc_lora, g, rows_partial, s);
   if (st) return st;
   // dB[n][j] = s sum_m dy[m][n] u[m][j]
-  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s);
+  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s, accumulate);
   if (st) return st;
   // dA[j][k] = sum_m g[m][j] x[m][k]
-  st = launch_lora_cols(g, M, r, x, act_dtype, K, 1.0f, false, dA, cols_partial, s);
+  st = launch_lora_cols(g, M, r, x, act_dtype, K, 1.0f, false, dA, cols_partial, s, accumulate);
   if (st) return st;
   if (!dx) return QL_OK;
   if (act_dtype == QL_BF16 && gemm_dx_supported(N, K))
     return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
                           (uint16_t *)dx, s);
   return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
+}
+
+int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                     const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                     int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                     float *dB, void *ws, size_t ws_bytes, void *stream) {
+  return linear_bwd(dy, x, act_dtype, M, W, A, B, lora_dtype, r, alpha, u_saved, dx, dA, dB, ws,
+                    ws_bytes, stream, false);
+}
+
+int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                         const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                         int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
+                         float *dB, void *ws, size_t ws_bytes, void *stream) {
+  return linear_bwd(dy, x, act_dtype, M, W, A, B, lora_dtype, r, alpha, u_saved, dx, dA, dB, ws,
+                    ws_bytes, stream, true);
+}
+
+int ql_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq,
+                  uint16_t *param_bf16, int64_t n, double lr, double beta1, double beta2,
+                  double eps, double weight_decay, int64_t step, void *stream) {
+  if (n < 0 || step < 1) return QL_EINVAL;
+  if (n == 0) return QL_OK;
+  if (!param || !grad || !exp_avg || !exp_avg_sq) return QL_EINVAL;
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      (param_bf16 && ((uintptr_t)param_bf16 & 7) != 0))
+    return QL_EALIGN;
+  if (!(lr == lr) || !(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) ||
+      !(eps > 0.0) || !(weight_decay == weight_decay))
+    return QL_EINVAL;
+  return launch_adamw(param, grad, exp_avg, exp_avg_sq, param_bf16, n, lr, beta1, beta2, eps,
+                      weight_decay, step, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -28,9 +28,10 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
                         int q_dtype, int64_t ldq_j, int64_t ldq_c, int32_t r, float scale,
                         float *out, float *partial, hipStream_t stream, int *slices = nullptr);
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r);
+// accumulate: out += result instead of out = result
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
-                     hipStream_t stream);
+                     hipStream_t stream, bool accumulate = false);
 
 // simple.hip: fp32-accumulating tiled kernels for any activation dtype.
 int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
@@ -54,5 +55,10 @@ bool gemm_dx_supported(int64_t N, int64_t K);
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
                    uint16_t *dx, hipStream_t stream);
+
+// optim.hip: one AdamW step (scalars from the fp64 hyperparameters)
+int launch_adamw(float *p, const float *g, float *m, float *v, uint16_t *p_bf16, int64_t n,
+                 double lr, double beta1, double beta2, double eps, double weight_decay,
+                 int64_t step, hipStream_t stream);
 
 }  // namespace qlora

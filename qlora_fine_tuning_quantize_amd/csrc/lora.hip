@@ -530,10 +530,12 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
 }
 
 // out = scale * sum_s partial[s][j][c] (s in increasing order, 8 slices per
-// batch loaded before they are added); written as [r][C] or transposed [C][r].
+// batch loaded before they are added); written as [r][C] or transposed [C][r],
+// or added to what out holds (accumulate != 0, one fp32 addition).
 __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ partial, int S,
                                                      int32_t r, int64_t C, float scale,
-                                                     int c_major, float *__restrict__ out) {
+                                                     int c_major, int accumulate,
+                                                     float *__restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t count = (int64_t)r * C;
   if (e >= count) return;
@@ -547,10 +549,8 @@ __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ p
       if (i0 + b < S) s += v[b];
   }
   const int64_t j = e / C, c = e % C;
-  if (c_major)
-    out[c * r + j] = scale * s;
-  else
-    out[e] = scale * s;
+  const int64_t o = c_major ? c * r + j : e;
+  out[o] = accumulate ? out[o] + scale * s : scale * s;
 }
 
 static int cols_slices(int64_t M, int64_t C) {
@@ -575,7 +575,7 @@ size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
 
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool accumulate) {
   if (C <= 0) return QL_OK;
   int S;
   if (cols_use_mfma(p_dtype, C)) {
@@ -607,7 +607,7 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   QL_HIP_CHECK_LAUNCH();
   const int64_t count = (int64_t)r * C;
   hipLaunchKernelGGL(k_reduce_cols, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
-                     partial, S, r, C, scale, out_c_major ? 1 : 0, out);
+                     partial, S, r, C, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0, out);
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 101
+    assert L.ql_abi_version() == 102
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -170,6 +170,27 @@ def test_linear_bwd_rejects_bad_arguments():
     assert bwd(dx=FAKE + 4) == b.QL_EALIGN
     assert bwd(M=-1) == b.QL_EINVAL
     assert bwd(ws_bytes=1024) == b.QL_EWORKSPACE
+
+
+@no_gpu
+def test_adamw_rejects_bad_arguments():
+    L = q.lib()
+
+    def adam(n=8, step=1, p=FAKE, bf=None, b1=0.9, b2=0.999, eps=1e-8, lr=2e-4):
+        return L.ql_adamw_step(ctypes.c_void_p(p) if p else None, ctypes.c_void_p(FAKE),
+                               ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                               ctypes.c_void_p(bf) if bf else None, n, lr, b1, b2, eps, 0.01,
+                               step, None)
+    assert adam(n=-1) == b.QL_EINVAL
+    assert adam(step=0) == b.QL_EINVAL
+    assert adam(p=0) == b.QL_EINVAL
+    assert adam(p=FAKE + 4) == b.QL_EALIGN
+    assert adam(bf=FAKE + 2) == b.QL_EALIGN
+    assert adam(b1=1.0) == b.QL_EINVAL
+    assert adam(b2=-0.1) == b.QL_EINVAL
+    assert adam(eps=0.0) == b.QL_EINVAL
+    assert adam(lr=float("nan")) == b.QL_EINVAL
+    assert adam(n=0) == b.QL_OK  # nothing to enqueue
 
 
 def test_strerror_and_python_errors():
