@@ -59,15 +59,18 @@ QuantWs quant_ws(int64_t n) {
   return w;
 }
 
+// The split-K partial tiles of a GEMM start at `rows`: the LoRA partials
+// stored there are dead once the GEMM (issued later on the same stream) runs.
 struct FwdWs {
   size_t u, rows, total;
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
-  (void)N;
   FwdWs w;
   w.u = 0;
   w.rows = round_up((size_t)M * r * 4);
   w.total = w.rows + round_up(lora_rows_partial_floats(M, K, r) * 4);
+  const size_t gemm_end = w.rows + round_up(gemm_fwd_partial_floats(M, N, K) * 4);
+  if (gemm_end > w.total) w.total = gemm_end;
   return w;
 }
 
@@ -87,6 +90,10 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   size_t cols_f2 = lora_cols_partial_floats(M, N, r);
   if (cols_f2 > cols_f) cols_f = cols_f2;
   w.total = w.cols + round_up(cols_f * 4);
+  if (gemm_dx_supported(N, K)) {
+    const size_t gemm_end = w.rows + round_up(gemm_dx_partial_floats(M, N, K) * 4);
+    if (gemm_end > w.total) w.total = gemm_end;
+  }
   return w;
 }
 
@@ -207,7 +214,7 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
   if (st) return st;
   if (act_dtype == QL_BF16)
     return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
-                           sc_lora, (uint16_t *)y, s);
+                           sc_lora, (uint16_t *)y, s, rows_partial);
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
 }
@@ -226,7 +233,7 @@ int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4
   const BlockScales sc = scales_of(W);
   if (act_dtype == QL_BF16)
     return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
-                           sc_lora, (uint16_t *)y, s);
+                           sc_lora, (uint16_t *)y, s, nullptr);
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
 }
@@ -271,7 +278,7 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   if (!dx) return QL_OK;
   if (act_dtype == QL_BF16 && gemm_dx_supported(N, K))
     return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
-                          (uint16_t *)dx, s);
+                          (uint16_t *)dx, s, rows_partial);
   return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
 }
 

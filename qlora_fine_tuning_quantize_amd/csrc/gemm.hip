@@ -150,6 +150,53 @@ __device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t
   }
 }
 
+// Store a wave's transposed accumulators as fp32 (a split-K partial tile):
+// 4 consecutive columns per 16-byte store when ld % 4 == 0 and the tile is
+// full, else element by element.
+template <int NJ>
+__device__ __forceinline__ void store_tile_f32(float *__restrict__ out, int64_t ld, int64_t rows,
+                                               int64_t cols, int64_t row_base, int64_t col_base,
+                                               const f32x16 (&acc)[4][NJ], int lane) {
+  const int lr = lane & 31, lk = lane >> 5;
+  const bool full = col_base + 32 * NJ <= cols && ld % 4 == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = row_base + 32 * i + lr;
+    if (m >= rows) continue;
+    float *p = out + m * ld + col_base + 4 * lk;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4 *>(p + 32 * j + 8 * q) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+    } else {
+      for (int j = 0; j < NJ; ++j)
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * j + 8 * (v >> 2) + (v & 3);
+          if (col_base + 4 * lk + c < cols) p[c] = acc[i][j][v];
+        }
+    }
+  }
+}
+
+// out[e] = bf16(sum_s part[s][e]), s in increasing order; 4 elements per lane
+// (count % 4 == 0).
+__global__ __launch_bounds__(256) void k_reduce_split(const float *__restrict__ part, int S,
+                                                      int64_t count, uint16_t *__restrict__ out) {
+  const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (e >= count) return;
+  f32x4 acc = *reinterpret_cast<const f32x4 *>(part + e);
+  for (int i = 1; i < S; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(part + (int64_t)i * count + e);
+    acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+  }
+  *reinterpret_cast<u32x2 *>(out + e) =
+      u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+}
+
 // Rank-r operand tiles are staged once per 16-rank chunk into LDS as bf16
 // rows of 16 values with a 48-byte stride (the 16 rows one 16-byte-per-lane
 // read pass touches then start on 16 distinct 4-bank groups).
@@ -229,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
                                                        BlockScales sc, int64_t N, int64_t K,
                                                        const float *__restrict__ u,
                                                        const LT *__restrict__ B, int32_t r,
-                                                       float s, uint16_t *__restrict__ y) {
+                                                       float s, uint16_t *__restrict__ y,
+                                                       float *__restrict__ part, int nsplit) {
   constexpr int TN = BN / 4;           // outputs per wave
   constexpr int NJ = TN / 32;          // 32-wide tiles per wave along outputs
   constexpr int WBYTES = BN * 32 / kThreads;  // packed bytes per lane per step (16 or 8)
@@ -246,7 +294,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   tile_of((M + kBM - 1) / kBM, (N + BN - 1) / BN, mt, nt);
   const int64_t m0 = mt * kBM, n0 = nt * BN;
   const int64_t KB = K >> 6;
-  const int nsteps = (int)KB;
+  // contraction slice of this workgroup (split-K: grid row blockIdx.y)
+  const int split = blockIdx.y;
+  const int ks0 = (int)(split * KB / nsplit), ks1 = (int)((split + 1) * KB / nsplit);
 
   // weight staging: lane -> (row, part) of the packed tile.  Rows past N
   // (and token rows past M below) are clamped to the last valid row instead
@@ -324,24 +374,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 
   __syncthreads();  // lut
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_x_chunk(0, i);
-  load_w(0);
+  for (int i = 0; i < 4; ++i) load_x_chunk(ks0, i);
+  load_w(ks0);
   // first 16-rank chunk of the bypass operands (s u and B), used after the
-  // main loop; staged here so that its loads overlap the first tile loads
-  stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, 0, s, t);
-  stage_lora<BN, kThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
+  // main loop by the first contraction slice; staged here so that its loads
+  // overlap the first tile loads
+  if (split == 0) {
+    stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, 0, s, t);
+    stage_lora<BN, kThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_x_chunk(nsteps > 1 ? 1 : 0, i);
-  load_w(nsteps > 1 ? 1 : 0);
+  for (int i = 0; i < 4; ++i) load_x_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
+  load_w(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
   __syncthreads();
   // The staging of step k+1 and the prefetch of step k+2 run unconditionally
   // (clamped to the last step): the extra work in the last two iterations
   // writes a buffer no one reads again and keeps the loop free of branches.
-  for (int k = 0; k < nsteps; ++k) {
-    const int cur = k & 1;
-    const int pf = k + 2 < nsteps ? k + 2 : nsteps - 1;
+  for (int k = ks0; k < ks1; ++k) {
+    const int cur = (k - ks0) & 1;
+    const int pf = k + 2 < ks1 ? k + 2 : ks1 - 1;
     const uint8_t *xb = xs[cur];
     const uint8_t *wb = ws[cur];
     u32x4 a[2][4], b[2][NJ];
@@ -375,8 +428,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   }
 
   // LoRA bypass: acc += B (s u)^T, 16 ranks per MFMA step (the main loop's
-  // last barrier orders the staged chunk 0 before these reads).
-  for (int j0 = 0; j0 < r; j0 += 16) {
+  // last barrier orders the staged chunk 0 before these reads); only the
+  // first contraction slice adds it.
+  for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
       stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, j0, s, t);
@@ -393,7 +447,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(bb[j], ua[i], acc[i][j]);
   }
-  if (n0 + BN <= N && N % 8 == 0)
+  if (nsplit > 1)
+    store_tile_f32<NJ>(part + (int64_t)split * M * N, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc,
+                       lane);
+  else if (n0 + BN <= N && N % 8 == 0)
     store_tile_lds<NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
                        &xs[0][0] + wave * 32 * (2 * TN + 16), lane);
   else
@@ -438,7 +495,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
                                                       BlockScales sc, int64_t N, int64_t K,
                                                       const float *__restrict__ g,
                                                       const LT *__restrict__ A, int32_t r,
-                                                      uint16_t *__restrict__ dx) {
+                                                      uint16_t *__restrict__ dx,
+                                                      float *__restrict__ part, int nsplit) {
   constexpr int TX = BX / 4;
   constexpr int NJ = TX / 32;
   constexpr int NU = BX / 64;  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
@@ -453,7 +511,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   int64_t mt, kt;
   tile_of((M + kBM - 1) / kBM, K / BX, mt, kt);
   const int64_t m0 = mt * kBM, k0 = kt * BX;
-  const int nsteps = (int)(N / kDxBC);
+  const int64_t NS = N / kDxBC;
+  // contraction slice of this workgroup (split-K: grid row blockIdx.y)
+  const int split = blockIdx.y;
+  const int ks0 = (int)(split * NS / nsplit), ks1 = (int)((split + 1) * NS / nsplit);
 
   // weight staging: lane -> row wrow of the step, 8 * NU codes from column wk
   const int wrow = t >> 3, wk = (t & 7) * 8 * NU;
@@ -536,22 +597,24 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
 
   __syncthreads();  // lut
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dy_chunk(0, i);
-  load_w(0);
+  for (int i = 0; i < 4; ++i) load_dy_chunk(ks0, i);
+  load_w(ks0);
   // first 16-rank chunk of the bypass operands (g, which already holds s,
-  // and A^T), used after the main loop; staged here so that its loads
-  // overlap the first tile loads
-  stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, 0, 1.0f, t);
-  stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, 0, t);
+  // and A^T), used after the main loop by the first contraction slice;
+  // staged here so that its loads overlap the first tile loads
+  if (split == 0) {
+    stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, 0, 1.0f, t);
+    stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, 0, t);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dy_chunk(nsteps > 1 ? 1 : 0, i);
-  load_w(nsteps > 1 ? 1 : 0);
+  for (int i = 0; i < 4; ++i) load_dy_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
+  load_w(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
   __syncthreads();
-  for (int k = 0; k < nsteps; ++k) {
-    const int cur = k & 1;
-    const int pf = k + 2 < nsteps ? k + 2 : nsteps - 1;
+  for (int k = ks0; k < ks1; ++k) {
+    const int cur = (k - ks0) & 1;
+    const int pf = k + 2 < ks1 ? k + 2 : ks1 - 1;
     const uint8_t *db = ds[cur];
     const uint8_t *wb = wt[cur];
     u32x4 a[2][4], b[2][NJ];
@@ -582,8 +645,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     __syncthreads();
   }
 
-  // LoRA bypass: acc += A^T g^T, 16 ranks per MFMA step.
-  for (int j0 = 0; j0 < r; j0 += 16) {
+  // LoRA bypass: acc += A^T g^T, 16 ranks per MFMA step (first slice only).
+  for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
       stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
@@ -601,8 +664,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
   }
   // K % 128 == 0 here, so every tile is full in the column direction
-  store_tile_lds<NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
-                     &ds[0][0] + wave * 32 * (2 * TX + 16), lane);
+  if (nsplit > 1)
+    store_tile_f32<NJ>(part + (int64_t)split * M * K, K, M, K, m0 + 128 * wm, k0 + TX * wn, acc,
+                       lane);
+  else
+    store_tile_lds<NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
+                       &ds[0][0] + wave * 32 * (2 * TX + 16), lane);
 }
 
 // Output tile width: 256 when that still gives at least ~1.5 workgroups per
@@ -614,15 +681,73 @@ static int pick_width(int64_t M, int64_t cols, int64_t divisor_ok) {
   return 128;
 }
 
+// Split-K: a launch with fewer tiles than compute units (a few token tiles,
+// e.g. 64 to 512 tokens) leaves units idle while each workgroup walks the
+// whole contraction.  Its contraction is then split into S slices (grid
+// rows) that write fp32 partial tiles, summed in fixed order by
+// k_reduce_split.  S minimises (waves of 256 workgroups) x (steps per slice
+// + ~4 steps of prologue and epilogue), keeps >= 8 steps per slice and the
+// partial buffer <= 64 MB, and prefers the smaller S on ties; it depends
+// only on the shape.
+static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols) {
+  if (tiles >= 256 || tiles <= 0 || cols % 4 != 0) return 1;
+  int64_t smax = steps / 8;
+  if (smax > 16) smax = 16;
+  const int64_t per = M * cols * 4;
+  const int64_t cap = (int64_t)64 << 20;
+  if (per > 0 && smax > cap / per) smax = cap / per;
+  int best = 1;
+  double best_cost = (double)steps + 4.0;  // S = 1: one wave
+  for (int64_t S = 2; S <= smax; ++S) {
+    const double waves = (double)((tiles * S + 255) / 256);
+    const double cost = waves * ((double)steps / (double)S + 4.0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = (int)S;
+    }
+  }
+  return best;
+}
+
+static int fwd_split(int64_t M, int64_t N, int64_t K) {
+  const int bn = pick_width(M, N, 1);
+  return split_count(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn), K >> 6, M, N);
+}
+
+static int dx_split(int64_t M, int64_t N, int64_t K) {
+  const int bx = pick_width(M, K, K % 256 == 0);
+  return split_count(((M + kBM - 1) / kBM) * (K / bx), N / kDxBC, M, K);
+}
+
+size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K) {
+  const int S = fwd_split(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N : 0;
+}
+
+size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K) {
+  const int S = dx_split(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)K : 0;
+}
+
+static int reduce_split(const float *part, int S, int64_t count, uint16_t *out,
+                        hipStream_t stream) {
+  const int64_t n4 = count / 4;
+  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     part, S, count, out);
+  QL_HIP_CHECK_LAUNCH();
+  return QL_OK;
+}
+
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
                     int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, hipStream_t stream) {
+                    float s, uint16_t *y, hipStream_t stream, float *part) {
   const int bn = pick_width(M, N, 1);
   const int64_t G = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
+  const int S = part ? fwd_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
-#define QL_FWD(BNV, LT, DQV)                                                                    \
-  hipLaunchKernelGGL((k_gemm_fwd<BNV, LT, DQV>), dim3((unsigned)G), dim3(kThreads), 0, stream, \
-                     x, M, packed, sc, N, K, u, (const LT *)B, r, s, y)
+#define QL_FWD(BNV, LT, DQV)                                                                     \
+  hipLaunchKernelGGL((k_gemm_fwd<BNV, LT, DQV>), dim3((unsigned)G, (unsigned)S), dim3(kThreads), \
+                     0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, y, part, S)
 #define QL_FWD_DQ(BNV, LT) \
   do { if (dq) QL_FWD(BNV, LT, true); else QL_FWD(BNV, LT, false); } while (0)
   if (bn == 256) {
@@ -635,6 +760,7 @@ int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockSc
 #undef QL_FWD_DQ
 #undef QL_FWD
   QL_HIP_CHECK_LAUNCH();
+  if (S > 1) return reduce_split(part, S, M * N, y, stream);
   return QL_OK;
 }
 
@@ -642,13 +768,14 @@ bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 
 
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream) {
+                   uint16_t *dx, hipStream_t stream, float *part) {
   const int bx = pick_width(M, K, K % 256 == 0);
   const int64_t G = ((M + kBM - 1) / kBM) * (K / bx);
+  const int S = part ? dx_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
 #define QL_DX(BXV, LT, DQV)                                                                      \
-  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV>), dim3((unsigned)G), dim3(kThreads), 0, stream,   \
-                     dy, M, packed, sc, N, K, g, (const LT *)A, r, dx)
+  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV>), dim3((unsigned)G, (unsigned)S), dim3(kThreads), \
+                     0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, r, dx, part, S)
 #define QL_DX_DQ(BXV, LT) \
   do { if (dq) QL_DX(BXV, LT, true); else QL_DX(BXV, LT, false); } while (0)
   if (bx == 256) {
@@ -661,6 +788,7 @@ int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockSc
 #undef QL_DX_DQ
 #undef QL_DX
   QL_HIP_CHECK_LAUNCH();
+  if (S > 1) return reduce_split(part, S, M * K, dx, stream);
   return QL_OK;
 }
 

@@ -47,14 +47,18 @@ int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockSc
                     int64_t N, int64_t K, const void *A, const void *B, int lora_dtype, int32_t r,
                     float s, uint16_t *y, float *u_save, hipStream_t stream);
 
-// gemm.hip: matrix-core forward and input-gradient products (bf16).
+// gemm.hip: matrix-core forward and input-gradient products (bf16).  part:
+// fp32 workspace of gemm_*_partial_floats floats for split-K launches, or
+// NULL (no split).
+size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
+size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K);
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
                     int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, hipStream_t stream);
+                    float s, uint16_t *y, hipStream_t stream, float *part);
 bool gemm_dx_supported(int64_t N, int64_t K);
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream);
+                   uint16_t *dx, hipStream_t stream, float *part);
 
 // optim.hip: one AdamW step (scalars from the fp64 hyperparameters)
 int launch_adamw(float *p, const float *g, float *m, float *v, uint16_t *p_bf16, int64_t n,

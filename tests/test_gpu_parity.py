@@ -159,6 +159,11 @@ BF16_CASES = [
     (512, 256, 640, 64, True, torch.bfloat16),  # r = 64
     (257, 128, 128, 128, True, torch.bfloat16), # r = 128
     (64, 64, 64, 5, True, torch.bfloat16),      # rank not a multiple of 8
+    # split-K (few tiles, long contraction): fp32 partial tiles + fixed-order sum
+    (300, 200, 1024, 16, False, torch.float32), # fwd 2 slices, ragged M and N
+    (77, 1024, 2048, 16, True, torch.bfloat16), # fwd 4 slices, dx 2 slices
+    (200, 512, 4096, 8, True, torch.bfloat16),  # fwd 8 slices
+    (130, 4096, 512, 16, True, torch.bfloat16), # dx 8 slices
 ]
 
 
@@ -230,6 +235,26 @@ def test_mlp8b_config_full_size_sampled(orc, proj):
     N, K = c["projs"][proj]
     M, r = c["M"], c["r"]
     rows = np.sort(np.random.default_rng(3).choice(M, 64, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    _say(f"mlp8b {proj}: M={M} N={N} K={K}")
+    got, ref = _layer_case(orc, M, N, K, r, True, torch.bfloat16, torch.bfloat16,
+                           alpha=c["alpha"], seed_cfg=c["config"], rows=rows)
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
+
+
+@pytest.mark.parametrize("M", [128, 512])
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_mlp8b_shape_few_tokens_sampled(orc, proj, M):
+    """8B-shaped MLP projection at 128 and 512 tokens (the split-K launches:
+    too few token tiles to fill the chip unsplit): y and dx on 32 sampled
+    token rows, dA and dB in full."""
+    c = si.MLP_8B
+    N, K = c["projs"][proj]
+    r = c["r"]
+    rows = np.sort(np.random.default_rng(5).choice(M, 32, replace=False))
     rows[0], rows[-1] = 0, M - 1
     _say(f"mlp8b {proj}: M={M} N={N} K={K}")
     got, ref = _layer_case(orc, M, N, K, r, True, torch.bfloat16, torch.bfloat16,
