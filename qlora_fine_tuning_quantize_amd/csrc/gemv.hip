@@ -4,10 +4,13 @@
 //   u = x A^T,   y = x W^^T + s u B^T     (26. QLoRA and 4bit Quantization, Step 3)
 //
 // Memory-bound: the packed 4-bit weight is the dominant traffic.  Each
-// workgroup owns 16 weight rows; its 8 waves split the K dimension.  A lane
-// of a wave holds 16 consecutive indices (8 bytes) of one row per NF4 block,
-// so one block of one row is read by 4 lanes as 32 contiguous bytes.  Every
-// load of a batch of 8 blocks is issued before any of them is used.
+// workgroup owns 16 consecutive weight rows, which are one contiguous span of
+// the packed array.  The contraction runs in rounds of 64 NF4 blocks (4096
+// columns): the round's slice of the 16 rows is read with 16-byte loads, each
+// wave instruction covering half a kilobyte of two rows, and staged in LDS;
+// the 8 waves then split the round's blocks and read their codes back in the
+// matrix-core operand layout.  The round's block constants (absmax, or the
+// double-quantised form q * sigma + mu) are resolved once into an LDS table.
 //
 // The 16x16x32 bf16 matrix-core op multiplies the activations by the
 // *unscaled* codebook values of one NF4 block (16 rows x 32 columns per op,
@@ -32,8 +35,20 @@ namespace qlora {
 
 constexpr int kGemvRows = 16;
 constexpr int kGemvWaves = 8;
-// NF4 blocks whose loads are in flight together: 8 for a 16-wide rank tile
-// in bf16, fewer as the per-block register footprint grows.
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvRound = 64;  // NF4 blocks per row per round
+// LDS stride of one staged row: 16 bytes of padding put the 8-byte reads of
+// 16 rows x 4 lane groups at the same column offset on distinct banks.
+constexpr int kGemvRowStride = kGemvRound * 32 + 16;
+// 16-byte weight chunks per lane per round (16 rows x 2 KB / 512 lanes)
+constexpr int kGemvChunks = kGemvRows * kGemvRound * 2 / kGemvThreads;
+// NF4 block constants per lane per round
+constexpr int kGemvScales = kGemvRows * kGemvRound / kGemvThreads;
+// LDS stride of one staged activation row (a round of bf16 values + 16 bytes)
+constexpr int kGemvXStride = kGemvRound * 128 + 16;
+
+// Blocks whose activation and A loads are in flight together: 8 for a
+// 16-wide rank tile in bf16, fewer as the per-block register footprint grows.
 template <typename LT, int JT>
 constexpr int gemv_batch() {
   constexpr int w = JT * (int)(sizeof(LT) / 2);
@@ -74,24 +89,29 @@ struct ARaw<float> {
   }
 };
 
+// Per-block register operands of one lane: 2 x 8 activations and JT x 16 A values.
 template <typename LT, int JT>
 struct GemvBlock {
-  u32x2 w;        // 16 packed indices of this lane's row
-  int q8;         // double-quantisation code (or unused)
-  float sg;       // its second-level scale, or the fp32 absmax
-  u32x4 x0, x1;   // 2 x 8 activations
-  ARaw<LT> a[JT]; // LoRA A rows 16 jt + l % 16
+  u32x4 x0, x1;
+  ARaw<LT> a[JT];
 };
 
-template <typename LT, int JT, bool DQ>
-__global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
-                                                  const uint8_t *__restrict__ packed,
-                                                  BlockScales sc, int64_t N, int64_t K,
-                                                  const LT *__restrict__ A,
-                                                  const LT *__restrict__ B, int32_t r, float s,
-                                                  uint16_t *__restrict__ y,
-                                                  float *__restrict__ u_save) {
+// XM > 0: the round's activations of all M <= XM token rows are staged in
+// LDS once per workgroup (the operand layout repeats a token row across the
+// 16 lanes of a lane group, which would otherwise be 16 / M copies of the
+// same bytes through the load path); XM = 0: read in operand layout.
+template <typename LT, int JT, bool DQ, int XM>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
+                                                           const uint8_t *__restrict__ packed,
+                                                           BlockScales sc, int64_t N, int64_t K,
+                                                           const LT *__restrict__ A,
+                                                           const LT *__restrict__ B, int32_t r,
+                                                           float s, uint16_t *__restrict__ y,
+                                                           float *__restrict__ u_save) {
   __shared__ uint32_t lut[256];
+  __shared__ __attribute__((aligned(16))) uint8_t wt[kGemvRows * kGemvRowStride];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XM > 0 ? XM * kGemvXStride : 16];
+  __shared__ float scl[kGemvRows][kGemvRound];
   __shared__ float red[kGemvWaves][16][16];
   __shared__ float ured[kGemvWaves][16][16 * JT];
   __shared__ float us[16][16 * JT];
@@ -100,15 +120,11 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t *__restrict__ x
   const int wave = t >> 6, lane = t & 63;
   const int nl = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * kGemvRows;
-  // Rows past N, token rows past M and rank rows past r are clamped to valid
-  // ones: they only produce outputs that are never stored or summed.
-  const int64_t n = n0 + nl < N ? n0 + nl : N - 1;
+  // Token rows past M and rank rows past r are clamped to valid ones: they
+  // only produce outputs that are never stored or summed.
   const int m = nl < M ? nl : M - 1;
   const int64_t KB = K >> 6;
-  const int64_t bpw = (KB + kGemvWaves - 1) / kGemvWaves;
-  const int64_t b_begin = wave * bpw < KB ? wave * bpw : KB;
-  const int64_t b_end = b_begin + bpw < KB ? b_begin + bpw : KB;
-  const uint8_t *wrow = packed + ((n * K) >> 1) + 8 * q;
+  const int64_t row_bytes = K >> 1;
   const uint16_t *xrow = x + (int64_t)m * K + 16 * q;
   const LT *arow[JT];
 #pragma unroll
@@ -116,92 +132,183 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t *__restrict__ x
     const int j = 16 * jt + nl < r ? 16 * jt + nl : r - 1;
     arow[jt] = A + (int64_t)j * K + 16 * q;
   }
-  const int64_t sbase = n * KB;
   const float mu = DQ ? sc.mu[0] : 0.0f;
 
-  constexpr int kGemvBatch = gemv_batch<LT, JT>();
-  GemvBlock<LT, JT> bl[kGemvBatch];
-  auto load_batch = [&](int64_t b0, int cnt) {
+  // Every load below is unconditional, its index clamped into the array:
+  // a load under a branch makes the compiler wait for it at the join, which
+  // would serialise the round trips this kernel overlaps.  Values loaded for
+  // clamped indices are masked where they are stored.
+  // This workgroup's rows of B: loaded first, staged in LDS with the first round.
+  constexpr int kBPer = (16 * 16 * JT + kGemvThreads - 1) / kGemvThreads;
+  float bv[kBPer];
 #pragma unroll
-    for (int i = 0; i < kGemvBatch; ++i) {
-      if (i < cnt) {
-        const int64_t b = b0 + i;
-        bl[i].w = *reinterpret_cast<const u32x2 *>(wrow + 32 * b);
-        if constexpr (DQ) {
-          bl[i].q8 = sc.q[sbase + b];
-          bl[i].sg = sc.sigma[(sbase + b) >> 8];
-        } else {
-          bl[i].q8 = 0;
-          bl[i].sg = sc.absmax[sbase + b];
-        }
-        const u32x4 *xp = reinterpret_cast<const u32x4 *>(xrow + 64 * b);
-        bl[i].x0 = xp[0];
-        bl[i].x1 = xp[1];
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) bl[i].a[jt].load(arow[jt] + 64 * b);
-      }
-    }
-  };
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 uacc[JT];
-#pragma unroll
-  for (int jt = 0; jt < JT; ++jt) uacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  int64_t b0 = b_begin;
-  int cnt = (int)(b_end - b0 < kGemvBatch ? b_end - b0 : kGemvBatch);
-  load_batch(b0, cnt);
-  // while the first loads are in flight: codebook table and this
-  // workgroup's rows of B
+  for (int i = 0; i < kBPer; ++i) {
+    const int e = t + kGemvThreads * i;
+    const int row = (e / (16 * JT)) & 15, j = e % (16 * JT);
+    const int64_t nn = n0 + row < N ? n0 + row : N - 1;
+    bv[i] = load_as_f32(B, nn * r + (j < r ? j : r - 1));
+  }
   if (t < 256) {
     const uint16_t hi = f32_to_bf16_bits(nf4_immediate(t >> 4));
     const uint16_t lo = f32_to_bf16_bits(nf4_immediate(t & 15));
     lut[t] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
-  for (int e = t; e < 16 * 16 * JT; e += 512) {
-    const int row = e / (16 * JT), j = e % (16 * JT);
-    const int64_t nn = n0 + row < N ? n0 + row : N - 1;
-    bs[row][j] = j < r ? load_as_f32(B, nn * r + j) : 0.0f;
-  }
-  __syncthreads();
 
-  while (cnt > 0) {
+  constexpr int kBatch = gemv_batch<LT, JT>();
+  constexpr int kWaveBlocks = kGemvRound / kGemvWaves;  // blocks per wave per full round
+  GemvBlock<LT, JT> bl[kBatch];
+  // loads of blocks first .. first + kBatch - 1 of the round, clamped to its last block
+  auto load_batch = [&](int64_t rb0, int first, int RB) {
 #pragma unroll
-    for (int i = 0; i < kGemvBatch; ++i) {
-      if (i < cnt) {
-        const GemvBlock<LT, JT> &g = bl[i];
-        u32x4 wb0, wb1;
-        wb0.x = lut[g.w.x & 0xFF];
-        wb0.y = lut[(g.w.x >> 8) & 0xFF];
-        wb0.z = lut[(g.w.x >> 16) & 0xFF];
-        wb0.w = lut[g.w.x >> 24];
-        wb1.x = lut[g.w.y & 0xFF];
-        wb1.y = lut[(g.w.y >> 8) & 0xFF];
-        wb1.z = lut[(g.w.y >> 16) & 0xFF];
-        wb1.w = lut[g.w.y >> 24];
-        const bf16x8 xa0 = __builtin_bit_cast(bf16x8, g.x0);
-        const bf16x8 xa1 = __builtin_bit_cast(bf16x8, g.x1);
-        f32x4 part = {0.f, 0.f, 0.f, 0.f};
-        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, __builtin_bit_cast(bf16x8, wb0), part,
-                                                       0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa1, __builtin_bit_cast(bf16x8, wb1), part,
-                                                       0, 0, 0);
-        // part[v] = sum over the block of x[4q+v][k] * cb[idx[n][k]] for column n = n0 + nl
-        const float a = DQ ? __builtin_fmaf((float)g.q8, g.sg, mu) : g.sg;
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t b = rb0 + (first + i < RB ? first + i : RB - 1);
+      if constexpr (XM == 0) {
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(xrow + 64 * b);
+        bl[i].x0 = xp[0];
+        bl[i].x1 = xp[1];
+      }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(a, part[v], acc[v]);
+      for (int jt = 0; jt < JT; ++jt) bl[i].a[jt].load(arow[jt] + 64 * b);
+    }
+  };
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 uacc[JT], uacc1[1];
+  uacc1[0] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          uacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              xa0, __builtin_bit_cast(bf16x8, g.a[jt].half(0)), uacc[jt], 0, 0, 0);
-          uacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              xa1, __builtin_bit_cast(bf16x8, g.a[jt].half(1)), uacc[jt], 0, 0, 0);
-        }
+  for (int jt = 0; jt < JT; ++jt) uacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t rb0 = 0; rb0 < KB; rb0 += kGemvRound) {
+    const int RB = KB - rb0 < kGemvRound ? (int)(KB - rb0) : kGemvRound;
+    // the round's weight slice: 16 rows x 2 RB chunks of 16 bytes; chunk c is
+    // column chunk c % 128 of row c / 128 (chunks past the slice or rows past
+    // N re-read the slice's first chunk and are not stored)
+    u32x4 wv[kGemvChunks];
+#pragma unroll
+    for (int i = 0; i < kGemvChunks; ++i) {
+      const int c = t + kGemvThreads * i;
+      const int row = c >> 7, cr = c & 127;
+      const bool ok = cr < 2 * RB && n0 + row < N;
+      wv[i] = *reinterpret_cast<const u32x4 *>(packed + (n0 + (ok ? row : 0)) * row_bytes +
+                                                32 * rb0 + 16 * (ok ? cr : 0));
+    }
+    // the round's block constants: entry e is block e % 64 of row e / 64
+    // (rows past N read the last row), loaded raw and combined only after
+    // every load of the round is out
+    int qv[kGemvScales];
+    float sv[kGemvScales];
+#pragma unroll
+    for (int i = 0; i < kGemvScales; ++i) {
+      const int e = t + kGemvThreads * i;
+      const int row = e >> 6, b = e & 63;
+      const int64_t nn = n0 + row < N ? n0 + row : N - 1;
+      const int64_t g = nn * KB + rb0 + (b < RB ? b : RB - 1);
+      qv[i] = DQ ? (int)sc.q[g] : 0;
+      sv[i] = DQ ? sc.sigma[g >> 8] : sc.absmax[g];
+    }
+    // the round's activations (XM > 0): row c >> 9, 16-byte chunk c & 511
+    u32x4 xv[XM > 0 ? XM : 1];
+#pragma unroll
+    for (int i = 0; i < XM; ++i) {
+      const int c = t + kGemvThreads * i;
+      const int row = (c >> 9) < M ? (c >> 9) : M - 1;
+      const int cc = (c & 511) < 8 * RB ? (c & 511) : 8 * RB - 1;
+      xv[i] = *reinterpret_cast<const u32x4 *>(x + (int64_t)row * K + 64 * rb0 + 8 * cc);
+    }
+    // this wave's blocks of the round: wb0 .. wb0 + cnt - 1
+    const int wb0 = wave * kWaveBlocks;
+    const int cnt = RB - wb0 < 0 ? 0 : (RB - wb0 < kWaveBlocks ? RB - wb0 : kWaveBlocks);
+    // the first batch's loads go out before the staging stores wait for the
+    // weight slice (at rank tile 8 after them: the registers are needed)
+    if constexpr (JT < 8) load_batch(rb0, wb0, RB);
+#pragma unroll
+    for (int i = 0; i < kGemvChunks; ++i) {
+      const int c = t + kGemvThreads * i;
+      if ((c & 127) < 2 * RB)
+        *reinterpret_cast<u32x4 *>(wt + (c >> 7) * kGemvRowStride + 16 * (c & 127)) = wv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kGemvScales; ++i) {
+      const int e = t + kGemvThreads * i;
+      scl[e >> 6][e & 63] = DQ ? __builtin_fmaf((float)qv[i], sv[i], mu) : sv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < XM; ++i) {
+      const int c = t + kGemvThreads * i;
+      if ((c & 511) < 8 * RB)
+        *reinterpret_cast<u32x4 *>(xs + (c >> 9) * kGemvXStride + 16 * (c & 511)) = xv[i];
+    }
+    if (rb0 == 0) {
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) {
+        const int e = t + kGemvThreads * i;
+        if (e < 16 * 16 * JT)
+          bs[e / (16 * JT)][e % (16 * JT)] = (e % (16 * JT)) < r ? bv[i] : 0.0f;
       }
     }
-    b0 += kGemvBatch;
-    cnt = (int)(b_end - b0 < kGemvBatch ? (b_end - b0 > 0 ? b_end - b0 : 0) : kGemvBatch);
-    if (cnt > 0) load_batch(b0, cnt);
+    if constexpr (JT >= 8) load_batch(rb0, wb0, RB);
+    __syncthreads();
+
+    // one block: 2 ops against the unscaled codes, then the block constant,
+    // and 2 JT ops against A (at one rank tile, two accumulator chains)
+    auto block = [&](const GemvBlock<LT, JT> &g, int bb) {
+      const u32x2 w =
+          *reinterpret_cast<const u32x2 *>(wt + nl * kGemvRowStride + 32 * bb + 8 * q);
+      u32x4 wb0v, wb1v;
+      wb0v.x = lut[w.x & 0xFF];
+      wb0v.y = lut[(w.x >> 8) & 0xFF];
+      wb0v.z = lut[(w.x >> 16) & 0xFF];
+      wb0v.w = lut[w.x >> 24];
+      wb1v.x = lut[w.y & 0xFF];
+      wb1v.y = lut[(w.y >> 8) & 0xFF];
+      wb1v.z = lut[(w.y >> 16) & 0xFF];
+      wb1v.w = lut[w.y >> 24];
+      u32x4 xr0, xr1;
+      if constexpr (XM > 0) {
+        const uint8_t *xp = xs + (m < XM ? m : XM - 1) * kGemvXStride + 128 * bb + 32 * q;
+        xr0 = *reinterpret_cast<const u32x4 *>(xp);
+        xr1 = *reinterpret_cast<const u32x4 *>(xp + 16);
+      } else {
+        xr0 = g.x0;
+        xr1 = g.x1;
+      }
+      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, xr0);
+      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, xr1);
+      f32x4 part = {0.f, 0.f, 0.f, 0.f};
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, __builtin_bit_cast(bf16x8, wb0v), part,
+                                                     0, 0, 0);
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa1, __builtin_bit_cast(bf16x8, wb1v), part,
+                                                     0, 0, 0);
+      // part[v] = sum over the block of x[4q+v][k] * cb[idx[n][k]] for column n = n0 + nl
+      const float a = scl[nl][bb];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(a, part[v], acc[v]);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        uacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            xa0, __builtin_bit_cast(bf16x8, g.a[jt].half(0)), uacc[jt], 0, 0, 0);
+        f32x4 &u1 = JT == 1 ? uacc1[jt] : uacc[jt];
+        u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            xa1, __builtin_bit_cast(bf16x8, g.a[jt].half(1)), u1, 0, 0, 0);
+      }
+    };
+    // A wave with all its blocks present (every full round of 4096 columns)
+    // runs branch-free, so that the compiler overlaps the LDS reads and the
+    // matrix ops of different blocks.
+    const bool full = JT < 8 && cnt == kWaveBlocks;  // (rank tile 8: registers are short)
+#pragma unroll
+    for (int i0 = 0; i0 < kWaveBlocks; i0 += kBatch) {
+      if (i0 > 0) load_batch(rb0, wb0 + i0, RB);
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) block(bl[i], wb0 + i0 + i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (i0 + i < cnt) block(bl[i], wb0 + i0 + i);
+      }
+    }
+    __syncthreads();  // the next round overwrites the staged slice
   }
 
   // D[4q + v][nl]: y partials per (m, n) and u partials per (m, j)
@@ -210,9 +317,9 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t *__restrict__ x
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) ured[wave][4 * q + v][16 * jt + nl] = uacc[jt][v];
+    for (int v = 0; v < 4; ++v) ured[wave][4 * q + v][16 * jt + nl] = (JT == 1 ? uacc[jt][v] + uacc1[0][v] : uacc[jt][v]);
   __syncthreads();
-  for (int e = t; e < 16 * 16 * JT; e += 512) {
+  for (int e = t; e < 16 * 16 * JT; e += kGemvThreads) {
     const int mo = e / (16 * JT), j = e % (16 * JT);
     float su = 0.0f;
 #pragma unroll
@@ -235,16 +342,25 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t *__restrict__ x
   }
 }
 
+template <typename LT, int JT, int XM>
+static void launch_xm(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
+                      const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
+                      const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
+  if (sc.absmax == nullptr)
+    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, true, XM>), grid, dim3(kGemvThreads), 0, stream, x, M,
+                       packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+  else
+    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, false, XM>), grid, dim3(kGemvThreads), 0, stream, x, M,
+                       packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+}
+
 template <typename LT, int JT>
 static void launch_jt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
-  if (sc.absmax == nullptr)
-    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, true>), grid, dim3(512), 0, stream, x, M, packed, sc, N,
-                       K, (const LT *)A, (const LT *)B, r, s, y, u_save);
-  else
-    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, false>), grid, dim3(512), 0, stream, x, M, packed, sc,
-                       N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+  if (M == 1) launch_xm<LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else if (M <= 4) launch_xm<LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else launch_xm<LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
 }
 
 template <typename LT>

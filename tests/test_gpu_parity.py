@@ -129,9 +129,16 @@ def _layer_case(orc, M, N, K, r, dq, act, lora, alpha=32.0, seed_cfg=90, dy_ones
     got = {"y": y.float().cpu().numpy()[sel], "u": u.cpu().numpy()[sel],
            "dx": dx.float().cpu().numpy()[sel], "dA": dA.cpu().numpy(), "dB": dB.cpu().numpy()}
     ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": dA_ref, "dB": dB_ref}
-    # the saved-u backward is the same computation
-    np.testing.assert_array_equal(dA2.cpu().numpy(), got["dA"])
-    np.testing.assert_array_equal(dB2.cpu().numpy(), got["dB"])
+    # the saved-u backward is the same computation.  A decode-sized bf16
+    # forward (M <= 16) computes u inside its own kernel, in another fp32
+    # summation order than the backward's recomputation: there dA and dB agree
+    # to fp32 rounding only.  dx does not depend on u.
+    if act == torch.bfloat16 and M <= 16:
+        np.testing.assert_allclose(dA2.cpu().numpy(), got["dA"], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(dB2.cpu().numpy(), got["dB"], rtol=1e-5, atol=1e-6)
+    else:
+        np.testing.assert_array_equal(dA2.cpu().numpy(), got["dA"])
+        np.testing.assert_array_equal(dB2.cpu().numpy(), got["dB"])
     np.testing.assert_array_equal(dx2.float().cpu().numpy()[sel], got["dx"])
     return got, ref
 
@@ -153,6 +160,9 @@ BF16_CASES = [
     (1, 256, 256, 8, True, torch.bfloat16),     # decode GEMV
     (3, 200, 320, 16, False, torch.float32),    # GEMV, ragged N, fp32 LoRA
     (16, 384, 1024, 16, True, torch.bfloat16),  # GEMV at M = 16
+    (1, 200, 4416, 16, True, torch.bfloat16),   # GEMV: second round of 5 blocks, ragged N
+    (16, 96, 8192, 128, False, torch.float32),  # GEMV: two full rounds, r = 128, fp32 absmax
+    (5, 64, 14336, 64, True, torch.bfloat16),   # GEMV: 3.5 rounds, r = 64
     (17, 128, 128, 16, True, torch.bfloat16),   # smallest matrix-core GEMM
     (300, 384, 384, 16, True, torch.bfloat16),  # ragged M over two token tiles
     (300, 200, 320, 8, False, torch.float32),   # ragged N: guarded fwd tile, tiled dx
