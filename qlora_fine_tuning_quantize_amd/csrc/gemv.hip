@@ -220,7 +220,13 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     const int cnt = RB - wb0 < 0 ? 0 : (RB - wb0 < kWaveBlocks ? RB - wb0 : kWaveBlocks);
     // the first batch's loads go out before the staging stores wait for the
     // weight slice (at rank tile 8 after them: the registers are needed)
-    if constexpr (JT < 8) load_batch(rb0, wb0, RB);
+    // A full round with activations in LDS and one load batch (one 16-rank
+    // tile in bf16) issues its A loads only after the staging barrier and
+    // runs all weight ops first: the staging stores then wait for the
+    // weight slice alone, and the A loads fly during the weight ops.
+    const bool late_a = XM > 0 && kBatch == kWaveBlocks && JT < 8 && cnt == kWaveBlocks;
+    if constexpr (JT < 8)
+      if (!late_a) load_batch(rb0, wb0, RB);
 #pragma unroll
     for (int i = 0; i < kGemvChunks; ++i) {
       const int c = t + kGemvThreads * i;
@@ -249,9 +255,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     if constexpr (JT >= 8) load_batch(rb0, wb0, RB);
     __syncthreads();
 
-    // one block: 2 ops against the unscaled codes, then the block constant,
-    // and 2 JT ops against A (at one rank tile, two accumulator chains)
-    auto block = [&](const GemvBlock<LT, JT> &g, int bb) {
+    // one block, weight part: 2 ops against the unscaled codes, then the
+    // block constant; returns the activation operand in xr0, xr1
+    auto wpart = [&](const GemvBlock<LT, JT> &g, int bb, u32x4 &xr0, u32x4 &xr1) {
       const u32x2 w =
           *reinterpret_cast<const u32x2 *>(wt + nl * kGemvRowStride + 32 * bb + 8 * q);
       u32x4 wb0v, wb1v;
@@ -263,7 +269,6 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
       wb1v.y = lut[(w.y >> 8) & 0xFF];
       wb1v.z = lut[(w.y >> 16) & 0xFF];
       wb1v.w = lut[w.y >> 24];
-      u32x4 xr0, xr1;
       if constexpr (XM > 0) {
         const uint8_t *xp = xs + (m < XM ? m : XM - 1) * kGemvXStride + 128 * bb + 32 * q;
         xr0 = *reinterpret_cast<const u32x4 *>(xp);
@@ -272,40 +277,60 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
         xr0 = g.x0;
         xr1 = g.x1;
       }
-      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, xr0);
-      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, xr1);
       f32x4 part = {0.f, 0.f, 0.f, 0.f};
-      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, __builtin_bit_cast(bf16x8, wb0v), part,
-                                                     0, 0, 0);
-      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa1, __builtin_bit_cast(bf16x8, wb1v), part,
-                                                     0, 0, 0);
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr0),
+                                                     __builtin_bit_cast(bf16x8, wb0v), part, 0,
+                                                     0, 0);
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr1),
+                                                     __builtin_bit_cast(bf16x8, wb1v), part, 0,
+                                                     0, 0);
       // part[v] = sum over the block of x[4q+v][k] * cb[idx[n][k]] for column n = n0 + nl
       const float a = scl[nl][bb];
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(a, part[v], acc[v]);
+    };
+    // one block, bypass part: 2 JT ops against A (at one rank tile, two
+    // accumulator chains)
+    auto upart = [&](const GemvBlock<LT, JT> &g, const u32x4 &xr0, const u32x4 &xr1) {
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         uacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            xa0, __builtin_bit_cast(bf16x8, g.a[jt].half(0)), uacc[jt], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, xr0), __builtin_bit_cast(bf16x8, g.a[jt].half(0)),
+            uacc[jt], 0, 0, 0);
         f32x4 &u1 = JT == 1 ? uacc1[jt] : uacc[jt];
         u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            xa1, __builtin_bit_cast(bf16x8, g.a[jt].half(1)), u1, 0, 0, 0);
+            __builtin_bit_cast(bf16x8, xr1), __builtin_bit_cast(bf16x8, g.a[jt].half(1)), u1, 0,
+            0, 0);
       }
+    };
+    auto block = [&](const GemvBlock<LT, JT> &g, int bb) {
+      u32x4 xr0, xr1;
+      wpart(g, bb, xr0, xr1);
+      upart(g, xr0, xr1);
     };
     // A wave with all its blocks present (every full round of 4096 columns)
     // runs branch-free, so that the compiler overlaps the LDS reads and the
     // matrix ops of different blocks.
     const bool full = JT < 8 && cnt == kWaveBlocks;  // (rank tile 8: registers are short)
+    if (late_a) {
+      load_batch(rb0, wb0, RB);
+      u32x4 xk0[kWaveBlocks], xk1[kWaveBlocks];
 #pragma unroll
-    for (int i0 = 0; i0 < kWaveBlocks; i0 += kBatch) {
-      if (i0 > 0) load_batch(rb0, wb0 + i0, RB);
-      if (full) {
+      for (int i = 0; i < kWaveBlocks; ++i) wpart(bl[i], wb0 + i, xk0[i], xk1[i]);
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) block(bl[i], wb0 + i0 + i);
-      } else {
+      for (int i = 0; i < kWaveBlocks; ++i) upart(bl[i], xk0[i], xk1[i]);
+    } else {
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          if (i0 + i < cnt) block(bl[i], wb0 + i0 + i);
+      for (int i0 = 0; i0 < kWaveBlocks; i0 += kBatch) {
+        if (i0 > 0) load_batch(rb0, wb0 + i0, RB);
+        if (full) {
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) block(bl[i], wb0 + i0 + i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i)
+            if (i0 + i < cnt) block(bl[i], wb0 + i0 + i);
+        }
       }
     }
     __syncthreads();  // the next round overwrites the staged slice
