@@ -172,21 +172,68 @@ void orc_round_bf16(const float *in, int64_t n, uint16_t *out) {
   }
 }
 
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11), written from
+ * its definition there: a 4-word counter and a 2-word key; one round maps
+ * (c0, c1, c2, c3) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+ * lo(M0 c0)) with the multipliers M0 = 0xD2511F53, M1 = 0xCD9E8D57; between
+ * rounds the key is bumped by the Weyl constants (0x9E3779B9, 0xBB67AE85);
+ * 10 rounds.  The pages name LoRA dropout without saying how its mask is
+ * drawn; this generator is the reading taken (see the dropout mask below). */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* LoRA dropout mask over the activations x [M, K] (the pages' LoraConfig
+ * lora_dropout: dropout on the bypass input, inverted scaling 1/(1-p)).
+ * Element e = m K + k takes word e % 4 of Philox4x32-10 at counter
+ * (e / 4 low, e / 4 high, 0, 0) with key (seed low, seed high), and is kept
+ * when that word >= threshold (threshold = floor(p 2^32)). */
+void orc_dropout_keep(int64_t M, int64_t K, uint32_t threshold, uint64_t seed, uint8_t *keep) {
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  const int64_t n = M * K;
+#pragma omp parallel for schedule(static)
+  for (int64_t grp = 0; grp < (n + 3) / 4; ++grp) {
+    const uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)((uint64_t)grp >> 32), 0u, 0u};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i < n) keep[4 * grp + i] = w[i] >= threshold ? 1 : 0;
+  }
+}
+
 /* Forward of the layer ([ch26] Step 3 / Step 4 answer):
- *   u = x A^T                 [M, r]
+ *   u = (d .* x) A^T          [M, r]
  *   y = x W^T + s * u B^T     [M, N],  s = alpha / r
- * x [M,K], w [N,K] (the dequantised weight), A [r,K], B [N,r]; all products
- * accumulate in fp64 in index order.  u may be NULL. */
+ * x [M,K], w [N,K] (the dequantised weight), A [r,K], B [N,r]; d [M,K] the
+ * dropout multipliers of the bypass input (0 or 1/(1-p)), or NULL for none.
+ * All products accumulate in fp64 in index order.  u may be NULL. */
 void orc_linear_fwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
                     const double *x, const float *w, const double *A,
-                    const double *B, double *y, double *u_out) {
+                    const double *B, const double *d, double *y, double *u_out) {
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; ++m) {
     const double *xm = x + m * K;
+    const double *dm = d ? d + m * K : NULL;
     double u[512];
     for (int32_t j = 0; j < r; ++j) {
       double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k) acc += xm[k] * A[j * K + k];
+      for (int64_t k = 0; k < K; ++k) acc += (dm ? dm[k] * xm[k] : xm[k]) * A[j * K + k];
       u[j] = acc;
       if (u_out) u_out[m * r + j] = acc;
     }
@@ -202,11 +249,12 @@ void orc_linear_fwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
 }
 
 /* Backward of the layer ([ch22] Step 1 item 4 and [ch26] Step 4 tests: the
- * gradient reaches x, A and B; the frozen base gets none).  With
- * u = x A^T and g = s * dy B:
- *   dB = s * dy^T u      [N, r]
- *   dA = g^T x           [r, K]
- *   dx = dy W + g A      [M, K]
+ * gradient reaches x, A and B; the frozen base gets none).  With the
+ * dropped input xd = d .* x (xd = x when d is NULL), u = xd A^T and
+ * g = s * dy B:
+ *   dB = s * dy^T u          [N, r]
+ *   dA = g^T xd              [r, K]
+ *   dx = dy W + d .* (g A)   [M, K]
  * dx is produced only for the rows listed in rows[0..n_rows) (all rows when
  * rows == NULL), into dx[i*K ...] for the i-th listed row; dx may be NULL.
  * Work buffers u_buf and g_buf hold M*r doubles each.  Every sum runs over
@@ -215,14 +263,15 @@ void orc_linear_fwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
 #define ORC_CHUNK 64
 void orc_linear_bwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
                     const double *x, const float *w, const double *A,
-                    const double *B, const double *dy, const int64_t *rows,
+                    const double *B, const double *d, const double *dy, const int64_t *rows,
                     int64_t n_rows, double *dx, double *dA, double *dB,
                     double *u_buf, double *g_buf) {
+#define ORC_XD(m, k) (d ? d[(m) * K + (k)] * x[(m) * K + (k)] : x[(m) * K + (k)])
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; ++m) {
     for (int32_t j = 0; j < r; ++j) {
       double au = 0.0;
-      for (int64_t k = 0; k < K; ++k) au += x[m * K + k] * A[j * K + k];
+      for (int64_t k = 0; k < K; ++k) au += ORC_XD(m, k) * A[j * K + k];
       u_buf[m * r + j] = au;
       double ag = 0.0;
       for (int64_t nn = 0; nn < N; ++nn) ag += dy[m * N + nn] * B[nn * r + j];
@@ -254,7 +303,7 @@ void orc_linear_bwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
     for (int64_t m = 0; m < M; ++m)
       for (int32_t j = 0; j < r; ++j) {
         double gv = g_buf[m * r + j];
-        for (int64_t k = k0; k < k1; ++k) dA[j * K + k] += gv * x[m * K + k];
+        for (int64_t k = k0; k < k1; ++k) dA[j * K + k] += gv * ORC_XD(m, k);
       }
   }
   if (!dx) return;
@@ -274,9 +323,10 @@ void orc_linear_bwd(int64_t M, int64_t N, int64_t K, int32_t r, double s,
     for (int64_t k = 0; k < K; ++k) {
       double lora = 0.0;
       for (int32_t j = 0; j < r; ++j) lora += g_buf[m * r + j] * A[j * K + k];
-      dxi[k] = dxi[k] + lora;
+      dxi[k] = dxi[k] + (d ? d[m * K + k] * lora : lora);
     }
   }
+#undef ORC_XD
 }
 
 #ifdef _OPENMP

@@ -55,9 +55,11 @@ def _load():
     lib.orc_dq_codes.argtypes = [_p, _i64, _f32, _i32, _p, _p]
     lib.orc_nf4_dequantize.argtypes = [_p, _i64, _i32, _p, _p, _p, _f32, _i32, _p]
     lib.orc_round_bf16.argtypes = [_p, _i64, _p]
-    lib.orc_linear_fwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p]
-    lib.orc_linear_bwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p,
+    lib.orc_linear_fwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p, _p]
+    lib.orc_linear_bwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p,
                                    _p, _i64, _p, _p, _p, _p, _p]
+    lib.orc_philox4x32_10.argtypes = [_p, _p, _p]
+    lib.orc_dropout_keep.argtypes = [_i64, _i64, ctypes.c_uint32, ctypes.c_uint64, _p]
     lib.orc_adamw_step.argtypes = [_p, _p, _p, _p, _p, _i64, _f32, _f32, _f32, _f32, _f32, _f32,
                                    _f32, _f32]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -208,11 +210,46 @@ def _as_f64(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(as_f32(a), dtype=np.float64)
 
 
-def linear_fwd(x, w_hat: np.ndarray, A, B, alpha: float, r: int):
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 (Salmon et al., SC'11) of one 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(4)
+    k = np.ascontiguousarray(key, dtype=np.uint32).reshape(2)
+    out = np.empty(4, dtype=np.uint32)
+    _load().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def dropout_params(p: float):
+    """LoRA dropout (the pages' LoraConfig lora_dropout) as the layer applies
+    it: keep threshold floor(p 2^32) on a 32-bit draw, and the inverted
+    scale fp32(1 / (1 - p)) of the kept inputs."""
+    assert 0.0 <= p < 1.0
+    return int(math.floor(p * 4294967296.0)), np.float32(1.0 / (1.0 - p))
+
+
+def dropout_keep(M: int, K: int, p: float, seed: int) -> np.ndarray:
+    """keep [M, K] (uint8 0/1) of the bypass input: element m K + k is kept
+    when word (m K + k) % 4 of Philox4x32-10 at counter ((m K + k) / 4, 0, 0)
+    with key = the 64-bit seed is >= floor(p 2^32)."""
+    thr, _ = dropout_params(p)
+    keep = np.empty((M, K), dtype=np.uint8)
+    _load().orc_dropout_keep(M, K, thr, seed, _ptr(keep))
+    return keep
+
+
+def dropout_mult(M: int, K: int, p: float, seed: int) -> np.ndarray:
+    """The dropout multipliers d [M, K] (fp64): 0 or fp32(1/(1-p))."""
+    _, scale = dropout_params(p)
+    return dropout_keep(M, K, p, seed).astype(np.float64) * float(scale)
+
+
+def linear_fwd(x, w_hat: np.ndarray, A, B, alpha: float, r: int, drop=None):
     """[ch26] Step 3: y = x W^T + (alpha/r) (x A^T) B^T, fp64 accumulation.
 
     x [M,K], w_hat [N,K] fp32 (dequantised), A [r,K], B [N,r]; x/A/B may be
-    fp32 or bf16 bit patterns.  Returns (y [M,N], u [M,r]) in fp64."""
+    fp32 or bf16 bit patterns.  drop: optional dropout multipliers d [M,K]
+    of the bypass input (u = (d .* x) A^T).  Returns (y [M,N], u [M,r]) in
+    fp64."""
     assert r <= 512
     xd = _as_f64(x)
     M, K = xd.shape
@@ -223,13 +260,17 @@ def linear_fwd(x, w_hat: np.ndarray, A, B, alpha: float, r: int):
     s = float(np.float32(alpha) / np.float32(r))
     y = np.empty((M, N), dtype=np.float64)
     u = np.empty((M, r), dtype=np.float64)
-    _load().orc_linear_fwd(M, N, K, r, s, _ptr(xd), _ptr(wf), _ptr(Ad), _ptr(Bd), _ptr(y), _ptr(u))
+    dd = None if drop is None else np.ascontiguousarray(drop, dtype=np.float64).reshape(M, K)
+    _load().orc_linear_fwd(M, N, K, r, s, _ptr(xd), _ptr(wf), _ptr(Ad), _ptr(Bd), _ptr(dd),
+                           _ptr(y), _ptr(u))
     return y, u
 
 
-def linear_bwd(x, w_hat: np.ndarray, A, B, dy, alpha: float, r: int, rows=None, want_dx=True):
+def linear_bwd(x, w_hat: np.ndarray, A, B, dy, alpha: float, r: int, rows=None, want_dx=True,
+               drop=None):
     """[ch22] Step 1 (gradients reach x, A, B; none for the frozen base):
-    dB = s dy^T u, dA = g^T x, dx = dy W + g A, with u = x A^T, g = s dy B.
+    dB = s dy^T u, dA = g^T xd, dx = dy W + d .* (g A), with xd = d .* x the
+    bypass input after dropout (xd = x without it), u = xd A^T, g = s dy B.
 
     rows: optional token-row indices for which dx is produced (dA and dB
     always use every row).  Returns (dx [len(rows) or M, K] | None, dA, dB)."""
@@ -248,7 +289,8 @@ def linear_bwd(x, w_hat: np.ndarray, A, B, dy, alpha: float, r: int, rows=None, 
     dB = np.empty((N, r), dtype=np.float64)
     ub = np.empty((M, r), dtype=np.float64)
     gb = np.empty((M, r), dtype=np.float64)
-    _load().orc_linear_bwd(M, N, K, r, s, _ptr(xd), _ptr(wf), _ptr(Ad), _ptr(Bd), _ptr(dyd),
+    dd = None if drop is None else np.ascontiguousarray(drop, dtype=np.float64).reshape(M, K)
+    _load().orc_linear_bwd(M, N, K, r, s, _ptr(xd), _ptr(wf), _ptr(Ad), _ptr(Bd), _ptr(dd), _ptr(dyd),
                            _ptr(rows_arr), nr, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ub), _ptr(gb))
     return dx, dA, dB
 

@@ -542,3 +542,76 @@ def test_adamw_special_cases(orc):
     assert np.array_equal(pb, orc.round_bf16(p3))
     with pytest.raises(ValueError):
         orc.adamw_step(p, g, m, v, 2e-4, step=0)
+
+
+# ---------------------------------------------------------------------------
+# LoRA dropout: counter-based mask (Philox4x32-10) and the layer with it
+# ---------------------------------------------------------------------------
+def test_philox_known_answer_vectors(orc):
+    """The oracle's Philox4x32-10 reproduces the generator's published
+    known-answer vectors (tests/golden/philox4x32_10_kat.json)."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        out = orc.philox4x32_10([int(h, 16) for h in v["ctr"]], [int(h, 16) for h in v["key"]])
+        assert [f"{w:08x}" for w in out] == v["out"]
+
+
+def test_dropout_mask_layout_and_threshold(orc):
+    """keep[m, k] is word (mK + k) % 4 of Philox at counter (mK + k) / 4 with
+    the seed as key, compared with floor(p 2^32)."""
+    M, K, p, seed = 3, 40, 0.3, 0x0123456789ABCDEF
+    keep = orc.dropout_keep(M, K, p, seed)
+    thr, scale = orc.dropout_params(p)
+    assert thr == math.floor(0.3 * 2 ** 32) and scale == np.float32(1 / 0.7)
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for e in (0, 1, 5, 39, 40, 77, M * K - 1):
+        w = orc.philox4x32_10([e // 4, 0, 0, 0], key)[e % 4]
+        assert keep.reshape(-1)[e] == (1 if w >= thr else 0)
+    assert orc.dropout_keep(M, K, 0.0, seed).all()  # p = 0 keeps everything
+
+
+@pytest.mark.parametrize("p", [0.05, 0.5])
+def test_dropout_mask_statistics(orc, p):
+    """Keep fraction within 6 sigma of 1 - p; neighbouring elements (same and
+    different Philox words) uncorrelated; another seed gives another mask."""
+    M, K = 256, 4096
+    keep = orc.dropout_keep(M, K, p, 7).astype(np.float64)
+    n = keep.size
+    assert abs(keep.mean() - (1 - p)) <= 6 * math.sqrt(p * (1 - p) / n)
+    flat = keep.reshape(-1) - keep.mean()
+    for lag in (1, 4, K):
+        corr = (flat[:-lag] * flat[lag:]).mean() / flat.var()
+        assert abs(corr) < 6 / math.sqrt(n)
+    other = orc.dropout_keep(M, K, p, 8)
+    assert (other != keep).mean() > 0.5 * 2 * p * (1 - p)
+
+
+def test_dropout_layer_matches_autograd(orc):
+    """With dropout multipliers d on the bypass input, the oracle's forward
+    equals y = x W^T + s ((d .* x) A^T) B^T and its backward equals torch
+    autograd (fp64, CPU) of sum(y * dy): a missing mask in dA or dx, or a
+    mask on the base path, fails here."""
+    M, N, K, r, alpha = 5, 7, 12, 3, 6.0
+    x, w, A, B, dy = _rand_layer(3, M, N, K, r)
+    d = orc.dropout_mult(M, K, 0.4, 99)
+    assert 0 < (d == 0).sum() < d.size
+    y, u = orc.linear_fwd(x, w, A, B, alpha, r, drop=d)
+    dx, dA, dB = orc.linear_bwd(x, w, A, B, dy, alpha, r, drop=d)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    At = torch.tensor(A, dtype=torch.float64, requires_grad=True)
+    Bt = torch.tensor(B, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64)
+    dt = torch.tensor(d)
+    ut = (dt * xt) @ At.T
+    yt = xt @ wt.T + (alpha / r) * ut @ Bt.T
+    np.testing.assert_allclose(u, ut.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (yt * torch.tensor(dy, dtype=torch.float64)).sum().backward()
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dA, At.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dB, Bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # all-ones multipliers are the layer without dropout, bit for bit
+    ones = np.ones((M, K))
+    np.testing.assert_array_equal(orc.linear_fwd(x, w, A, B, alpha, r, drop=ones)[0],
+                                  orc.linear_fwd(x, w, A, B, alpha, r)[0])
