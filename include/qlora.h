@@ -207,6 +207,62 @@ int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64
                          float *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * LoRA dropout (the pages' training configs set LoraConfig's lora_dropout
+ * to 0.05: 26. ..., Step 5.1 and 5.2; 65. QLoRA Selection Project, Step 5.3;
+ * Gemma lesson 9, sec. 9.6).  The pages do not say how the mask is drawn.
+ * Here it applies to the input of the bypass only (the base product sees x
+ * unchanged), with inverted scaling, from a counter-based generator so that
+ * the backward regenerates the forward's mask instead of storing it:
+ *     xd = d .* x,   d[m][k] = keep[m][k] / (1 - p)   (fp32 of 1 / (1 - p))
+ *     keep[m][k] = 1 iff word e % 4 of Philox4x32-10 (Salmon et al., SC'11)
+ *                  at counter (e / 4 low 32 bits, e / 4 high 32 bits, 0, 0)
+ *                  with key (seed low 32 bits, seed high 32 bits) is
+ *                  >= floor(p 2^32) (computed in double),  e = m K + k.
+ *   dropout_p  in [0, 1); 0 gives exactly the entry point without dropout.
+ *   seed       any 64-bit value; one seed per training step and layer.
+ */
+
+/*
+ * Forward with LoRA dropout:  u = xd A^T,  y = x W^^T + s u B^T.
+ * Arguments as for qlora_linear_fwd (same workspace size).  u_save receives
+ * the u of the dropped input, which is what qlora_linear_bwd_dropout's
+ * u_saved expects.  dropout_p > 0 requires bf16 activations (QL_EUNSUPPORTED
+ * otherwise) and always takes the matrix-core GEMM, also for M <= 16.
+ * Errors: as qlora_linear_fwd; QL_EINVAL for dropout_p outside [0, 1).
+ */
+int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                             const void *A, const void *B, int32_t lora_dtype, int32_t r,
+                             float alpha, double dropout_p, uint64_t seed, void *y,
+                             float *u_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward with LoRA dropout (same p and seed as the forward):
+ *     u = xd A^T (or u_saved),  g = s dy B,  dB = s dy^T u,
+ *     dA = g^T xd,  dx = dy W^ + d .* (g A).
+ * accumulate 0 overwrites dA and dB, 1 adds into them (as
+ * qlora_linear_bwd_acc).  Workspace as qlora_linear_bwd.  dropout_p > 0
+ * requires bf16 activations and, when dx is wanted, N % 64 == 0 and
+ * K % 128 == 0 (QL_EUNSUPPORTED otherwise).
+ * Errors: as qlora_linear_bwd; QL_EINVAL for dropout_p outside [0, 1) or
+ * accumulate not 0/1.
+ */
+int qlora_linear_bwd_dropout(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                             const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                             int32_t r, float alpha, double dropout_p, uint64_t seed,
+                             const float *u_saved, void *dx, float *dA, float *dB,
+                             int32_t accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The keep mask of the LoRA dropout above as bytes: keep [M, K] uint8 (device,
+ * 16-byte aligned) receives 1 for a kept and 0 for a dropped element.  The
+ * layer never reads it; it is for callers that want to see the mask.
+ * Errors: QL_EINVAL (M or K <= 0, keep NULL, dropout_p outside [0, 1)),
+ * QL_EALIGN, QL_EHIP.
+ */
+int ql_dropout_mask(int64_t M, int64_t K, double dropout_p, uint64_t seed, uint8_t *keep,
+                    void *stream);
+
+/*
  * One AdamW step over n fp32 parameters, in place (gufacode fine-tuning
  * chapter 4, "显存计算实战" and "分页优化器": the LoRA factors train with
  * AdamW holding fp32 moments, 8 bytes per parameter; Gemma lesson 9, sec.

@@ -24,6 +24,7 @@ NF4_BLOCK, DQ_BLOCK = 64, 256
 # every extern "C" symbol declared in include/qlora.h
 EXPORTED = ("ql_nf4_sizes", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
             "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "qlora_linear_bwd_acc",
+            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "ql_dropout_mask",
             "ql_adamw_step", "ql_strerror", "ql_abi_version")
 
 
@@ -66,7 +67,15 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.qlora_linear_bwd_acc.argtypes = L.qlora_linear_bwd.argtypes
     L.qlora_linear_bwd_acc.restype = ctypes.c_int
-    f64 = ctypes.c_double
+    f64, u64 = ctypes.c_double, ctypes.c_uint64
+    L.qlora_linear_fwd_dropout.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, f64, u64, p, p, p,
+                                           sz, p]
+    L.qlora_linear_fwd_dropout.restype = ctypes.c_int
+    L.qlora_linear_bwd_dropout.argtypes = [p, p, i32, i64, sp, p, p, i32, i32, f32, f64, u64, p, p,
+                                           p, p, i32, p, sz, p]
+    L.qlora_linear_bwd_dropout.restype = ctypes.c_int
+    L.ql_dropout_mask.argtypes = [i64, i64, f64, u64, p, p]
+    L.ql_dropout_mask.restype = ctypes.c_int
     L.ql_adamw_step.argtypes = [p, p, p, p, p, i64, f64, f64, f64, f64, f64, i64, p]
     L.ql_adamw_step.restype = ctypes.c_int
     L.ql_strerror.argtypes = [ctypes.c_int]
@@ -211,6 +220,38 @@ def qlora_linear_fwd(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Te
     return y
 
 
+def qlora_linear_fwd_dropout(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Tensor,
+                             alpha: float, dropout_p: float, seed: int,
+                             y: torch.Tensor | None = None, u_save: torch.Tensor | None = None,
+                             ws: torch.Tensor | None = None) -> torch.Tensor:
+    """The forward with LoRA dropout on the bypass input: u = (d .* x) A^T,
+    y = x W^T + (alpha/r) u B^T, the mask drawn from (dropout_p, seed)."""
+    assert x.dim() == 2 and x.is_contiguous() and A.is_contiguous() and B.is_contiguous()
+    M, K = x.shape
+    r = A.shape[0]
+    assert K == W.cols and A.shape == (r, K) and B.shape == (W.rows, r) and A.dtype == B.dtype
+    if y is None:
+        y = torch.empty((M, W.rows), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = workspace(QL_OP_FWD, M, W.rows, K, r, x.device)
+    st = W.struct()
+    _check(lib().qlora_linear_fwd_dropout(_ptr(x), _dtype_code(x.dtype), M, ctypes.byref(st),
+                                          _ptr(A), _ptr(B), _dtype_code(A.dtype), r, float(alpha),
+                                          float(dropout_p), int(seed) & (2**64 - 1), _ptr(y),
+                                          _ptr(u_save), _ptr(ws), ws.numel(), _stream(x.device)),
+           "qlora_linear_fwd_dropout")
+    return y
+
+
+def dropout_mask(M: int, K: int, dropout_p: float, seed: int, device) -> torch.Tensor:
+    """The LoRA dropout keep mask [M, K] (uint8 0/1) the layer draws for
+    (dropout_p, seed)."""
+    keep = torch.empty((M, K), dtype=torch.uint8, device=device)
+    _check(lib().ql_dropout_mask(M, K, float(dropout_p), int(seed) & (2**64 - 1), _ptr(keep),
+                                 _stream(keep.device)), "ql_dropout_mask")
+    return keep
+
+
 def qlora_linear_fwd_u(x: torch.Tensor, W: NF4Weight, u: torch.Tensor, B: torch.Tensor,
                        alpha: float, y: torch.Tensor | None = None) -> torch.Tensor:
     """y = x W^T + (alpha/r) u B^T with u = x A^T given (fp32 [M, r])."""
@@ -257,6 +298,40 @@ def qlora_linear_bwd(dy: torch.Tensor, x: torch.Tensor, W: NF4Weight, A: torch.T
               _dtype_code(A.dtype), r, float(alpha), _ptr(u_saved), _ptr(dx), _ptr(dA), _ptr(dB),
               _ptr(ws), ws.numel(), _stream(dev)),
            "qlora_linear_bwd_acc" if accumulate else "qlora_linear_bwd")
+    return dx, dA, dB
+
+
+def qlora_linear_bwd_dropout(dy: torch.Tensor, x: torch.Tensor, W: NF4Weight, A: torch.Tensor,
+                             B: torch.Tensor, alpha: float, dropout_p: float, seed: int,
+                             u_saved: torch.Tensor | None = None, need_dx: bool = True,
+                             dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                             dB: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                             accumulate: bool = False):
+    """The backward with LoRA dropout (the forward's dropout_p and seed):
+    returns (dx | None, dA, dB).  u_saved, if given, is the dropout forward's
+    u_save."""
+    M, K = x.shape
+    r = A.shape[0]
+    N = W.rows
+    assert dy.shape == (M, N) and dy.dtype == x.dtype and dy.is_contiguous() and x.is_contiguous()
+    dev = x.device
+    if need_dx and dx is None:
+        dx = torch.empty((M, K), dtype=x.dtype, device=dev)
+    if not need_dx:
+        dx = None
+    if accumulate and (dA is None or dB is None):
+        raise ValueError("accumulate needs the dA and dB to add into")
+    dA = dA if dA is not None else torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = dB if dB is not None else torch.empty((N, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(QL_OP_BWD, M, N, K, r, dev)
+    st = W.struct()
+    _check(lib().qlora_linear_bwd_dropout(_ptr(dy), _ptr(x), _dtype_code(x.dtype), M,
+                                          ctypes.byref(st), _ptr(A), _ptr(B), _dtype_code(A.dtype),
+                                          r, float(alpha), float(dropout_p),
+                                          int(seed) & (2**64 - 1), _ptr(u_saved), _ptr(dx),
+                                          _ptr(dA), _ptr(dB), int(accumulate), _ptr(ws), ws.numel(),
+                                          _stream(dev)), "qlora_linear_bwd_dropout")
     return dx, dA, dB
 
 

@@ -1,6 +1,7 @@
 // api.hip -- the C ABI declared in include/qlora.h: argument checks on the
 // host, workspace carve-up, and the choice of kernels.  No allocation, no
 // synchronisation, no state.
+#include <math.h>
 #include <string.h>
 
 #include "kernels.h"
@@ -111,11 +112,23 @@ int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const voi
   return QL_OK;
 }
 
+// LoRA dropout parameters of a call: keep threshold floor(p 2^32) on the
+// 32-bit draw (computed in double), inverted scale fp32(1 / (1 - p)), key =
+// the 64-bit seed.  p must lie in [0, 1).
+int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
+  if (!(p >= 0.0 && p < 1.0)) return QL_EINVAL;
+  d.k0 = (uint32_t)seed;
+  d.k1 = (uint32_t)(seed >> 32);
+  d.thr = (uint32_t)floor(p * 4294967296.0);
+  scale = (float)(1.0 / (1.0 - p));
+  return QL_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int ql_abi_version(void) { return 102; }
+int ql_abi_version(void) { return 103; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -190,11 +203,15 @@ int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) 
                                (hipStream_t)stream);
 }
 
-int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
-                     const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
-                     void *y, float *u_save, void *ws, size_t ws_bytes, void *stream) {
+// drop: LoRA dropout of the bypass input (bf16 activations only), with
+// dscale = 1 / (1 - p); NULL for none.
+static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                      const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
+                      const Dropout *drop, float dscale, void *y, float *u_save, void *ws,
+                      size_t ws_bytes, void *stream) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
+  if (drop && act_dtype != QL_BF16) return QL_EUNSUPPORTED;
   if (!x || !y) return QL_EINVAL;
   if (!aligned16(x) || !aligned16(y) || (u_save && !aligned16(u_save))) return QL_EALIGN;
   const int64_t N = W->rows, K = W->cols;
@@ -207,16 +224,36 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype == QL_BF16 && M <= 16)  // decode: one launch computes u and y
+  if (act_dtype == QL_BF16 && M <= 16 && !drop)  // decode: one launch computes u and y
     return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, A, B, lora_dtype, r,
                            sc_lora, (uint16_t *)y, u_save, s);
-  st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
+  st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
+                           rows_partial, s, nullptr, drop);
   if (st) return st;
   if (act_dtype == QL_BF16)
     return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
                            sc_lora, (uint16_t *)y, s, rows_partial);
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
+}
+
+int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                     const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
+                     void *y, float *u_save, void *ws, size_t ws_bytes, void *stream) {
+  return linear_fwd(x, act_dtype, M, W, A, B, lora_dtype, r, alpha, nullptr, 1.0f, y, u_save, ws,
+                    ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                             const void *A, const void *B, int32_t lora_dtype, int32_t r,
+                             float alpha, double dropout_p, uint64_t seed, void *y,
+                             float *u_save, void *ws, size_t ws_bytes, void *stream) {
+  Dropout d;
+  float dscale;
+  const int st = dropout_of(dropout_p, seed, d, dscale);
+  if (st) return st;
+  return linear_fwd(x, act_dtype, M, W, A, B, lora_dtype, r, alpha, dropout_p > 0.0 ? &d : nullptr,
+                    dscale, y, u_save, ws, ws_bytes, stream);
 }
 
 int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
@@ -241,9 +278,12 @@ int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4
 static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,
                       const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
                       int32_t r, float alpha, const float *u_saved, void *dx, float *dA,
-                      float *dB, void *ws, size_t ws_bytes, void *stream, bool accumulate) {
+                      float *dB, void *ws, size_t ws_bytes, void *stream, bool accumulate,
+                      const Dropout *drop = nullptr, float dscale = 1.0f) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
+  if (drop && (act_dtype != QL_BF16 || (dx && !gemm_dx_supported(W->rows, W->cols))))
+    return QL_EUNSUPPORTED;
   if (!dy || !x || !dA || !dB) return QL_EINVAL;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(dA) || !aligned16(dB) ||
       (dx && !aligned16(dx)) || (u_saved && !aligned16(u_saved)))
@@ -263,7 +303,8 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   if (u_saved) {
     u = const_cast<float *>(u_saved);
   } else {
-    st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, 1.0f, u, rows_partial, s);
+    st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
+                             rows_partial, s, nullptr, drop);
     if (st) return st;
   }
   // g = s dy B: Q(j, c) = B[c][j]
@@ -272,13 +313,14 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   // dB[n][j] = s sum_m dy[m][n] u[m][j]
   st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s, accumulate);
   if (st) return st;
-  // dA[j][k] = sum_m g[m][j] x[m][k]
-  st = launch_lora_cols(g, M, r, x, act_dtype, K, 1.0f, false, dA, cols_partial, s, accumulate);
+  // dA[j][k] = sum_m g[m][j] x[m][k] (x after dropout: keep / (1 - p) times x)
+  st = launch_lora_cols(g, M, r, x, act_dtype, K, drop ? dscale : 1.0f, false, dA, cols_partial, s,
+                        accumulate, drop);
   if (st) return st;
   if (!dx) return QL_OK;
   if (act_dtype == QL_BF16 && gemm_dx_supported(N, K))
     return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
-                          (uint16_t *)dx, s, rows_partial);
+                          (uint16_t *)dx, s, rows_partial, drop, dscale);
   return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
 }
 
@@ -296,6 +338,31 @@ int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64
                          float *dB, void *ws, size_t ws_bytes, void *stream) {
   return linear_bwd(dy, x, act_dtype, M, W, A, B, lora_dtype, r, alpha, u_saved, dx, dA, dB, ws,
                     ws_bytes, stream, true);
+}
+
+int qlora_linear_bwd_dropout(const void *dy, const void *x, int32_t act_dtype, int64_t M,
+                             const ql_nf4 *W, const void *A, const void *B, int32_t lora_dtype,
+                             int32_t r, float alpha, double dropout_p, uint64_t seed,
+                             const float *u_saved, void *dx, float *dA, float *dB,
+                             int32_t accumulate, void *ws, size_t ws_bytes, void *stream) {
+  Dropout d;
+  float dscale;
+  const int st = dropout_of(dropout_p, seed, d, dscale);
+  if (st) return st;
+  if (accumulate != 0 && accumulate != 1) return QL_EINVAL;
+  return linear_bwd(dy, x, act_dtype, M, W, A, B, lora_dtype, r, alpha, u_saved, dx, dA, dB, ws,
+                    ws_bytes, stream, accumulate == 1, dropout_p > 0.0 ? &d : nullptr, dscale);
+}
+
+int ql_dropout_mask(int64_t M, int64_t K, double dropout_p, uint64_t seed, uint8_t *keep,
+                    void *stream) {
+  Dropout d;
+  float dscale;
+  const int st = dropout_of(dropout_p, seed, d, dscale);
+  if (st) return st;
+  if (M <= 0 || K <= 0 || !keep) return QL_EINVAL;
+  if (!aligned16(keep)) return QL_EALIGN;
+  return launch_dropout_mask(M, K, d, keep, (hipStream_t)stream);
 }
 
 int ql_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq,

@@ -95,6 +95,58 @@ struct BlockScales {
   }
 };
 
+// LoRA dropout of the bypass input (the pages' LoraConfig lora_dropout):
+// element e = m K + k of the activations [M, K] is kept when word e % 4 of
+// Philox4x32-10 at counter (e / 4, 0, 0) under the 64-bit seed (k0 low
+// word, k1 high) is >= thr = floor(p 2^32); kept inputs are scaled by
+// 1/(1-p), which the kernels apply to the finished sums.
+struct Dropout {
+  uint32_t k0, k1, thr;
+};
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11) of counter (c0, c1, 0, 0) and key (k0, k1): ten
+// rounds of two 32x32 -> 64-bit multiplies (0xD2511F53, 0xCD9E8D57) mixing
+// the counter words with the key, the key advancing by the Weyl constants
+// (0x9E3779B9, 0xBB67AE85) between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0,
+                                               uint32_t k1) {
+  uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// keep bits of the 4 elements e .. e + 3 (e % 4 == 0): bit i for e + i
+__device__ __forceinline__ uint32_t dropout_keep4(const Dropout &d, uint64_t e) {
+  const uint64_t g = e >> 2;
+  const u32x4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), d.k0, d.k1);
+  return (uint32_t)(w[0] >= d.thr) | ((uint32_t)(w[1] >= d.thr) << 1) |
+         ((uint32_t)(w[2] >= d.thr) << 2) | ((uint32_t)(w[3] >= d.thr) << 3);
+}
+
+// 8 bf16 values (elements e .. e + 7 in order, e % 4 == 0) with the dropped
+// ones set to zero
+__device__ __forceinline__ u32x4 dropout_mask8(const Dropout &d, uint64_t e, u32x4 v) {
+  const uint32_t bits = dropout_keep4(d, e) | (dropout_keep4(d, e + 4) << 4);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (bits >> (2 * w)) & 1u ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (bits >> (2 * w + 1)) & 1u ? 0xFFFF0000u : 0u;
+    v[w] &= lo | hi;
+  }
+  return v;
+}
+
 }  // namespace qlora
 
 #define QL_HIP_CHECK_LAUNCH()                               \

@@ -489,14 +489,18 @@ __device__ __forceinline__ int wswz(int n, int c) {
   return n * (2 * BX) + (p << 4);
 }
 
-template <int BX, typename LT, bool DQ>
+// DROP: LoRA dropout on the bypass input; the bypass term of output (m, k)
+// is multiplied by keep(m, k) / (1 - p) (dscale) before the base product is
+// added to it.
+template <int BX, typename LT, bool DQ, bool DROP>
 __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
                                                       const uint8_t *__restrict__ packed,
                                                       BlockScales sc, int64_t N, int64_t K,
                                                       const float *__restrict__ g,
                                                       const LT *__restrict__ A, int32_t r,
                                                       uint16_t *__restrict__ dx,
-                                                      float *__restrict__ part, int nsplit) {
+                                                      float *__restrict__ part, int nsplit,
+                                                      Dropout drop, float dscale) {
   constexpr int TX = BX / 4;
   constexpr int NJ = TX / 32;
   constexpr int NU = BX / 64;  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
@@ -612,6 +616,47 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   for (int i = 0; i < 4; ++i) load_dy_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
   load_w(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
   __syncthreads();
+  if constexpr (DROP) {
+    // LoRA bypass under dropout, first slice only, before the main loop so
+    // that it needs no registers beyond the accumulator: acc = A^T g^T over
+    // all ranks, then each output (m, k) is kept times 1/(1-p) or zeroed.
+    // acc[i][j][v] is output row m0 + 128 wm + 32 i + lr, column
+    // k0 + TX wn + 32 j + 4 lk + 8 (v / 4) + v % 4; columns k .. k + 3
+    // (k % 4 == 0, and K % 4 == 0) share one Philox draw.
+    if (split == 0) {
+      for (int j0 = 0; j0 < r; j0 += 16) {
+        if (j0 > 0) {
+          __syncthreads();
+          stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
+          stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, j0, t);
+          __syncthreads();
+        }
+        u32x4 ga[4], ab[NJ];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ga[i] = lora_frag(ls_g, 128 * wm + 32 * i + lr, lk);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) ab[j] = lora_frag(ls_a, TX * wn + 32 * j + lr, lk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t m = (uint64_t)(m0 + 128 * wm + 32 * i + lr);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int64_t k = k0 + TX * wn + 32 * j + 8 * qq + 4 * lk;
+            const uint32_t bits = dropout_keep4(drop, m * (uint64_t)K + (uint64_t)k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][4 * qq + e] = (bits >> e) & 1u ? dscale * acc[i][j][4 * qq + e] : 0.0f;
+          }
+      }
+    }
+  }
   for (int k = ks0; k < ks1; ++k) {
     const int cur = (k - ks0) & 1;
     const int pf = k + 2 < ks1 ? k + 2 : ks1 - 1;
@@ -645,8 +690,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     __syncthreads();
   }
 
-  // LoRA bypass: acc += A^T g^T, 16 ranks per MFMA step (first slice only).
-  for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
+  // LoRA bypass: acc += A^T g^T, 16 ranks per MFMA step (first slice only;
+  // with dropout it ran before the main loop)
+  for (int j0 = 0; j0 < (split == 0 && !DROP ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
       stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
@@ -768,16 +814,21 @@ bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 
 
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream, float *part) {
+                   uint16_t *dx, hipStream_t stream, float *part, const Dropout *drop,
+                   float drop_scale) {
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const int bx = pick_width(M, K, K % 256 == 0);
   const int64_t G = ((M + kBM - 1) / kBM) * (K / bx);
   const int S = part ? dx_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
-#define QL_DX(BXV, LT, DQV)                                                                      \
-  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV>), dim3((unsigned)G, (unsigned)S), dim3(kThreads), \
-                     0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, r, dx, part, S)
+#define QL_DX(BXV, LT, DQV, DRV)                                                                 \
+  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),            \
+                     dim3(kThreads), 0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, r, dx, \
+                     part, S, dr, drop_scale)
+#define QL_DX_DR(BXV, LT, DQV) \
+  do { if (drop) QL_DX(BXV, LT, DQV, true); else QL_DX(BXV, LT, DQV, false); } while (0)
 #define QL_DX_DQ(BXV, LT) \
-  do { if (dq) QL_DX(BXV, LT, true); else QL_DX(BXV, LT, false); } while (0)
+  do { if (dq) QL_DX_DR(BXV, LT, true); else QL_DX_DR(BXV, LT, false); } while (0)
   if (bx == 256) {
     if (lora_dtype == QL_BF16) QL_DX_DQ(256, uint16_t);
     else QL_DX_DQ(256, float);
@@ -786,6 +837,7 @@ int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockSc
     else QL_DX_DQ(128, float);
   }
 #undef QL_DX_DQ
+#undef QL_DX_DR
 #undef QL_DX
   QL_HIP_CHECK_LAUNCH();
   if (S > 1) return reduce_split(part, S, M * K, dx, stream);

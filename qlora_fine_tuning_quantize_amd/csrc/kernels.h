@@ -26,12 +26,14 @@ size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r);
 // slices is returned through *slices (the caller reduces them).
 int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const void *Q,
                         int q_dtype, int64_t ldq_j, int64_t ldq_c, int32_t r, float scale,
-                        float *out, float *partial, hipStream_t stream, int *slices = nullptr);
+                        float *out, float *partial, hipStream_t stream, int *slices = nullptr,
+                        const Dropout *drop = nullptr);
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r);
 // accumulate: out += result instead of out = result
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
-                     hipStream_t stream, bool accumulate = false);
+                     hipStream_t stream, bool accumulate = false,
+                     const Dropout *drop = nullptr);
 
 // simple.hip: fp32-accumulating tiled kernels for any activation dtype.
 int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
@@ -58,7 +60,11 @@ int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockSc
 bool gemm_dx_supported(int64_t N, int64_t K);
 int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
                    int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream, float *part);
+                   uint16_t *dx, hipStream_t stream, float *part, const Dropout *drop = nullptr,
+                   float drop_scale = 1.0f);
+// dropout.hip: the keep mask of the LoRA dropout as bytes (0/1), [M, K]
+int launch_dropout_mask(int64_t M, int64_t K, const Dropout &d, uint8_t *keep,
+                        hipStream_t stream);
 
 // optim.hip: one AdamW step (scalars from the fp64 hyperparameters)
 int launch_adamw(float *p, const float *g, float *m, float *v, uint16_t *p_bf16, int64_t n,

@@ -132,11 +132,13 @@ struct Vec8<float> {
   }
 };
 
-template <int CS, int JT, typename QT, int QMODE>
+// DROP: P is the activation x of the LoRA dropout; its dropped elements
+// are zeroed as loaded (the 1/(1-p) scale is applied by the reduction).
+template <int CS, int JT, typename QT, int QMODE, bool DROP>
 __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ P, int64_t M,
                                                    int64_t C, const QT *__restrict__ Q,
                                                    int64_t ldq_j, int64_t ldq_c, int32_t r,
-                                                   float *__restrict__ partial) {
+                                                   float *__restrict__ partial, Dropout dr) {
   constexpr int QST = 2 * CS + 16;   // bytes per staged rank row
   constexpr int JW = JT * 16;
   __shared__ __attribute__((aligned(16))) uint8_t qs[JW * QST];
@@ -186,6 +188,13 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
     const int64_t c = c0 + 32 * i + 8 * q;
     a[i] = *reinterpret_cast<const u32x4 *>(prow + (c + 8 <= C ? c : C - 8));
     if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
+#pragma unroll
+    for (int i = 0; i < CS / 32; ++i) {
+      const int64_t c = c0 + 32 * i + 8 * q;
+      if (c + 8 <= C) a[i] = dropout_mask8(dr, (uint64_t)mrow * C + c, a[i]);
+    }
   }
 
   // ---- factor slice to LDS, bf16 [j][c] ----
@@ -293,9 +302,13 @@ size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r) {
 
 int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const void *Q,
                         int q_dtype, int64_t ldq_j, int64_t ldq_c, int32_t r, float scale,
-                        float *out, float *partial, hipStream_t stream, int *slices) {
+                        float *out, float *partial, hipStream_t stream, int *slices,
+                        const Dropout *drop) {
   if (M <= 0) return QL_OK;
   int S;
+  if (drop && (!rows_use_mfma(p_dtype, C) || ldq_c != 1 || ldq_j % 8 != 0 || C < 8))
+    return QL_EUNSUPPORTED;
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (rows_use_mfma(p_dtype, C)) {
     S = mrows_slices(C, r, q_dtype);
     const dim3 grid((unsigned)((M + kMRowsTile - 1) / kMRowsTile), (unsigned)S);
@@ -305,14 +318,16 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     int mode = kQElem;
     if (ldq_c == 1 && C % 8 == 0 && ldq_j % 8 == 0 && C >= 8) mode = kQRowJ;
     else if (ldq_j == 1 && r % 8 == 0 && ldq_c % 8 == 0) mode = kQRowC;
-#define QL_ROWS_M(JTV, QT, MODEV)                                                                \
-  hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, QT, MODEV>), grid, dim3(256), 0,     \
-                     stream, (const uint16_t *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r, partial)
+#define QL_ROWS_M(JTV, QT, MODEV, DRV)                                                           \
+  hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, QT, MODEV, DRV>), grid, dim3(256),   \
+                     0, stream, (const uint16_t *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r, partial, \
+                     dr)
 #define QL_ROWS_Q(JTV, QT)                                                                       \
   do {                                                                                           \
-    if (mode == kQRowJ) QL_ROWS_M(JTV, QT, kQRowJ);                                              \
-    else if (mode == kQRowC) QL_ROWS_M(JTV, QT, kQRowC);                                         \
-    else QL_ROWS_M(JTV, QT, kQElem);                                                             \
+    if (drop) QL_ROWS_M(JTV, QT, kQRowJ, true);                                                  \
+    else if (mode == kQRowJ) QL_ROWS_M(JTV, QT, kQRowJ, false);                                  \
+    else if (mode == kQRowC) QL_ROWS_M(JTV, QT, kQRowC, false);                                  \
+    else QL_ROWS_M(JTV, QT, kQElem, false);                                                      \
   } while (0)
 #define QL_ROWS_JT(JTV) \
   do { if (q_dtype == QL_BF16) QL_ROWS_Q(JTV, uint16_t); else QL_ROWS_Q(JTV, float); } while (0)
@@ -428,10 +443,13 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int TM, int JT, bool RVEC>
+// DROP: P is the activation x of the LoRA dropout; its dropped elements
+// are zeroed as loaded (the 1/(1-p) scale is applied by the reduction).
+template <int TM, int JT, bool RVEC, bool DROP>
 __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
                                                    int32_t r, const uint16_t *__restrict__ P,
-                                                   int64_t C, float *__restrict__ partial) {
+                                                   int64_t C, float *__restrict__ partial,
+                                                   Dropout dr) {
   constexpr int JW = JT * 16;
   constexpr int RST = 2 * TM + 16;  // bytes per staged rank row
   __shared__ __attribute__((aligned(16))) uint8_t ps[TM * 128];
@@ -470,6 +488,13 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
     const int64_t m = m0 + prow + 32 * i;
     pv[i] = *reinterpret_cast<const u32x4 *>(P + (m < M ? m : M - 1) * C + (cok ? pc : C - 8));
     if (m >= M || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i) {
+      const int64_t m = m0 + prow + 32 * i;
+      if (m < M && cok) pv[i] = dropout_mask8(dr, (uint64_t)m * C + pc, pv[i]);
+    }
   }
   // ---- to LDS ----
   if constexpr (RVEC) {
@@ -536,6 +561,8 @@ __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ p
                                                      int32_t r, int64_t C, float scale,
                                                      int c_major, int accumulate,
                                                      float *__restrict__ out) {
+  // accumulation is the product scale * s, rounded, then one addition
+#pragma clang fp contract(off)
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t count = (int64_t)r * C;
   if (e >= count) return;
@@ -575,17 +602,23 @@ size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
 
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
-                     hipStream_t stream, bool accumulate) {
+                     hipStream_t stream, bool accumulate, const Dropout *drop) {
   if (C <= 0) return QL_OK;
   int S;
+  if (drop && !cols_use_mfma(p_dtype, C)) return QL_EUNSUPPORTED;
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (cols_use_mfma(p_dtype, C)) {
     S = mcols_slices(M);
     const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
     const bool rvec = r % 4 == 0;
-#define QL_COLS_M(JTV, RV)                                                                       \
-  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, RV>), grid, dim3(256), 0, stream, R, M, r,     \
-                     (const uint16_t *)P, C, partial)
-#define QL_COLS_JT(JTV) do { if (rvec) QL_COLS_M(JTV, true); else QL_COLS_M(JTV, false); } while (0)
+#define QL_COLS_M(JTV, RV, DRV)                                                                  \
+  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, RV, DRV>), grid, dim3(256), 0, stream, R, M, r, \
+                     (const uint16_t *)P, C, partial, dr)
+#define QL_COLS_JT(JTV)                                                                          \
+  do {                                                                                           \
+    if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \
+    else { if (drop) QL_COLS_M(JTV, false, true); else QL_COLS_M(JTV, false, false); }           \
+  } while (0)
     const int jt = rows_jt(r);
     if (jt == 1) QL_COLS_JT(1);
     else if (jt == 2) QL_COLS_JT(2);

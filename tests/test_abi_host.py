@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 102
+    assert L.ql_abi_version() == 103
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -202,3 +202,39 @@ def test_strerror_and_python_errors():
         b._check(b.QL_ESHAPE, "x")
     with pytest.raises(b.QLoRAError):
         b._check(b.QL_EHIP, "x")
+
+
+@no_gpu
+def test_dropout_entry_points_reject_bad_arguments():
+    L = q.lib()
+    d = _desc(rows=128, cols=256)
+
+    def fwd(p=0.05, act=b.QL_BF16, M=32, ws_bytes=1 << 30):
+        return L.qlora_linear_fwd_dropout(ctypes.c_void_p(FAKE), act, M, ctypes.byref(d),
+                                          ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), b.QL_BF16,
+                                          8, 16.0, p, 7, ctypes.c_void_p(FAKE), None,
+                                          ctypes.c_void_p(FAKE), ws_bytes, None)
+
+    def bwd(p=0.05, act=b.QL_BF16, acc=0, desc=d, dx=FAKE, ws_bytes=1 << 30):
+        return L.qlora_linear_bwd_dropout(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), act, 32,
+                                          ctypes.byref(desc), ctypes.c_void_p(FAKE),
+                                          ctypes.c_void_p(FAKE), b.QL_BF16, 8, 16.0, p, 7, None,
+                                          ctypes.c_void_p(dx) if dx else None,
+                                          ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), acc,
+                                          ctypes.c_void_p(FAKE), ws_bytes, None)
+    for p in (1.0, -0.1, float("nan"), 2.0):
+        assert fwd(p=p) == b.QL_EINVAL
+        assert bwd(p=p) == b.QL_EINVAL
+        assert L.ql_dropout_mask(4, 4, p, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
+    assert fwd(act=b.QL_F32) == b.QL_EUNSUPPORTED   # dropout runs on the bf16 path only
+    assert fwd(M=0) == b.QL_EINVAL
+    assert fwd(ws_bytes=255) == b.QL_EWORKSPACE
+    assert bwd(act=b.QL_F32) == b.QL_EUNSUPPORTED
+    assert bwd(acc=2) == b.QL_EINVAL
+    assert bwd(ws_bytes=1024) == b.QL_EWORKSPACE
+    # dx with dropout needs the matrix-core dx GEMM's shapes (N % 64, K % 128)
+    assert bwd(desc=_desc(rows=100, cols=256)) == b.QL_EUNSUPPORTED
+    assert L.ql_dropout_mask(0, 4, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
+    assert L.ql_dropout_mask(4, -1, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
+    assert L.ql_dropout_mask(4, 4, 0.1, 7, None, None) == b.QL_EINVAL
+    assert L.ql_dropout_mask(4, 4, 0.1, 7, ctypes.c_void_p(FAKE + 1), None) == b.QL_EALIGN

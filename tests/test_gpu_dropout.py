@@ -1,0 +1,137 @@
+"""GPU parity of the LoRA dropout (through the C ABI) against the CPU oracle.
+
+The mask is integer work and is compared bit for bit; the layer with
+dropout is compared with the oracle's layer given the oracle's own mask as
+multipliers, within the bf16 tolerance (max |d| / max(max|ref|, rms ref) <=
+2e-2 against fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import qlora_fine_tuning_quantize_amd as q
+import synth_inputs as si
+from tests.helpers import BF16_TOL, host, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (1, 3), (3, 5), (1, 17), (7, 129), (64, 4096),
+                                 (2048, 4096)])
+@pytest.mark.parametrize("p,seed", [(0.05, 0), (0.5, 12345), (0.999, 2**63 + 5), (0.0, 77)])
+def test_dropout_mask_bit_exact(orc, M, K, p, seed):
+    _say(f"dropout mask M={M} K={K} p={p} seed={seed}")
+    keep = q.dropout_mask(M, K, p, seed, DEV)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(keep.cpu().numpy(), orc.dropout_keep(M, K, p, seed))
+
+
+def _drop_case(orc, M, N, K, r, dq, lora, p, seed, alpha=32.0, rows=None, cfg=95):
+    t = si.linear_inputs(cfg, M, N, K, r, lora_dtype=lora, sub=M + N + K + r)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=dq)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y = q.qlora_linear_fwd_dropout(d["x"], W, d["A"], d["B"], alpha, p, seed, u_save=u)
+    dx, dA, dB = q.qlora_linear_bwd_dropout(d["dy"], d["x"], W, d["A"], d["B"], alpha, p, seed)
+    dx2, dA2, dB2 = q.qlora_linear_bwd_dropout(d["dy"], d["x"], W, d["A"], d["B"], alpha, p, seed,
+                                               u_saved=u)
+    torch.cuda.synchronize()
+    # the saved-u backward runs the same kernels on the same u
+    np.testing.assert_array_equal(dA2.cpu().numpy(), dA.cpu().numpy())
+    np.testing.assert_array_equal(dB2.cpu().numpy(), dB.cpu().numpy())
+    np.testing.assert_array_equal(dx2.float().cpu().numpy(), dx.float().cpu().numpy())
+    st = orc.quantize_nf4(host(t["W"]), double_quant=dq)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    mult = orc.dropout_mult(M, K, p, seed)
+    sel = slice(None) if rows is None else rows
+    xs = host(t["x"])[sel]
+    y_ref, u_ref = orc.linear_fwd(xs, w_hat, host(t["A"]), host(t["B"]), alpha, r,
+                                  drop=mult[sel])
+    dx_ref, dA_ref, dB_ref = orc.linear_bwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]),
+                                            host(t["dy"]), alpha, r, rows=rows, drop=mult)
+    got = {"y": y.float().cpu().numpy()[sel], "u": u.cpu().numpy()[sel],
+           "dx": dx.float().cpu().numpy()[sel], "dA": dA.cpu().numpy(), "dB": dB.cpu().numpy()}
+    ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": dA_ref, "dB": dB_ref}
+    errs = {k: rel_err(got[k], ref[k]) for k in got}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
+    # the mask matters: without it u would be far outside the tolerance
+    _, u_nod = orc.linear_fwd(xs, w_hat, host(t["A"]), host(t["B"]), alpha, r)
+    assert rel_err(u_nod, u_ref) > 10 * max(errs["u"], 1e-4)
+
+
+DROP_CASES = [
+    # M, N, K, r, dq, lora dtype, p      (path exercised)
+    (3, 256, 256, 8, True, torch.bfloat16, 0.05),     # few tokens: GEMM, not the decode kernel
+    (17, 128, 128, 16, True, torch.bfloat16, 0.1),    # smallest matrix-core GEMM
+    (300, 384, 384, 16, True, torch.bfloat16, 0.05),  # ragged M over two token tiles
+    (257, 128, 128, 128, True, torch.bfloat16, 0.3),  # r = 128 (8 rank chunks in dx)
+    (64, 64, 128, 5, False, torch.bfloat16, 0.5),     # rank not a multiple of 8
+    (512, 256, 640, 64, True, torch.float32, 0.05),   # r = 64, fp32 LoRA factors
+    (77, 1024, 2048, 16, True, torch.bfloat16, 0.05), # split-K: fwd 4 slices, dx 2
+    (130, 4096, 512, 16, True, torch.bfloat16, 0.2),  # split-K: dx 8 slices
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,dq,lora,p", DROP_CASES)
+def test_layer_dropout_parity(orc, M, N, K, r, dq, lora, p):
+    _say(f"dropout layer M={M} N={N} K={K} r={r} dq={dq} lora={lora} p={p}")
+    _drop_case(orc, M, N, K, r, dq, lora, p, seed=1000 + M)
+
+
+def test_layer_dropout_mlp8b_gate_sampled(orc):
+    """8B-shaped gate projection (14336 x 4096, 2048 tokens, r 16, alpha 32,
+    NF4 + double quant) with the pages' lora_dropout 0.05: y and dx on 64
+    sampled token rows, u, dA and dB in full."""
+    c = si.MLP_8B
+    N, K = c["projs"]["gate"]
+    M, r = c["M"], c["r"]
+    rows = np.sort(np.random.default_rng(6).choice(M, 64, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    _say(f"dropout mlp8b gate: M={M} N={N} K={K}")
+    _drop_case(orc, M, N, K, r, True, torch.bfloat16, 0.05, seed=2**40 + 3, alpha=c["alpha"],
+               rows=rows, cfg=c["config"])
+
+
+@pytest.mark.parametrize("M", [5, 300])
+def test_dropout_p0_is_the_plain_layer(M):
+    """dropout_p = 0 runs exactly the entry points without dropout."""
+    N, K, r = 256, 512, 16
+    t = si.linear_inputs(96, M, N, K, r, sub=M)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=True)
+    y0 = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], 32.0)
+    y1 = q.qlora_linear_fwd_dropout(d["x"], W, d["A"], d["B"], 32.0, 0.0, 99)
+    g0 = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], 32.0)
+    g1 = q.qlora_linear_bwd_dropout(d["dy"], d["x"], W, d["A"], d["B"], 32.0, 0.0, 99)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
+def test_dropout_accumulate_adds_once():
+    """accumulate = 1 adds this micro-batch's dA and dB into the buffers with
+    one fp32 addition per element; dx is overwritten as usual."""
+    M, N, K, r, p = 300, 256, 512, 16, 0.05
+    t1 = si.linear_inputs(97, M, N, K, r, sub=1)
+    t2 = si.linear_inputs(97, M, N, K, r, sub=2)
+    d1 = {k: v.to(DEV) for k, v in t1.items()}
+    d2 = {k: v.to(DEV) for k, v in t2.items()}
+    W = q.nf4_quantize(d1["W"], double_quant=True)
+    A, B = d1["A"], d1["B"]
+    _, dA1, dB1 = q.qlora_linear_bwd_dropout(d1["dy"], d1["x"], W, A, B, 32.0, p, 5)
+    dx2, dA2, dB2 = q.qlora_linear_bwd_dropout(d2["dy"], d2["x"], W, A, B, 32.0, p, 6)
+    accA, accB = dA1.clone(), dB1.clone()
+    dxa, _, _ = q.qlora_linear_bwd_dropout(d2["dy"], d2["x"], W, A, B, 32.0, p, 6, dA=accA,
+                                           dB=accB, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(accA, dA1 + dA2)
+    assert torch.equal(accB, dB1 + dB2)
+    assert torch.equal(dxa, dx2)
