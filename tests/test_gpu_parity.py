@@ -71,6 +71,34 @@ def test_quant_subnormal_and_signed_zero_blocks(orc):
         _check_quant(orc, w.to(torch.bfloat16).view(4, 64), dq)
 
 
+def test_quant_block_maxima_at_the_reciprocal_limits(orc):
+    """fp32 blocks whose maximum lies at or beyond 2^-125 / 2^125 (the
+    quantiser then divides instead of multiplying by a reciprocal), at the
+    normal minimum, near the fp32 maximum, and blocks with elements planted
+    exactly on the codepoint midpoints times the block maximum."""
+    rng = np.random.default_rng(11)
+    maxima = [2.0 ** -126, 2.0 ** -125, 2.0 ** -124, 1.5 * 2.0 ** -125, 2.0 ** 124, 2.0 ** 125,
+              1.5 * 2.0 ** 125, 2.0 ** 126, 3.0e38, 1.0, 0.02, 7.0]
+    blocks = []
+    for a in maxima:
+        b = (rng.uniform(-1, 1, 64) * a).astype(np.float32)
+        b[rng.integers(64)] = np.float32(a) * (1 if rng.integers(2) else -1)
+        blocks.append(b)
+    cb = np.array(orc.codebook(), dtype=np.float64)
+    mids = (cb[:-1] + cb[1:]) / 2
+    for a in (0.02, 1.0, 3.0, 2.0 ** -100):
+        b = np.zeros(64, np.float32)
+        b[0] = a
+        b[1:16] = (mids * a).astype(np.float32)
+        b[16:31] = np.nextafter(b[1:16], np.float32(np.inf))
+        b[31:46] = np.nextafter(b[1:16], np.float32(-np.inf))
+        blocks.append(b)
+    w = torch.from_numpy(np.concatenate(blocks).reshape(len(blocks), 64))
+    # single-level constants only: a mean over maxima 2^250 apart is not
+    # what the double-quantisation pins are about
+    _check_quant(orc, w, False)
+
+
 def _bf16_sweep_weights(a_scale_exp: int) -> torch.Tensor:
     """Blocks of 64 bf16 values: element 0 is the block maximum a (128 bf16
     mantissas times 2**a_scale_exp), the other 63 run through every finite
