@@ -121,14 +121,14 @@ __device__ __forceinline__ void zero_acc(f32x16 *acc, int n) {
 // l % 32, col = col_base + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4.  Full
 // tiles use 8-byte stores; a tile crossing the last column stores element
 // by element.
-template <int NJ>
+template <int MI, int NJ>
 __device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t ld, int64_t rows,
                                              int64_t cols, int64_t row_base, int64_t col_base,
-                                             const f32x16 (&acc)[4][NJ], int lane) {
+                                             const f32x16 (&acc)[MI][NJ], int lane) {
   const int lr = lane & 31, lk = lane >> 5;
   const bool full = col_base + 32 * NJ <= cols && ld % 4 == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
     const int64_t m = row_base + 32 * i + lr;
     if (m >= rows) continue;
     uint16_t *p = out + m * ld + col_base + 4 * lk;
@@ -153,14 +153,14 @@ __device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t
 // Store a wave's transposed accumulators as fp32 (a split-K partial tile):
 // 4 consecutive columns per 16-byte store when ld % 4 == 0 and the tile is
 // full, else element by element.
-template <int NJ>
+template <int MI, int NJ>
 __device__ __forceinline__ void store_tile_f32(float *__restrict__ out, int64_t ld, int64_t rows,
                                                int64_t cols, int64_t row_base, int64_t col_base,
-                                               const f32x16 (&acc)[4][NJ], int lane) {
+                                               const f32x16 (&acc)[MI][NJ], int lane) {
   const int lr = lane & 31, lk = lane >> 5;
   const bool full = col_base + 32 * NJ <= cols && ld % 4 == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
     const int64_t m = row_base + 32 * i + lr;
     if (m >= rows) continue;
     float *p = out + m * ld + col_base + 4 * lk;
@@ -238,10 +238,10 @@ __device__ __forceinline__ u32x4 lora_frag(const uint8_t *src, int row, int lk) 
 // wave-private LDS slice of 32 rows, so every global store instruction
 // writes whole 16-byte pieces of 64 / (TN / 8) consecutive rows.  Needs a
 // full tile in the column direction and ld % 8 == 0.
-template <int NJ>
+template <int MI, int NJ>
 __device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64_t ld,
                                                int64_t rows, int64_t row_base, int64_t col_base,
-                                               const f32x16 (&acc)[4][NJ], uint8_t *slice,
+                                               const f32x16 (&acc)[MI][NJ], uint8_t *slice,
                                                int lane) {
   constexpr int TN = 32 * NJ;
   constexpr int OS = 2 * TN + 16;   // bytes per staged row
@@ -249,7 +249,7 @@ __device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64
   constexpr int RPI = 64 / CPR;     // rows per store instruction
   const int lr = lane & 31, lk = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -448,13 +448,179 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(bb[j], ua[i], acc[i][j]);
   }
   if (nsplit > 1)
-    store_tile_f32<NJ>(part + (int64_t)split * M * N, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc,
+    store_tile_f32<4, NJ>(part + (int64_t)split * M * N, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc,
                        lane);
   else if (n0 + BN <= N && N % 8 == 0)
-    store_tile_lds<NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
+    store_tile_lds<4, NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
                        &xs[0][0] + wave * 32 * (2 * TN + 16), lane);
   else
-    store_tile_t<NJ>(y, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc, lane);
+    store_tile_t<4, NJ>(y, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc, lane);
+}
+
+// ===========================================================================
+// Forward for few tokens (up to a few hundred): 64 tokens x 128 outputs per
+// workgroup, 4 waves, wave w owning outputs 32 w .. 32 w + 31 for all 64
+// tokens.  A 256-token tile would run the matrix cores mostly on padding
+// rows, and with one wave per output row the weight tile needs no
+// dequantised copy in LDS: it is staged as packed codes (4 KB per step)
+// plus one block constant per row, and every wave dequantises its own rows
+// in registers right before its matrix ops.
+//
+// The contraction order inside a step is permuted so that a lane's 16
+// packed bytes (32 consecutive codes of one row) feed all four 16-deep
+// matrix ops of the step: for op kk, lane half h = l / 32 covers
+// k = 32 h + 8 kk + 0..7 in both operands (the weight from registers, the
+// activations from LDS chunk 4 h + kk of the token row).
+// ===========================================================================
+constexpr int kSmBM = 64;
+constexpr int kSmBN = 128;
+constexpr int kSmThreads = 256;
+
+template <typename LT, bool DQ>
+__global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
+    const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
+    int64_t N, int64_t K, const float *__restrict__ u, const LT *__restrict__ B, int32_t r,
+    float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kSmBM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wp[2][kSmBN * 32];
+  __shared__ float wsc[2][kSmBN];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_u[kSmBM * kLoraStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_b[kSmBN * kLoraStride];
+  __shared__ float2 lut[256];
+  const int t = threadIdx.x;
+  lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
+
+  int64_t mt, nt;
+  tile_of((M + kSmBM - 1) / kSmBM, (N + kSmBN - 1) / kSmBN, mt, nt);
+  const int64_t m0 = mt * kSmBM, n0 = nt * kSmBN;
+  const int64_t KB = K >> 6;
+  const int split = blockIdx.y;
+  const int ks0 = (int)(split * KB / nsplit), ks1 = (int)((split + 1) * KB / nsplit);
+
+  // staging: lane t stages half t & 1 (16 bytes) of weight row t >> 1 and
+  // activation chunks t and t + 256 (token row (t >> 3) and 32 + (t >> 3));
+  // rows past N or M are clamped to the last valid row (their outputs are
+  // never stored)
+  const int w_row = t >> 1, w_half = t & 1;
+  const int64_t w_n = n0 + w_row < N ? n0 + w_row : N - 1;
+  const uint8_t *w_src = packed + ((w_n * K) >> 1) + 16 * w_half;
+  const int64_t w_sc = w_n * KB;
+  const float mu = DQ ? sc.mu[0] : 0.0f;
+  const uint16_t *x_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = t + kSmThreads * i;
+    const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
+    x_src[i] = x + rr * K + 8 * (id & 7);
+  }
+  u32x4 xr[2], wr;
+  int wq = 0;
+  float wsig = 0.0f;
+  auto load_x = [&](int step, int i) {
+    xr[i] = *reinterpret_cast<const u32x4 *>(x_src[i] + (int64_t)step * kBK);
+  };
+  auto load_w = [&](int step) {
+    wr = *reinterpret_cast<const u32x4 *>(w_src + 32 * (int64_t)step);
+    const int64_t b = w_sc + step;
+    if constexpr (DQ) {
+      wq = sc.q[b];
+      wsig = sc.sigma[b >> 8];
+    } else {
+      wsig = sc.absmax[b];
+    }
+  };
+  auto store_x = [&](int buf, int i) {
+    const int id = t + kSmThreads * i;
+    *reinterpret_cast<u32x4 *>(xs[buf] + swz(id >> 3, id & 7)) = xr[i];
+  };
+  auto store_w = [&](int buf) {
+    *reinterpret_cast<u32x4 *>(wp[buf] + 32 * w_row + 16 * w_half) = wr;
+    if (w_half == 0) wsc[buf][w_row] = DQ ? __builtin_fmaf((float)wq, wsig, mu) : wsig;
+  };
+
+  const int wave = t >> 6, lane = t & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int my_row = 32 * wave + lr;  // this lane's weight row in the tile
+  f32x16 acc[2][1];
+  zero_acc(&acc[0][0], 2);
+
+  __syncthreads();  // lut
+  load_x(ks0, 0);
+  load_x(ks0, 1);
+  load_w(ks0);
+  if (split == 0) {
+    stage_lora<kSmBM, kSmThreads>(ls_u, u, m0, M, r, 0, s, t);
+    stage_lora<kSmBN, kSmThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
+  }
+  store_x(0, 0);
+  store_x(0, 1);
+  store_w(0);
+  {
+    const int nx = ks0 + 1 < ks1 ? ks0 + 1 : ks0;
+    load_x(nx, 0);
+    load_x(nx, 1);
+    load_w(nx);
+  }
+  __syncthreads();
+  for (int k = ks0; k < ks1; ++k) {
+    const int cur = (k - ks0) & 1;
+    const int pf = k + 2 < ks1 ? k + 2 : ks1 - 1;
+    const uint8_t *xb = xs[cur];
+    const u32x4 wv = *reinterpret_cast<const u32x4 *>(wp[cur] + 32 * my_row + 16 * lk);
+    const float wa = wsc[cur][my_row];
+    u32x4 xa[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      xa[0][i] = *reinterpret_cast<const u32x4 *>(xb + swz(32 * i + lr, 4 * lk));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          xa[nb][i] = *reinterpret_cast<const u32x4 *>(xb + swz(32 * i + lr, 4 * lk + kk + 1));
+      }
+      // the 8 codes of op kk: bytes 4 kk .. 4 kk + 3 of the lane's 16
+      u32x4 wop;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float2 p = lut[(wv[kk] >> (8 * bb)) & 0xFF];
+        wop[bb] = pack_bf16x2(p.x * wa, p.y * wa);
+      }
+      // staging of step k + 1 into the other buffer, one piece per op, each
+      // register refilled for step k + 2 right after it was stored
+      if (kk < 2) {
+        store_x(cur ^ 1, kk);
+        load_x(pf, kk);
+      } else if (kk == 2) {
+        store_w(cur ^ 1);
+        load_w(pf);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][0] = mfma32(wop, xa[cb][i], acc[i][0]);
+    }
+    __syncthreads();
+  }
+
+  // LoRA bypass: acc += B (s u)^T, 16 ranks per MFMA step, first slice only
+  for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
+    if (j0 > 0) {
+      __syncthreads();
+      stage_lora<kSmBM, kSmThreads>(ls_u, u, m0, M, r, j0, s, t);
+      stage_lora<kSmBN, kSmThreads>(ls_b, B, n0, N, r, j0, 1.0f, t);
+      __syncthreads();
+    }
+    const u32x4 bb = lora_frag(ls_b, my_row, lk);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = mfma32(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
+  }
+  const int64_t col = n0 + 32 * wave;
+  if (nsplit > 1)
+    store_tile_f32<2, 1>(part + (int64_t)split * M * N, N, M, N, m0, col, acc, lane);
+  else if (n0 + kSmBN <= N && N % 8 == 0)  // per-wave slices of 32 rows in a dead staging buffer
+    store_tile_lds<2, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
+  else
+    store_tile_t<2, 1>(y, N, M, N, m0, col, acc, lane);
 }
 
 // ===========================================================================
@@ -711,10 +877,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   }
   // K % 128 == 0 here, so every tile is full in the column direction
   if (nsplit > 1)
-    store_tile_f32<NJ>(part + (int64_t)split * M * K, K, M, K, m0 + 128 * wm, k0 + TX * wn, acc,
+    store_tile_f32<4, NJ>(part + (int64_t)split * M * K, K, M, K, m0 + 128 * wm, k0 + TX * wn, acc,
                        lane);
   else
-    store_tile_lds<NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
+    store_tile_lds<4, NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
                        &ds[0][0] + wave * 32 * (2 * TX + 16), lane);
 }
 
@@ -727,16 +893,18 @@ static int pick_width(int64_t M, int64_t cols, int64_t divisor_ok) {
   return 128;
 }
 
-// Split-K: a launch with fewer tiles than compute units (a few token tiles,
-// e.g. 64 to 512 tokens) leaves units idle while each workgroup walks the
-// whole contraction.  Its contraction is then split into S slices (grid
-// rows) that write fp32 partial tiles, summed in fixed order by
-// k_reduce_split.  S minimises (waves of 256 workgroups) x (steps per slice
-// + ~4 steps of prologue and epilogue), keeps >= 8 steps per slice and the
-// partial buffer <= 64 MB, and prefers the smaller S on ties; it depends
-// only on the shape.
-static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols) {
-  if (tiles >= 256 || tiles <= 0 || cols % 4 != 0) return 1;
+// Split-K: a launch with fewer tiles than the chip runs at once (a few
+// token tiles) leaves units idle while each workgroup walks the whole
+// contraction.  Its contraction is then split into S slices (grid rows) that
+// write fp32 partial tiles, summed in fixed order by k_reduce_split.  S
+// minimises (waves of `slots` workgroups: 256 for the 256-token kernels, one
+// per compute unit; 512 for the few-token forward, which runs up to four per
+// unit but gains little past two) x (steps per slice + ~4 steps of prologue
+// and epilogue), keeps >= 8 steps per slice
+// and the partial buffer <= 64 MB, and prefers the smaller S on ties; it
+// depends only on the shape.
+static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols, int64_t slots = 256) {
+  if (tiles >= slots || tiles <= 0 || cols % 4 != 0) return 1;
   int64_t smax = steps / 8;
   if (smax > 16) smax = 16;
   const int64_t per = M * cols * 4;
@@ -745,7 +913,7 @@ static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols) {
   int best = 1;
   double best_cost = (double)steps + 4.0;  // S = 1: one wave
   for (int64_t S = 2; S <= smax; ++S) {
-    const double waves = (double)((tiles * S + 255) / 256);
+    const double waves = (double)((tiles * S + slots - 1) / slots);
     const double cost = waves * ((double)steps / (double)S + 4.0);
     if (cost < best_cost) {
       best_cost = cost;
@@ -755,7 +923,14 @@ static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols) {
   return best;
 }
 
+// Forward tile: 64 tokens x 128 outputs (k_gemm_fwd_small) up to kFwdSmallM
+// tokens, else 256 tokens x pick_width outputs (measured on the 8B MLP
+// shapes: the small tile is faster up to 128 tokens, slower at 256).
+constexpr int64_t kFwdSmallM = 128;
+
 static int fwd_split(int64_t M, int64_t N, int64_t K) {
+  if (M <= kFwdSmallM)
+    return split_count(((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN), K >> 6, M, N, 512);
   const int bn = pick_width(M, N, 1);
   return split_count(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn), K >> 6, M, N);
 }
@@ -787,6 +962,24 @@ static int reduce_split(const float *part, int S, int64_t count, uint16_t *out,
 int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
                     int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
                     float s, uint16_t *y, hipStream_t stream, float *part) {
+  if (M <= kFwdSmallM) {
+    const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+    const int S = part ? fwd_split(M, N, K) : 1;
+    const bool dq = sc.absmax == nullptr;
+#define QL_FWS(LT, DQV)                                                                          \
+  hipLaunchKernelGGL((k_gemm_fwd_small<LT, DQV>), dim3((unsigned)G, (unsigned)S),               \
+                     dim3(kSmThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, \
+                     y, part, S)
+    if (lora_dtype == QL_BF16) {
+      if (dq) QL_FWS(uint16_t, true); else QL_FWS(uint16_t, false);
+    } else {
+      if (dq) QL_FWS(float, true); else QL_FWS(float, false);
+    }
+#undef QL_FWS
+    QL_HIP_CHECK_LAUNCH();
+    if (S > 1) return reduce_split(part, S, M * N, y, stream);
+    return QL_OK;
+  }
   const int bn = pick_width(M, N, 1);
   const int64_t G = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
   const int S = part ? fwd_split(M, N, K) : 1;
