@@ -8,11 +8,15 @@ step's algorithmic TFLOP/s (4MNK + 6Mr(K+N) per projection).
 
 In the same run (reported beside the step):
   roofline     the forward GEMM timed alone in a loop with HIP events
+  rows         each step row per projection, timed through the entry points
+  few_tokens   the gate projection at 17 .. 512 tokens, forward and backward
+  dropout      the gate projection with LoRA dropout 0.05 against without
   decode_gemv  Llama-3-8B attention projection (4096x4096) at M = 1, 4, 16,
                packed-weight GB/s, rotating over 64 weight copies so the
                256 MB Infinity Cache cannot hold them
   quantize     NF4 + double quantisation and full dequantisation of an
                8B-shaped weight set, GB/s and bits/param
+  optimizer    one AdamW step over an 8B model's LoRA factors
   cpu_baseline the CPU oracle on a bounded sample of the step (host cores)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -247,12 +251,91 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        result["few_tokens"] = bench_few_tokens(q, si, dev)
+        result["dropout"] = bench_dropout(q, si, dev)
         result["decode_gemv"] = bench_decode(q, si, dev)
         result["quantize"] = bench_quantize(q, si, dev)
         result["optimizer"] = bench_adamw(q, si, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(si, M, r, alpha)
     print(json.dumps(result), flush=True)
+
+
+def bench_few_tokens(q, si, dev, token_counts=(17, 64, 128, 256, 512)):
+    """The gate projection (14336x4096, NF4 + double quant, r=16) with few
+    tokens: forward (u + y) and backward (g, dA, dB, dx) per call, eager."""
+    c = si.MLP_8B
+    N, K = c["projs"]["gate"]
+    r, alpha = c["r"], c["alpha"]
+    W = None
+    out = {"workload": "gate projection 14336x4096 NF4 + double quant, r=16, alpha=32, bf16, "
+                       "forward and backward per call (eager, every launch of the call)",
+           "unit": "us"}
+    for M in token_counts:
+        t = si.linear_inputs(c["config"], M, N, K, r, device=dev)
+        if W is None:
+            W = q.nf4_quantize(t["W"], double_quant=True)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        u = torch.empty((M, r), dtype=torch.float32, device=dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+        dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+        wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
+        wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, dev)
+        tf = timed(lambda: q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], alpha, y=y, u_save=u,
+                                              ws=wsf), 30, 3)
+        tb = timed(lambda: q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], alpha,
+                                              u_saved=u, dx=dx, dA=dA, dB=dB, ws=wsb), 30, 3)
+        fl = layer_flops(M, N, K, r)
+        out[f"M{M}"] = {"fwd_us": round(tf * 1e3, 2), "bwd_us": round(tb * 1e3, 2),
+                        "fwd_bwd_TFLOPs": round(fl / ((tf + tb) * 1e-3) / 1e12, 1),
+                        "fwd_packed_weight_GBps": round(W.storage_bytes() / (tf * 1e-3) / 1e9, 1)}
+        log(f"few tokens M={M}: fwd {tf * 1e3:.1f} us, bwd {tb * 1e3:.1f} us")
+        del t, y, u, dx, dA, dB, wsf, wsb
+    del W
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_dropout(q, si, dev):
+    """LoRA dropout (p = 0.05) on the gate projection at 2048 tokens: the
+    forward + backward with dropout against the same without it."""
+    c = si.MLP_8B
+    N, K = c["projs"]["gate"]
+    M, r, alpha = c["M"], c["r"], c["alpha"]
+    t = si.linear_inputs(c["config"], M, N, K, r, device=dev)
+    W = q.nf4_quantize(t["W"], double_quant=True)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((M, r), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
+    wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, dev)
+
+    def plain():
+        q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], alpha, y=y, u_save=u, ws=wsf)
+        q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], alpha, u_saved=u, dx=dx, dA=dA,
+                           dB=dB, ws=wsb)
+
+    def dropped():
+        q.qlora_linear_fwd_dropout(t["x"], W, t["A"], t["B"], alpha, 0.05, 1234, y=y, u_save=u,
+                                   ws=wsf)
+        q.qlora_linear_bwd_dropout(t["dy"], t["x"], W, t["A"], t["B"], alpha, 0.05, 1234,
+                                   u_saved=u, dx=dx, dA=dA, dB=dB, ws=wsb)
+
+    tp = timed(plain, 20, 3)
+    td = timed(dropped, 20, 3)
+    fl = layer_flops(M, N, K, r)
+    out = {"workload": "gate projection 2048x14336x4096 NF4 + double quant, r=16, lora_dropout "
+                       "0.05, forward + backward", "unit": "us",
+           "with_dropout_us": round(td * 1e3, 2), "without_us": round(tp * 1e3, 2),
+           "with_dropout_TFLOPs": round(fl / (td * 1e-3) / 1e12, 1),
+           "overhead_frac": round(td / tp - 1.0, 4)}
+    log(f"dropout: {td * 1e3:.1f} us with, {tp * 1e3:.1f} us without")
+    del t, W, y, u, dx, dA, dB, wsf, wsb
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(q, si, dev, copies=64, iters=1000):
