@@ -11,6 +11,8 @@ In the same run (reported beside the step):
   rows         each step row per projection, timed through the entry points
   few_tokens   the gate projection at 17 .. 512 tokens, forward and backward
   dropout      the gate projection with LoRA dropout 0.05 against without
+  formats      the gate projection in each storage variant (blocks of 64 or
+               128, with or without double quantisation)
   decode_gemv  Llama-3-8B attention projection (4096x4096) at M = 1, 4, 16,
                packed-weight GB/s, rotating over 64 weight copies so the
                256 MB Infinity Cache cannot hold them
@@ -253,6 +255,7 @@ def main():
     if not args.no_extras:
         result["few_tokens"] = bench_few_tokens(q, si, dev)
         result["dropout"] = bench_dropout(q, si, dev)
+        result["formats"] = bench_formats(q, si, dev)
         result["decode_gemv"] = bench_decode(q, si, dev)
         result["quantize"] = bench_quantize(q, si, dev)
         result["optimizer"] = bench_adamw(q, si, dev)
@@ -334,6 +337,52 @@ def bench_dropout(q, si, dev):
            "overhead_frac": round(td / tp - 1.0, 4)}
     log(f"dropout: {td * 1e3:.1f} us with, {tp * 1e3:.1f} us without")
     del t, W, y, u, dx, dA, dB, wsf, wsb
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_formats(q, si, dev):
+    """The NF4 storage variants on the gate projection (14336x4096, 2048
+    tokens, r=16): blocks of 64 or 128 weights, with or without double
+    quantisation of the block constants.  Per format: bits/param, quantise
+    time of the weight, and the layer's forward + backward."""
+    c = si.MLP_8B
+    N, K = c["projs"]["gate"]
+    M, r, alpha = c["M"], c["r"], c["alpha"]
+    t = si.linear_inputs(c["config"], M, N, K, r, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((M, r), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
+    wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, dev)
+    wsq = q.workspace(q.QL_OP_QUANTIZE, 0, N, K, 0, dev)
+    out = {"workload": "gate projection 2048x14336x4096, r=16, alpha=32, bf16: quantise the "
+                       "weight, then forward + backward", "unit": "us"}
+    fl = layer_flops(M, N, K, r)
+    fmts = [(block, dq) for block in (64, 128) for dq in (True, False)]
+    Ws = {}
+    for block, dq in fmts:
+        W = q.NF4Weight.empty(N, K, dq, dev, block=block)
+        tq = timed(lambda: q.nf4_quantize(t["W"], dq, out=W, ws=wsq, block=block), 20, 3)
+        Ws[(block, dq)] = (W, tq)
+
+    def fb(W):
+        q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], alpha, y=y, u_save=u, ws=wsf)
+        q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], alpha, u_saved=u, dx=dx, dA=dA,
+                           dB=dB, ws=wsb)
+    timed(lambda: fb(Ws[fmts[0]][0]), 20, 0)  # clocks up before the first timed format
+    for block, dq in fmts:
+        W, tq = Ws[(block, dq)]
+        tl = timed(lambda: fb(W), 10, 3)
+        key = f"block{block}_{'dq' if dq else 'fp32absmax'}"
+        out[key] = {"bits_per_param": round(8 * W.storage_bytes() / (N * K), 5),
+                    "quantize_us": round(tq * 1e3, 2), "fwd_bwd_us": round(tl * 1e3, 2),
+                    "fwd_bwd_TFLOPs": round(fl / (tl * 1e-3) / 1e12, 1)}
+        log(f"format {key}: {out[key]}")
+    del Ws
+    del t, y, u, dx, dA, dB, wsf, wsb, wsq
     torch.cuda.empty_cache()
     return out
 

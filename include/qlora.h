@@ -59,9 +59,11 @@ extern "C" {
 #define QL_OP_FWD 1
 #define QL_OP_BWD 2
 
-/* Fixed format parameters: 64 weights per NF4 block, 256 block constants per
- * double-quantisation block. */
+/* Format parameters: 64 weights per NF4 block (or 128: 22. QLoRA and 4bit
+ * Quantization, engineering notes: 64 or 128 parameters share one scale),
+ * 256 block constants per double-quantisation block. */
 #define QL_NF4_BLOCK 64
+#define QL_NF4_BLOCK_LARGE 128
 #define QL_DQ_BLOCK 256
 
 /*
@@ -75,7 +77,8 @@ extern "C" {
  *  absmax_q      int8 [nb]: codes of the centred constants (double_quant == 1).
  *  absmax_scale  fp32 [nb2]: one scale per block2 codes (double_quant == 1).
  *  absmax_mean   fp32 [1]: per-tensor mean of the constants (double_quant == 1).
- *  block, block2 must be QL_NF4_BLOCK and QL_DQ_BLOCK in this build.
+ *  block is QL_NF4_BLOCK (64) or QL_NF4_BLOCK_LARGE (128); block2 must be
+ *  QL_DQ_BLOCK.  The layer entry points need cols % block == 0.
  *
  * Dequantised element i (block b = i / block):
  *   a'  = absmax[b]                                         (no double quant)
@@ -106,6 +109,14 @@ typedef struct ql_nf4 {
 int ql_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t bytes_out[5]);
 
 /*
+ * Host only.  As ql_nf4_sizes, for blocks of `block` weights (QL_NF4_BLOCK or
+ * QL_NF4_BLOCK_LARGE; QL_EINVAL otherwise).  ql_nf4_sizes is this with
+ * block = QL_NF4_BLOCK.
+ */
+int ql_nf4_sizes_block(int64_t rows, int64_t cols, int32_t block, int32_t double_quant,
+                       size_t bytes_out[5]);
+
+/*
  * Host only.  Workspace bytes an operation needs (a multiple of 256).
  *   QL_OP_QUANTIZE: M and r ignored, N x K is the weight (double-quant form;
  *                   the single-level form needs none).
@@ -121,7 +132,8 @@ size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
  *             16-byte aligned.
  *   q         host struct describing device outputs: packed and either absmax
  *             (double_quant 0) or absmax_q, absmax_scale, absmax_mean (1).
- * Per block: a = max |w|; v = w / a (correctly rounded fp32 division); the
+ * Per block (64 or 128 consecutive elements of the flattened weight):
+ * a = max |w|; v = w / a (correctly rounded fp32 division); the
  * index is the nearest codepoint of v, ties to the lower index; a zero block
  * codes every element as index 7 (the exact zero).  Double quantisation:
  * mu = mean of all a (exact sum, fp64 division, rounded to fp32);
@@ -148,7 +160,7 @@ int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream);
  *     u = x A^T,   y = x W^^T + s u B^T,   s = fp32(alpha / r)
  * with W^ dequantised on the fly, never stored.
  *   x       device [M, K] act_dtype (QL_BF16, or QL_F32 for the fp32 path)
- *   W       host struct, rows = N, cols = K, K % 64 == 0
+ *   W       host struct, rows = N, cols = K, K % W->block == 0
  *   A, B    device [r, K] and [N, r] of lora_dtype (QL_BF16 or QL_F32)
  *   r       1..128;  alpha any finite value
  *   y       device [M, N] act_dtype (overwritten)

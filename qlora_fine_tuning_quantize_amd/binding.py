@@ -19,10 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libqlora.so")
 QL_OK, QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP = range(7)
 QL_F32, QL_BF16 = 0, 1
 QL_OP_QUANTIZE, QL_OP_FWD, QL_OP_BWD = 0, 1, 2
-NF4_BLOCK, DQ_BLOCK = 64, 256
+NF4_BLOCK, NF4_BLOCK_LARGE, DQ_BLOCK = 64, 128, 256
 
 # every extern "C" symbol declared in include/qlora.h
-EXPORTED = ("ql_nf4_sizes", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
+EXPORTED = ("ql_nf4_sizes", "ql_nf4_sizes_block", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
             "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "qlora_linear_bwd_acc",
             "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "ql_dropout_mask",
             "ql_adamw_step", "ql_strerror", "ql_abi_version")
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     sp = ctypes.POINTER(QlNf4)
     L.ql_nf4_sizes.argtypes = [i64, i64, i32, ctypes.POINTER(sz * 5)]
     L.ql_nf4_sizes.restype = ctypes.c_int
+    L.ql_nf4_sizes_block.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz * 5)]
+    L.ql_nf4_sizes_block.restype = ctypes.c_int
     L.ql_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     L.ql_workspace_bytes.restype = sz
     L.nf4_quantize.argtypes = [p, i32, sp, p, sz, p]
@@ -120,9 +122,14 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def nf4_sizes(rows: int, cols: int, double_quant: bool) -> list[int]:
+def nf4_sizes(rows: int, cols: int, double_quant: bool, block: int = NF4_BLOCK) -> list[int]:
     out = (ctypes.c_size_t * 5)()
-    _check(lib().ql_nf4_sizes(rows, cols, int(double_quant), ctypes.byref(out)), "ql_nf4_sizes")
+    if block == NF4_BLOCK:
+        _check(lib().ql_nf4_sizes(rows, cols, int(double_quant), ctypes.byref(out)),
+               "ql_nf4_sizes")
+    else:
+        _check(lib().ql_nf4_sizes_block(rows, cols, int(block), int(double_quant),
+                                        ctypes.byref(out)), "ql_nf4_sizes_block")
     return list(out)
 
 
@@ -137,7 +144,8 @@ def workspace(op: int, M: int, N: int, K: int, r: int, device) -> torch.Tensor:
 
 @dataclass
 class NF4Weight:
-    """Device buffers of an NF4-quantised weight [rows = N, cols = K]."""
+    """Device buffers of an NF4-quantised weight [rows = N, cols = K] with
+    blocks of `block` (64 or 128) weights."""
     packed: torch.Tensor
     rows: int
     cols: int
@@ -146,15 +154,17 @@ class NF4Weight:
     absmax_q: torch.Tensor | None = None
     absmax_scale: torch.Tensor | None = None
     absmax_mean: torch.Tensor | None = None
+    block: int = NF4_BLOCK
 
     @staticmethod
-    def empty(rows: int, cols: int, double_quant: bool, device) -> "NF4Weight":
-        b = nf4_sizes(rows, cols, double_quant)
+    def empty(rows: int, cols: int, double_quant: bool, device,
+              block: int = NF4_BLOCK) -> "NF4Weight":
+        b = nf4_sizes(rows, cols, double_quant, block)
         # round each buffer up to 16 bytes so all vector loads stay in bounds
         mk = lambda n, dt, es: torch.empty(max(1, (n + 15) // 16 * 16 // es), dtype=dt,
                                            device=device)
         w = NF4Weight(packed=mk(b[0], torch.uint8, 1), rows=rows, cols=cols,
-                      double_quant=double_quant)
+                      double_quant=double_quant, block=block)
         if double_quant:
             w.absmax_q = mk(b[2], torch.int8, 1)
             w.absmax_scale = mk(b[3], torch.float32, 4)
@@ -169,18 +179,19 @@ class NF4Weight:
                      self.absmax_q.data_ptr() if self.absmax_q is not None else None,
                      self.absmax_scale.data_ptr() if self.absmax_scale is not None else None,
                      self.absmax_mean.data_ptr() if self.absmax_mean is not None else None,
-                     self.rows, self.cols, NF4_BLOCK, DQ_BLOCK, int(self.double_quant), 0)
+                     self.rows, self.cols, self.block, DQ_BLOCK, int(self.double_quant), 0)
 
     def storage_bytes(self) -> int:
-        return sum(nf4_sizes(self.rows, self.cols, self.double_quant))
+        return sum(nf4_sizes(self.rows, self.cols, self.double_quant, self.block))
 
 
 def nf4_quantize(w: torch.Tensor, double_quant: bool = True, out: NF4Weight | None = None,
-                 ws: torch.Tensor | None = None) -> NF4Weight:
-    """NF4-quantise a 2-D weight [N, K] (bf16 or fp32, on the GPU)."""
+                 ws: torch.Tensor | None = None, block: int = NF4_BLOCK) -> NF4Weight:
+    """NF4-quantise a 2-D weight [N, K] (bf16 or fp32, on the GPU) with blocks
+    of `block` (64 or 128) weights."""
     assert w.dim() == 2 and w.is_contiguous() and w.is_cuda
     N, K = w.shape
-    q = out or NF4Weight.empty(N, K, double_quant, w.device)
+    q = out or NF4Weight.empty(N, K, double_quant, w.device, block)
     if ws is None and double_quant:
         ws = workspace(QL_OP_QUANTIZE, 0, N, K, 0, w.device)
     st = q.struct()

@@ -27,7 +27,8 @@ int check_nf4(const ql_nf4 *q) {
   if (q->rows <= 0 || q->cols <= 0) return QL_EINVAL;
   if (q->double_quant != 0 && q->double_quant != 1) return QL_EINVAL;
   if (q->reserved != 0) return QL_EINVAL;
-  if (q->block != QL_NF4_BLOCK || q->block2 != QL_DQ_BLOCK) return QL_EUNSUPPORTED;
+  if ((q->block != QL_NF4_BLOCK && q->block != QL_NF4_BLOCK_LARGE) || q->block2 != QL_DQ_BLOCK)
+    return QL_EUNSUPPORTED;
   if (!q->packed) return QL_EINVAL;
   if (q->double_quant) {
     if (!q->absmax_q || !q->absmax_scale || !q->absmax_mean) return QL_EINVAL;
@@ -44,6 +45,7 @@ BlockScales scales_of(const ql_nf4 *q) {
   sc.q = q->absmax_q;
   sc.sigma = q->absmax_scale;
   sc.mu = q->absmax_mean;
+  sc.shift = q->block == 128 ? 1 : 0;
   return sc;
 }
 
@@ -105,7 +107,7 @@ int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const voi
   if (check_dtype(act_dtype) || check_dtype(lora_dtype)) return QL_EINVAL;
   if (M <= 0 || r <= 0) return QL_EINVAL;
   if (r > 128) return QL_EUNSUPPORTED;
-  if (W->cols % QL_NF4_BLOCK != 0) return QL_ESHAPE;
+  if (W->cols % W->block != 0) return QL_ESHAPE;  // blocks never straddle weight rows
   if (!A || !B) return QL_EINVAL;
   if (!aligned16(A) || !aligned16(B)) return QL_EALIGN;
   if (!(alpha == alpha) || alpha - alpha != 0.0f) return QL_EINVAL;  // not finite
@@ -128,7 +130,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 103; }
+int ql_abi_version(void) { return 104; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -144,10 +146,16 @@ const char *ql_strerror(int status) {
 }
 
 int ql_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t bytes_out[5]) {
-  if (!bytes_out || rows <= 0 || cols <= 0 || (double_quant != 0 && double_quant != 1))
+  return ql_nf4_sizes_block(rows, cols, QL_NF4_BLOCK, double_quant, bytes_out);
+}
+
+int ql_nf4_sizes_block(int64_t rows, int64_t cols, int32_t block, int32_t double_quant,
+                       size_t bytes_out[5]) {
+  if (!bytes_out || rows <= 0 || cols <= 0 || (double_quant != 0 && double_quant != 1) ||
+      (block != QL_NF4_BLOCK && block != QL_NF4_BLOCK_LARGE))
     return QL_EINVAL;
   const int64_t n = rows * cols;
-  const int64_t nb = ceil_div(n, QL_NF4_BLOCK);
+  const int64_t nb = ceil_div(n, block);
   const int64_t nb2 = ceil_div(nb, QL_DQ_BLOCK);
   bytes_out[0] = (size_t)((n + 1) / 2);
   bytes_out[1] = double_quant ? 0 : (size_t)nb * 4;
@@ -180,16 +188,17 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
   if (!w || check_dtype(w_dtype)) return QL_EINVAL;
   if (!aligned16(w)) return QL_EALIGN;
   const int64_t n = q->rows * q->cols;
-  const int64_t nb = ceil_div(n, QL_NF4_BLOCK);
+  const int64_t nb = ceil_div(n, q->block);
   hipStream_t s = (hipStream_t)stream;
-  if (!q->double_quant) return launch_nf4_quantize(w, w_dtype, n, q->packed, q->absmax, s);
-  const QuantWs L = quant_ws(n);
+  if (!q->double_quant)
+    return launch_nf4_quantize(w, w_dtype, n, q->block, q->packed, q->absmax, s);
+  const QuantWs L = quant_ws(n);  // sized for blocks of 64, an upper bound for 128
   if (!ws || ws_bytes < L.total) return QL_EWORKSPACE;
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
   uint8_t *base = (uint8_t *)ws;
   float *absmax = (float *)(base + L.absmax);
   double *partial = (double *)(base + L.partial);
-  st = launch_nf4_quantize(w, w_dtype, n, q->packed, absmax, s);
+  st = launch_nf4_quantize(w, w_dtype, n, q->block, q->packed, absmax, s);
   if (st) return st;
   return launch_double_quant(absmax, nb, partial, q->absmax_q, q->absmax_scale, q->absmax_mean, s);
 }

@@ -82,14 +82,19 @@ __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p, int64_t i,
   p[i] = f32_to_bf16_bits(v);
 }
 
-// The constant of NF4 block b: stored fp32 absmax, or rebuilt from its 8-bit
-// code with one rounding.
+// The block constants of an NF4 weight: stored fp32 absmax, or rebuilt
+// from their 8-bit codes with one rounding.  Kernels address them by the
+// index c of a 64-element chunk of the flattened weight; an NF4 block is
+// 64 << shift elements (64 or 128), so chunk c lies in block c >> shift.
 struct BlockScales {
   const float *absmax;   // non-null: single-level form
   const int8_t *q;       // double-quantised form
   const float *sigma;
   const float *mu;
-  __device__ __forceinline__ float operator()(int64_t b) const {
+  int shift;             // 0: blocks of 64, 1: blocks of 128
+  __device__ __forceinline__ int64_t index(int64_t c) const { return c >> shift; }
+  __device__ __forceinline__ float operator()(int64_t c) const {
+    const int64_t b = c >> shift;
     if (absmax) return absmax[b];
     return __builtin_fmaf((float)q[b], sigma[b >> 8], mu[0]);
   }

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
       const u32x2 v = *reinterpret_cast<const u32x2 *>(w_src + 32 * (int64_t)step);
       wr[0] = v.x; wr[1] = v.y;
     }
-    const int64_t b = w_sc + step;
+    const int64_t b = sc.index(w_sc + step);
     if constexpr (DQ) {
       wq = sc.q[b];
       wsig = sc.sigma[b >> 8];
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   };
   auto load_w = [&](int step) {
     wr = *reinterpret_cast<const u32x4 *>(w_src + 32 * (int64_t)step);
-    const int64_t b = w_sc + step;
+    const int64_t b = sc.index(w_sc + step);
     if constexpr (DQ) {
       wq = sc.q[b];
       wsig = sc.sigma[b >> 8];
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
       wr[2] = v[2];
       wr[3] = v[3];
     }
-    const int64_t b = e >> 6;  // the lane's codes lie inside one 64-block
+    const int64_t b = sc.index(e >> 6);  // the lane's codes lie inside one 64-chunk
     if constexpr (DQ) {
       wq = sc.q[b];
       wsig = sc.sigma[b >> 8];

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
       const int e = t + kGemvThreads * i;
       const int row = e >> 6, b = e & 63;
       const int64_t nn = n0 + row < N ? n0 + row : N - 1;
-      const int64_t g = nn * KB + rb0 + (b < RB ? b : RB - 1);
+      const int64_t g = sc.index(nn * KB + rb0 + (b < RB ? b : RB - 1));
       qv[i] = DQ ? (int)sc.q[g] : 0;
       sv[i] = DQ ? sc.sigma[g >> 8] : sc.absmax[g];
     }

@@ -9,8 +9,9 @@
 namespace qlora {
 
 // quant.hip
-int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, uint8_t *packed, float *absmax,
-                        hipStream_t stream);
+// block: 64 or 128 elements per NF4 block
+int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
+                        float *absmax, hipStream_t stream);
 size_t dq_partial_count(int64_t nb);
 int launch_double_quant(const float *absmax, int64_t nb, double *partial, int8_t *q, float *sigma,
                         float *mean_out, hipStream_t stream);

@@ -93,31 +93,36 @@ __device__ __forceinline__ uint32_t nf4_index_fast(float vp, const BucketEntry *
   return (uint32_t)e.c + (vp > e.t ? 1u : 0u);
 }
 
-// Max over the 8 lanes of an aligned group (DPP: swap neighbours, swap
-// pairs, then mirror within the group of 8; every lane ends with the max).
-__device__ __forceinline__ float max8_lanes(float m) {
-  const int qp_1032 = 0xB1, qp_2301 = 0x4E, row_half_mirror = 0x141;
+// Max over the L = 8 or 16 lanes of an aligned group (DPP: swap neighbours,
+// swap pairs, mirror within the group of 8, then for 16 mirror within the
+// row of 16; every lane ends with the max).
+template <int L>
+__device__ __forceinline__ float max_lanes(float m) {
+  const int qp_1032 = 0xB1, qp_2301 = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140;
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), qp_1032, 0xF,
                                                             0xF, true)));
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), qp_2301, 0xF,
                                                             0xF, true)));
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), row_half_mirror,
                                                             0xF, 0xF, true)));
+  if constexpr (L == 16)
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), row_mirror,
+                                                              0xF, 0xF, true)));
   return m;
 }
 
 // ---------------------------------------------------------------------------
-// K1: a wave owns 2 runs of 512 consecutive elements (8 NF4 blocks each);
-// in every run lane l takes the 8 elements 8l .. 8l + 7, so each block is
-// held by a group of 8 lanes and every load and store instruction of the
-// wave covers one contiguous span.  All loads are issued first.  The group
+// K1: a wave owns 2 runs of 512 consecutive elements (8 NF4 blocks of 64,
+// or 4 of 128); in every run lane l takes the 8 elements 8l .. 8l + 7, so
+// each block is held by a group of BLK / 8 lanes and every load and store
+// instruction of the wave covers one contiguous span.  All loads are issued first.  The group
 // reduces |w| (DPP), then each lane finds its 8 indices and packs them into
 // one 32-bit word.  The indices are those of the correctly rounded w / a:
 // each lane takes a reciprocal of a once and the index of w times it; a lane with
 // any element in a guard band (or with a block maximum outside the normal
 // range) redoes its 8 elements with the division.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int BLK>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, int64_t n,
                                                       uint8_t *__restrict__ packed,
                                                       float *__restrict__ absmax,
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, i
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
-    m = max8_lanes(m);
+    m = max_lanes<BLK / 8>(m);
     if (e0[j] >= n) continue;  // after the group reduction: lanes past the end only helped
     // element i goes to byte i / 2, high nibble for even i
     uint32_t word = 0x77777777u;  // a zero block: every element is the exact zero
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, i
       for (int b = 0; b < 4; ++b)
         if (e0[j] + 2 * b < n) packed[(e0[j] >> 1) + b] = (uint8_t)(word >> (8 * b));
     }
-    if ((lane & 7) == 0) absmax[e0[j] >> 6] = m;
+    if ((lane & (BLK / 8 - 1)) == 0) absmax[e0[j] / BLK] = m;
   }
 }
 
@@ -370,19 +375,22 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t *__restric
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, uint8_t *packed, float *absmax,
-                        hipStream_t stream) {
+int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
+                        float *absmax, hipStream_t stream) {
   if (n <= 0) return QL_OK;
   // one wave per 1024 elements (2 runs of 512)
   const int64_t waves = (n + 1023) / 1024;
   const dim3 grid((unsigned)((waves + 3) / 4));
   const NF4Thresholds th = nf4_thresholds();
-  if (w_dtype == QL_BF16)
-    hipLaunchKernelGGL(k_nf4_quantize<uint16_t>, grid, dim3(256), 0, stream,
-                       (const uint16_t *)w, n, packed, absmax, th);
-  else
-    hipLaunchKernelGGL(k_nf4_quantize<float>, grid, dim3(256), 0, stream, (const float *)w, n,
-                       packed, absmax, th);
+#define QL_QUANT(T, BLKV)                                                                        \
+  hipLaunchKernelGGL((k_nf4_quantize<T, BLKV>), grid, dim3(256), 0, stream, (const T *)w, n,      \
+                     packed, absmax, th)
+  if (w_dtype == QL_BF16) {
+    if (block == 128) QL_QUANT(uint16_t, 128); else QL_QUANT(uint16_t, 64);
+  } else {
+    if (block == 128) QL_QUANT(float, 128); else QL_QUANT(float, 64);
+  }
+#undef QL_QUANT
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 103
+    assert L.ql_abi_version() == 104
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -44,6 +44,19 @@ def test_nf4_sizes_and_bits_per_param(orc):
     # ragged and odd sizes
     assert q.nf4_sizes(3, 7, False) == [11, 4, 0, 0, 0]
     assert q.nf4_sizes(1, 64 * 257, True) == [32 * 257, 0, 257, 8, 4]
+
+
+def test_nf4_sizes_block_128():
+    """Blocks of 128 weights (one constant per 128): 4.25 bits/param without
+    double quantisation, 4 + 8/128 + 32/(128*256) (+ 32/n) with it."""
+    n = 4096 * 4096
+    sz = q.nf4_sizes(4096, 4096, True, block=128)
+    assert sz == [n // 2, 0, n // 128, 4 * (n // 128 // 256), 4]
+    assert 8 * sum(sz) / n == 4 + 8 / 128 + 32 / (128 * 256) + 32 / n
+    assert 8 * sum(q.nf4_sizes(4096, 4096, False, block=128)) / n == 4.25
+    assert q.nf4_sizes(3, 7, False, block=128) == [11, 4, 0, 0, 0]
+    with pytest.raises(ValueError):
+        q.nf4_sizes(4, 4, False, block=96)
 
 
 def test_workspace_sizes():
@@ -77,7 +90,8 @@ def _desc(rows=64, cols=64, dq=0, **kw):
 @no_gpu
 @pytest.mark.parametrize("desc,expect", [
     (dict(rows=0), b.QL_EINVAL), (dict(cols=-1), b.QL_EINVAL), (dict(dq=2), b.QL_EINVAL),
-    (dict(block=128), b.QL_EUNSUPPORTED), (dict(block2=512), b.QL_EUNSUPPORTED),
+    (dict(block=96), b.QL_EUNSUPPORTED), (dict(block=32), b.QL_EUNSUPPORTED),
+    (dict(block2=512), b.QL_EUNSUPPORTED),
     (dict(packed=None), b.QL_EINVAL), (dict(absmax=None), b.QL_EINVAL),
     (dict(dq=1, absmax_mean=None), b.QL_EINVAL), (dict(packed=FAKE + 8), b.QL_EALIGN),
     (dict(reserved=1), b.QL_EINVAL),
@@ -128,6 +142,7 @@ def test_linear_fwd_rejects_bad_arguments():
     assert _fwd(L, y=FAKE + 2) == b.QL_EALIGN
     assert _fwd(L, A=FAKE + 8) == b.QL_EALIGN
     assert _fwd(L, desc=_desc(rows=128, cols=100)) == b.QL_ESHAPE
+    assert _fwd(L, desc=_desc(rows=128, cols=192, block=128)) == b.QL_ESHAPE  # K % 128
     assert _fwd(L, ws=0) == b.QL_EWORKSPACE
     assert _fwd(L, ws_bytes=255) == b.QL_EWORKSPACE
     assert _fwd(L, ws=FAKE + 16) == b.QL_EALIGN

@@ -24,10 +24,10 @@ def _say(*a):
 # ---------------------------------------------------------------------------
 # quantisation / double quantisation / dequantisation: bit-exact
 # ---------------------------------------------------------------------------
-def _check_quant(orc, w_cpu: torch.Tensor, dq: bool):
-    Wq = q.nf4_quantize(w_cpu.to(DEV).contiguous(), double_quant=dq)
+def _check_quant(orc, w_cpu: torch.Tensor, dq: bool, block: int = 64):
+    Wq = q.nf4_quantize(w_cpu.to(DEV).contiguous(), double_quant=dq, block=block)
     torch.cuda.synchronize()
-    st = orc.quantize_nf4(host(w_cpu).reshape(-1), double_quant=dq)
+    st = orc.quantize_nf4(host(w_cpu).reshape(-1), double_quant=dq, block=block)
     np.testing.assert_array_equal(host(Wq.packed)[:st["packed"].size], st["packed"])
     if dq:
         np.testing.assert_array_equal(host(Wq.absmax_q)[:st["absmax_q"].size], st["absmax_q"])
@@ -58,6 +58,22 @@ def test_quant_dequant_bit_exact(orc, rows, cols, dtype, dq):
         flat[5] = 0.4                          # 20-sigma outliers
         flat[200] = -0.4
     _check_quant(orc, w, dq)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 127), (1, 128), (1, 129), (3, 5), (7, 129),
+                                       (64, 256), (300, 1000), (33, 128 * 257)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dq", [False, True])
+def test_quant_dequant_bit_exact_block128(orc, rows, cols, dtype, dq):
+    """Blocks of 128 weights (one constant per 128)."""
+    _say(f"quant block 128 rows={rows} cols={cols} dtype={dtype} dq={dq}")
+    w = si.normal((rows, cols), 0.02, seed=rows * 137 + cols, dtype=dtype)
+    flat = w.view(-1)
+    if flat.numel() >= 512:
+        flat[128:256] = 0                      # an all-zero block
+        flat[5] = 0.4                          # 20-sigma outliers
+        flat[300] = -0.4
+    _check_quant(orc, w, dq, block=128)
 
 
 def test_quant_subnormal_and_signed_zero_blocks(orc):
@@ -135,19 +151,19 @@ def test_quant_exhaustive_bf16_ratios(orc, a_exp):
 # the layer: forward and backward
 # ---------------------------------------------------------------------------
 def _layer_case(orc, M, N, K, r, dq, act, lora, alpha=32.0, seed_cfg=90, dy_ones=False,
-                rows=None):
+                rows=None, block=64):
     t = si.linear_inputs(seed_cfg, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora,
                          sub=M + N + K + r)
     if dy_ones:
         t["dy"] = torch.ones((M, N), dtype=act)
     d = {k: v.to(DEV) for k, v in t.items()}
-    W = q.nf4_quantize(d["W"], double_quant=dq)
+    W = q.nf4_quantize(d["W"], double_quant=dq, block=block)
     u = torch.empty((M, r), dtype=torch.float32, device=DEV)
     y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], alpha, u_save=u)
     dx, dA, dB = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], alpha)
     dx2, dA2, dB2 = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], alpha, u_saved=u)
     torch.cuda.synchronize()
-    st = orc.quantize_nf4(host(t["W"]), double_quant=dq)
+    st = orc.quantize_nf4(host(t["W"]), double_quant=dq, block=block)
     w_hat = orc.dequantize(st).reshape(N, K)
     xs = host(t["x"]) if rows is None else host(t["x"])[rows]
     y_ref, u_ref = orc.linear_fwd(xs, w_hat, host(t["A"]), host(t["B"]), alpha, r)
@@ -217,6 +233,30 @@ def test_layer_bf16_parity(orc, M, N, K, r, dq, lora):
     _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e <= BF16_TOL, (k, e)
+
+
+BLOCK128_CASES = [
+    # M, N, K, r, dq, act                       (path exercised)
+    (1, 256, 1024, 16, True, torch.bfloat16),   # decode GEMV
+    (16, 200, 4352, 16, False, torch.bfloat16), # GEMV, second round, ragged N
+    (64, 256, 512, 8, True, torch.bfloat16),    # 64-token forward tile, split
+    (300, 384, 768, 16, True, torch.bfloat16),  # 256-token GEMM, ragged M
+    (77, 1024, 2048, 16, False, torch.bfloat16),# split-K forward and dx
+    (300, 200, 384, 8, True, torch.bfloat16),   # ragged N: guarded tile, tiled dx
+    (4, 256, 256, 8, False, torch.float32),     # fp32 path
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,dq,act", BLOCK128_CASES)
+def test_layer_parity_block128(orc, M, N, K, r, dq, act):
+    """The layer with blocks of 128 weights, every kernel path."""
+    _say(f"layer block 128 M={M} N={N} K={K} r={r} dq={dq} act={act}")
+    got, ref = _layer_case(orc, M, N, K, r, dq, act, act, block=128)
+    for k in ("y", "u", "dx", "dA", "dB"):
+        if act == torch.float32:
+            assert_f32_close(got[k], ref[k], k)
+        else:
+            assert rel_err(got[k], ref[k]) <= BF16_TOL, k
 
 
 @pytest.mark.parametrize("M,N,K,r,act,lora", [

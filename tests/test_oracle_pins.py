@@ -121,7 +121,9 @@ def _quantize_brute(w32: np.ndarray, block: int, cb):
 
 
 @pytest.mark.parametrize("n,block,dtype", [(64, 64, "f32"), (200, 64, "f32"), (129, 64, "bf16"),
-                                           (77, 10, "f32"), (1, 64, "f32"), (64 * 5, 64, "bf16")])
+                                           (77, 10, "f32"), (1, 64, "f32"), (64 * 5, 64, "bf16"),
+                                           (128, 128, "f32"), (300, 128, "bf16"),
+                                           (128 * 3 + 5, 128, "f32")])
 def test_quantize_matches_exact_brute_force(orc, n, block, dtype):
     cb = orc.codebook()
     rng = np.random.default_rng(n * 7 + block)
