@@ -13,11 +13,17 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("M,N,K,r", [(300, 384, 640, 16), (8, 256, 512, 8)])
-def test_graph_replay_matches_eager(M, N, K, r):
-    print(f"graph replay M={M} N={N} K={K} r={r}", flush=True)
+@pytest.mark.parametrize("M,N,K,r,dropout,block", [
+    (300, 384, 640, 16, 0.0, 64),   # 256-token GEMMs
+    (8, 256, 512, 8, 0.0, 64),      # decode GEMV forward
+    (64, 256, 1024, 16, 0.0, 64),   # 64-token forward tiles with split-K
+    (300, 384, 640, 16, 0.1, 64),   # LoRA dropout, forward and backward
+    (64, 256, 1024, 16, 0.0, 128),  # blocks of 128
+])
+def test_graph_replay_matches_eager(M, N, K, r, dropout, block):
+    print(f"graph replay M={M} N={N} K={K} r={r} dropout={dropout} block={block}", flush=True)
     t = {k: v.to(DEV) for k, v in si.linear_inputs(92, M, N, K, r, sub=M).items()}
-    W = q.nf4_quantize(t["W"], double_quant=True)
+    W = q.nf4_quantize(t["W"], double_quant=True, block=block)
     bufs = dict(y=torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
                 u=torch.empty((M, r), dtype=torch.float32, device=DEV),
                 dx=torch.empty((M, K), dtype=torch.bfloat16, device=DEV),
@@ -27,6 +33,13 @@ def test_graph_replay_matches_eager(M, N, K, r):
     wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, DEV)
 
     def step():
+        if dropout > 0:
+            q.qlora_linear_fwd_dropout(t["x"], W, t["A"], t["B"], 32.0, dropout, 77, y=bufs["y"],
+                                       u_save=bufs["u"], ws=wsf)
+            q.qlora_linear_bwd_dropout(t["dy"], t["x"], W, t["A"], t["B"], 32.0, dropout, 77,
+                                       u_saved=bufs["u"], dx=bufs["dx"], dA=bufs["dA"],
+                                       dB=bufs["dB"], ws=wsb)
+            return
         q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], 32.0, y=bufs["y"], u_save=bufs["u"], ws=wsf)
         q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], 32.0, u_saved=bufs["u"],
                            dx=bufs["dx"], dA=bufs["dA"], dB=bufs["dB"], ws=wsb)
