@@ -658,8 +658,20 @@ __device__ __forceinline__ int wswz(int n, int c) {
 // DROP: LoRA dropout on the bypass input; the bypass term of output (m, k)
 // is multiplied by keep(m, k) / (1 - p) (dscale) before the base product is
 // added to it.
-template <int BX, typename LT, bool DQ, bool DROP>
-__global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
+// Token tile BM = 256: 8 waves as 2 (tokens) x 4 (columns), each owning a
+// 128 x BX/4 block; BM = 64 (few tokens): 4 waves as 1 x 4, each owning a
+// 64 x BX/4 block.
+template <int BM>
+struct DxShape {
+  static constexpr int NT = BM == 256 ? 512 : 256;  // threads
+  static constexpr int WM = BM == 256 ? 2 : 1;      // waves along tokens
+  static constexpr int MI = BM / WM / 32;           // 32-row token tiles per wave
+  static constexpr int XC = BM * 8 / NT;            // 16-byte dy chunks per lane per step
+  static constexpr int LPR = NT / kDxBC;            // staging lanes per weight row
+};
+
+template <int BM, int BX, typename LT, bool DQ, bool DROP>
+__global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
                                                       const uint8_t *__restrict__ packed,
                                                       BlockScales sc, int64_t N, int64_t K,
                                                       const float *__restrict__ g,
@@ -667,29 +679,34 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
                                                       uint16_t *__restrict__ dx,
                                                       float *__restrict__ part, int nsplit,
                                                       Dropout drop, float dscale) {
+  constexpr int NT = DxShape<BM>::NT, WM = DxShape<BM>::WM, MI = DxShape<BM>::MI;
+  constexpr int XC = DxShape<BM>::XC, LPR = DxShape<BM>::LPR;
+  constexpr int TM = 32 * MI;  // tokens per wave
   constexpr int TX = BX / 4;
   constexpr int NJ = TX / 32;
-  constexpr int NU = BX / 64;  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
-  __shared__ __attribute__((aligned(16))) uint8_t ds[2][kBM * kRowBytes];  // dy [m][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];   // W^ [n][k] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t ls_g[kBM * kLoraStride];
+  constexpr int NU = BX / (8 * LPR);  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
+  static_assert(XC == 2 || XC == 4, "dy staging is split into 2 or 4 chunks");
+  static_assert(NU == 2 || NU == 4, "a lane stages 2 or 4 code words per step");
+  __shared__ __attribute__((aligned(16))) uint8_t ds[2][BM * kRowBytes];  // dy [m][n] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];  // W^ [n][k] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t ls_g[BM * kLoraStride];
   __shared__ __attribute__((aligned(16))) uint8_t ls_a[BX * kLoraStride];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, kt;
-  tile_of((M + kBM - 1) / kBM, K / BX, mt, kt);
-  const int64_t m0 = mt * kBM, k0 = kt * BX;
+  tile_of((M + BM - 1) / BM, K / BX, mt, kt);
+  const int64_t m0 = mt * BM, k0 = kt * BX;
   const int64_t NS = N / kDxBC;
   // contraction slice of this workgroup (split-K: grid row blockIdx.y)
   const int split = blockIdx.y;
   const int ks0 = (int)(split * NS / nsplit), ks1 = (int)((split + 1) * NS / nsplit);
 
   // weight staging: lane -> row wrow of the step, 8 * NU codes from column wk
-  const int wrow = t >> 3, wk = (t & 7) * 8 * NU;
+  const int wrow = t / LPR, wk = (t % LPR) * 8 * NU;
   const float mu = DQ ? sc.mu[0] : 0.0f;
-  ActStage dr;
+  u32x4 drv[XC];
   uint32_t wr[NU];
   int wq;
   float wsig;
@@ -716,21 +733,24 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     }
   };
   // token rows past M are clamped (their outputs are never stored)
-  const uint16_t *dy_src[4];
+  const uint16_t *dy_src[XC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = t + kThreads * i;
+  for (int i = 0; i < XC; ++i) {
+    const int id = t + NT * i;
     const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
     dy_src[i] = dy + rr * N + 8 * (id & 7);
   }
   auto load_dy_chunk = [&](int step, int i) {
-    dr.v[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (int64_t)step * kDxBC);
+    drv[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (int64_t)step * kDxBC);
   };
-  // quarter q of one step's staging: dy chunk q, and the weight words
-  // assigned to that quarter (one word = 8 codes = one 16-byte chunk)
+  // quarter q of one step's staging: the dy chunk(s) of that quarter, and
+  // the weight words assigned to it (one word = 8 codes = one 16-byte chunk)
   auto store_quarter = [&](int buf, int qq) {
-    const int id = t + kThreads * qq;
-    *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) = dr.v[qq];
+    if (XC == 4 || (qq & 1) == 0) {
+      const int ci = XC == 4 ? qq : qq >> 1;
+      const int id = t + NT * ci;
+      *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) = drv[ci];
+    }
     constexpr int every = 4 / NU;
     if (qq % every == 0) {
       const int u = qq / every;
@@ -747,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   };
 
   const int wave = t >> 6, lane = t & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int lr = lane & 31, lk = lane >> 5;
   // transposing-read address of this lane within a 16-lane group:
   // row offset e = (lane & 15) / 4, column piece 4 * (lane & 3); groups
@@ -762,54 +782,54 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     const u32x2 hi = lds_read_tr16(wb + wswz<BX>(n + 4, col >> 3) + off);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  f32x16 acc[4][NJ];
-  zero_acc(&acc[0][0], 4 * NJ);
+  f32x16 acc[MI][NJ];
+  zero_acc(&acc[0][0], MI * NJ);
 
   __syncthreads();  // lut
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dy_chunk(ks0, i);
+  for (int i = 0; i < XC; ++i) load_dy_chunk(ks0, i);
   load_w(ks0);
   // first 16-rank chunk of the bypass operands (g, which already holds s,
   // and A^T), used after the main loop by the first contraction slice;
   // staged here so that its loads overlap the first tile loads
   if (split == 0) {
-    stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, 0, 1.0f, t);
-    stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, 0, t);
+    stage_lora<BM, NT>(ls_g, g, m0, M, r, 0, 1.0f, t);
+    stage_lora_t<BX, NT>(ls_a, A, K, k0, r, 0, t);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dy_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
+  for (int i = 0; i < XC; ++i) load_dy_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
   load_w(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
   __syncthreads();
   if constexpr (DROP) {
     // LoRA bypass under dropout, first slice only, before the main loop so
     // that it needs no registers beyond the accumulator: acc = A^T g^T over
     // all ranks, then each output (m, k) is kept times 1/(1-p) or zeroed.
-    // acc[i][j][v] is output row m0 + 128 wm + 32 i + lr, column
+    // acc[i][j][v] is output row m0 + TM wm + 32 i + lr, column
     // k0 + TX wn + 32 j + 4 lk + 8 (v / 4) + v % 4; columns k .. k + 3
     // (k % 4 == 0, and K % 4 == 0) share one Philox draw.
     if (split == 0) {
       for (int j0 = 0; j0 < r; j0 += 16) {
         if (j0 > 0) {
           __syncthreads();
-          stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
-          stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, j0, t);
+          stage_lora<BM, NT>(ls_g, g, m0, M, r, j0, 1.0f, t);
+          stage_lora_t<BX, NT>(ls_a, A, K, k0, r, j0, t);
           __syncthreads();
         }
-        u32x4 ga[4], ab[NJ];
+        u32x4 ga[MI], ab[NJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ga[i] = lora_frag(ls_g, 128 * wm + 32 * i + lr, lk);
+        for (int i = 0; i < MI; ++i) ga[i] = lora_frag(ls_g, TM * wm + 32 * i + lr, lk);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) ab[j] = lora_frag(ls_a, TX * wn + 32 * j + lr, lk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t m = (uint64_t)(m0 + 128 * wm + 32 * i + lr);
+      for (int i = 0; i < MI; ++i) {
+        const uint64_t m = (uint64_t)(m0 + TM * wm + 32 * i + lr);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -828,10 +848,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
     const int pf = k + 2 < ks1 ? k + 2 : ks1 - 1;
     const uint8_t *db = ds[cur];
     const uint8_t *wb = wt[cur];
-    u32x4 a[2][4], b[2][NJ];
+    u32x4 a[2][MI], b[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[0][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, lk));
+    for (int i = 0; i < MI; ++i)
+      a[0][i] = *reinterpret_cast<const u32x4 *>(db + swz(TM * wm + 32 * i + lr, lk));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b[0][j] = read_b(wb, 0, j);
 #pragma unroll
@@ -840,16 +860,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
       if (kk < 3) {
         const int chunk = 2 * (kk + 1) + lk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[nb][i] = *reinterpret_cast<const u32x4 *>(db + swz(128 * wm + 32 * i + lr, chunk));
+        for (int i = 0; i < MI; ++i)
+          a[nb][i] = *reinterpret_cast<const u32x4 *>(db + swz(TM * wm + 32 * i + lr, chunk));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) b[nb][j] = read_b(wb, kk + 1, j);
       }
+      // each dy chunk is reloaded right after it was stored
       store_quarter(cur ^ 1, kk);
-      load_dy_chunk(pf, kk);
+      if (XC == 4) load_dy_chunk(pf, kk);
+      else if ((kk & 1) == 0) load_dy_chunk(pf, kk >> 1);
       if (kk == 3) load_w(pf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(b[cb][j], a[cb][i], acc[i][j]);
     }
@@ -861,27 +883,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint16_t *__restrict
   for (int j0 = 0; j0 < (split == 0 && !DROP ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora<kBM, kThreads>(ls_g, g, m0, M, r, j0, 1.0f, t);
-      stage_lora_t<BX, kThreads>(ls_a, A, K, k0, r, j0, t);
+      stage_lora<BM, NT>(ls_g, g, m0, M, r, j0, 1.0f, t);
+      stage_lora_t<BX, NT>(ls_a, A, K, k0, r, j0, t);
       __syncthreads();
     }
-    u32x4 ga[4], ab[NJ];
+    u32x4 ga[MI], ab[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ga[i] = lora_frag(ls_g, 128 * wm + 32 * i + lr, lk);
+    for (int i = 0; i < MI; ++i) ga[i] = lora_frag(ls_g, TM * wm + 32 * i + lr, lk);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) ab[j] = lora_frag(ls_a, TX * wn + 32 * j + lr, lk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
   }
   // K % 128 == 0 here, so every tile is full in the column direction
   if (nsplit > 1)
-    store_tile_f32<4, NJ>(part + (int64_t)split * M * K, K, M, K, m0 + 128 * wm, k0 + TX * wn, acc,
-                       lane);
-  else
-    store_tile_lds<4, NJ>(dx, K, M, m0 + 128 * wm, k0 + TX * wn, acc,
-                       &ds[0][0] + wave * 32 * (2 * TX + 16), lane);
+    store_tile_f32<MI, NJ>(part + (int64_t)split * M * K, K, M, K, m0 + TM * wm, k0 + TX * wn,
+                           acc, lane);
+  else  // per-wave slices of 32 rows in a dead staging buffer
+    store_tile_lds<MI, NJ>(dx, K, M, m0 + TM * wm, k0 + TX * wn, acc,
+                           (BM == 256 ? &ds[0][0] : &wt[0][0]) + wave * 32 * (2 * TX + 16), lane);
 }
 
 // Output tile width: 256 when that still gives at least ~1.5 workgroups per
@@ -935,7 +957,12 @@ static int fwd_split(int64_t M, int64_t N, int64_t K) {
   return split_count(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn), K >> 6, M, N);
 }
 
+// Input-gradient tile: 64 tokens x 128 columns up to kDxSmallM tokens, else
+// 256 tokens x pick_width columns.
+constexpr int64_t kDxSmallM = 128;
+
 static int dx_split(int64_t M, int64_t N, int64_t K) {
+  if (M <= kDxSmallM) return split_count(((M + 63) / 64) * (K / 128), N / kDxBC, M, K, 512);
   const int bx = pick_width(M, K, K % 256 == 0);
   return split_count(((M + kBM - 1) / kBM) * (K / bx), N / kDxBC, M, K);
 }
@@ -1010,25 +1037,26 @@ int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockSc
                    uint16_t *dx, hipStream_t stream, float *part, const Dropout *drop,
                    float drop_scale) {
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
-  const int bx = pick_width(M, K, K % 256 == 0);
-  const int64_t G = ((M + kBM - 1) / kBM) * (K / bx);
+  const bool small = M <= kDxSmallM;
+  const int bm = small ? 64 : kBM;
+  const int bx = small ? 128 : pick_width(M, K, K % 256 == 0);
+  const int64_t G = ((M + bm - 1) / bm) * (K / bx);
   const int S = part ? dx_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
-#define QL_DX(BXV, LT, DQV, DRV)                                                                 \
-  hipLaunchKernelGGL((k_gemm_dx<BXV, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),            \
-                     dim3(kThreads), 0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, r, dx, \
-                     part, S, dr, drop_scale)
-#define QL_DX_DR(BXV, LT, DQV) \
-  do { if (drop) QL_DX(BXV, LT, DQV, true); else QL_DX(BXV, LT, DQV, false); } while (0)
-#define QL_DX_DQ(BXV, LT) \
-  do { if (dq) QL_DX_DR(BXV, LT, true); else QL_DX_DR(BXV, LT, false); } while (0)
-  if (bx == 256) {
-    if (lora_dtype == QL_BF16) QL_DX_DQ(256, uint16_t);
-    else QL_DX_DQ(256, float);
-  } else {
-    if (lora_dtype == QL_BF16) QL_DX_DQ(128, uint16_t);
-    else QL_DX_DQ(128, float);
-  }
+#define QL_DX(BMV, BXV, LT, DQV, DRV)                                                            \
+  hipLaunchKernelGGL((k_gemm_dx<BMV, BXV, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),       \
+                     dim3(DxShape<BMV>::NT), 0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, \
+                     r, dx, part, S, dr, drop_scale)
+#define QL_DX_DR(BMV, BXV, LT, DQV) \
+  do { if (drop) QL_DX(BMV, BXV, LT, DQV, true); else QL_DX(BMV, BXV, LT, DQV, false); } while (0)
+#define QL_DX_DQ(BMV, BXV, LT) \
+  do { if (dq) QL_DX_DR(BMV, BXV, LT, true); else QL_DX_DR(BMV, BXV, LT, false); } while (0)
+#define QL_DX_LT(BMV, BXV) \
+  do { if (lora_dtype == QL_BF16) QL_DX_DQ(BMV, BXV, uint16_t); else QL_DX_DQ(BMV, BXV, float); } while (0)
+  if (small) QL_DX_LT(64, 128);
+  else if (bx == 256) QL_DX_LT(256, 256);
+  else QL_DX_LT(256, 128);
+#undef QL_DX_LT
 #undef QL_DX_DQ
 #undef QL_DX_DR
 #undef QL_DX
