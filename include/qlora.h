@@ -9,10 +9,10 @@
  * (26. QLoRA and 4bit Quantization, datawhalechina, Step 3; same formula in
  * 22. QLoRA and 4bit Quantization, Step 4).  W is stored as 4-bit indices into
  * a fixed 16-entry NF4 codebook (26. ..., Step 4 lookup table), one fp32
- * absmax per block of 64 consecutive elements of the row-major flattened
- * weight (Gemma lesson 09, sec. 9.2.1: each block is normalised to [-1, 1];
- * 22. ..., engineering notes: 64 parameters share one scale), two indices per
- * byte (22. ..., Step 4).  Optionally the block constants are quantised again
+ * absmax per block of 64 (or 128) consecutive elements of the row-major
+ * flattened weight (Gemma lesson 09, sec. 9.2.1: each block is normalised to
+ * [-1, 1]; 22. ..., engineering notes: 64 or 128 parameters share one scale),
+ * two indices per byte (22. ..., Step 4).  Optionally the block constants are quantised again
  * to 8-bit integers (Gemma lesson 09, sec. 9.2.2 "double quantization";
  * gufacode ch. 4: ~4.5 -> ~4.127 bits per parameter).
  *

@@ -1,8 +1,8 @@
 // common.h -- shared definitions of the gfx950 kernels of the QLoRA layer.
 //
 // Storage format (see include/qlora.h): row-major flattened weight, blocks
-// of 64 elements with one constant each, two 4-bit codebook indices per byte
-// (element 2j in the high nibble).
+// of 64 (or 128) elements with one constant each, two 4-bit codebook indices
+// per byte (element 2j in the high nibble).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -13,7 +13,8 @@
 // bf16 for those steps).
 //
 // Tiles: 256 tokens x BN outputs per workgroup (BN = 256 or 128), contraction
-// step 64 (= one NF4 block of every weight row in the forward), 8 waves laid
+// step 64 (= one 64-element chunk of every weight row in the forward: one
+// NF4 block, or half of one with blocks of 128), 8 waves laid
 // out 2 (tokens) x 4 (outputs), each owning a 128 x BN/4 block of 32x32
 // accumulator tiles.  LDS is double-buffered: while the matrix cores work on
 // step k, the registers loaded during step k-1 (step k+1's tiles) are written

@@ -13,10 +13,11 @@
 // double-quantised form q * sigma + mu) are resolved once into an LDS table.
 //
 // The 16x16x32 bf16 matrix-core op multiplies the activations by the
-// *unscaled* codebook values of one NF4 block (16 rows x 32 columns per op,
-// two ops per block); the block's fp32 constant is then applied to the 4
-// partial sums each lane holds (26. ..., Step 4: table[index] * scale, with
-// the scale taken out of the 64-term sum it multiplies).  The codebook lookup
+// *unscaled* codebook values of one 64-element chunk (16 rows x 32 columns
+// per op, two ops per chunk; a chunk lies inside one NF4 block of 64 or 128);
+// the block's fp32 constant is then applied to the 4 partial sums each lane
+// holds (26. ..., Step 4: table[index] * scale, with the scale taken out of
+// the 64-term sum it multiplies).  The codebook lookup
 // goes through a byte -> bf16x2 table in LDS built from immediates.
 //
 // The rank-r pre-product u = x A^T is recomputed by every workgroup from the

@@ -6,8 +6,9 @@
 //
 // W^ is dequantised on the fly (26. ..., Step 4: table[index] * scale) into
 // fp32 tiles in LDS; it is never written to global memory.  Tiles are 64x64
-// with a contraction step of 64, which for the forward is exactly one NF4
-// block of each weight row.
+// with a contraction step of 64, which for the forward is exactly one
+// 64-element chunk of each weight row (one NF4 block, or half of one with
+// blocks of 128).
 #include "kernels.h"
 
 namespace qlora {
@@ -91,7 +92,8 @@ __global__ __launch_bounds__(256) void k_simple_fwd(const void *__restrict__ x, 
 }
 
 // Input gradient.  Contraction over n in steps of 64; the weight tile holds
-// rows n0..n0+64 of W^ restricted to columns k0..k0+64 (one NF4 block each).
+// rows n0..n0+64 of W^ restricted to columns k0..k0+64 (one 64-element
+// chunk of each row, inside one NF4 block).
 template <typename AT, typename LT>
 __global__ __launch_bounds__(256) void k_simple_dx(const void *__restrict__ dy, int64_t M,
                                                    const uint8_t *__restrict__ packed,
