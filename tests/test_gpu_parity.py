@@ -218,6 +218,8 @@ BF16_CASES = [
     (77, 1024, 2048, 16, True, torch.bfloat16), # fwd 4 slices, dx 2 slices
     (200, 512, 4096, 8, True, torch.bfloat16),  # fwd 8 slices
     (130, 4096, 512, 16, True, torch.bfloat16), # dx 8 slices
+    (7, 64, 512, 16, True, torch.bfloat16),     # GEMV: a round of 8 blocks
+    (1, 200, 2048, 5, False, torch.bfloat16),   # GEMV: ragged N, rank 5, fp32 absmax
     # 64-token forward tiles (17..128 tokens)
     (100, 200, 320, 8, False, torch.float32),   # ragged M and N, fp32 absmax and factors
     (48, 256, 512, 128, True, torch.bfloat16),  # r = 128 (8 rank chunks), split
