@@ -172,6 +172,36 @@ void orc_round_bf16(const float *in, int64_t n, uint16_t *out) {
   }
 }
 
+/* fp32 -> IEEE 754 binary16 bit pattern, round to nearest, ties to even,
+ * from the format's definition: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits.  A finite x with |x| in [2^e, 2^(e+1)), e >= -14, is
+ * m 2^(e-10) with m = rint(|x| 2^(10-e)) in [1024, 2048] (m = 2048 carries
+ * into the next binade); |x| < 2^-14 is the subnormal m 2^-24 with
+ * m = rint(|x| 2^24) (m = 1024 is the smallest normal, whose bit pattern is
+ * the same integer).  Exponents past 15 are infinity (|x| >= 65520).  Every
+ * scaling is by a power of two, exact in double; rint rounds half to even
+ * in the default rounding mode.  (finite inputs; NaN is out of scope) */
+static uint16_t orc_f16_bits(float x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  const double a = fabs((double)x);
+  if (a < ldexp(1.0, -14)) return sign | (uint16_t)rint(ldexp(a, 24));
+  int e;
+  frexp(a, &e);  /* a = f 2^e, f in [0.5, 1): the binade exponent is e - 1 */
+  e -= 1;
+  double m = rint(ldexp(a, 10 - e));
+  if (m == 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  if (e > 15) return sign | 0x7C00u;
+  return sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)m - 1024);
+}
+
+void orc_round_f16(const float *in, int64_t n, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_bits(in[i]);
+}
+
 /* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
  * Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11), written from
  * its definition there: a 4-word counter and a 2-word key; one round maps

@@ -14,7 +14,8 @@ section:
          (agentupdate.ai), sections 9.2.1 and 9.2.2.
   [gc4]  gufacode fine-tuning chapter 4, "three core techniques of QLoRA".
 
-bfloat16 tensors travel as numpy uint16 bit patterns.
+bfloat16 tensors travel as numpy uint16 bit patterns, fp16 tensors as numpy
+float16.
 
 Parity pins live in tests/test_oracle_pins.py.  Double-quantisation bit
 patterns and large-shape GEMM values have no printed value to compare with:
@@ -55,6 +56,7 @@ def _load():
     lib.orc_dq_codes.argtypes = [_p, _i64, _f32, _i32, _p, _p]
     lib.orc_nf4_dequantize.argtypes = [_p, _i64, _i32, _p, _p, _p, _f32, _i32, _p]
     lib.orc_round_bf16.argtypes = [_p, _i64, _p]
+    lib.orc_round_f16.argtypes = [_p, _i64, _p]
     lib.orc_linear_fwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p, _p]
     lib.orc_linear_bwd.argtypes = [_i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p, _p, _p,
                                    _p, _i64, _p, _p, _p, _p, _p]
@@ -94,8 +96,19 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> IEEE binary16 (numpy float16 values), round to nearest even;
+    the rounding is the oracle's own, in C, written from the format's
+    definition (Gemma lesson 09, sec. 9.3 names fp16 as a compute dtype)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_round_f16(_ptr(x), x.size, _ptr(out))
+    return out.view(np.float16)
+
+
 def as_f32(w: np.ndarray) -> np.ndarray:
-    """Weights/activations given as fp32 or as bf16 bit patterns (uint16)."""
+    """Weights/activations given as fp32, fp16 (numpy float16; widening is
+    exact) or as bf16 bit patterns (uint16)."""
     if w.dtype == np.uint16:
         return bf16_to_f32(w)
     return np.ascontiguousarray(w, dtype=np.float32)

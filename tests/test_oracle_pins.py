@@ -345,6 +345,65 @@ def test_round_bf16_is_rne(orc):
         assert frac(g) == _rn_bf16_exact(frac(v)), v
 
 
+def test_round_f16_hand_values(orc):
+    """fp16 rounding (Gemma lesson 09, sec. 9.3 names fp16 as the other
+    16-bit compute dtype): bit patterns worked out by hand from the binary16
+    format (bias 15, 10 fraction bits, subnormal step 2^-24)."""
+    cases = [
+        (1.0, 0x3C00), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+        (1.0 + 2.0 ** -11, 0x3C00),                 # tie between 1 and 1 + 2^-10: even
+        (1.0 + 3 * 2.0 ** -11, 0x3C02),             # tie: up to the even 1 + 2^-9
+        (1.0 + 2.0 ** -11 + 2.0 ** -20, 0x3C01),    # just past the tie
+        (0.1, 0x2E66),                              # rint(0.1 * 2^14) = 1638 -> fraction 614
+        (0.161, 0x3127),                            # rint(0.161 * 2^13) = 1319 -> fraction 295
+        (65504.0, 0x7BFF),                          # largest finite
+        (65519.99609375, 0x7BFF),                   # below the overflow tie
+        (65520.0, 0x7C00),                          # tie with 2^16: to infinity
+        (-1.0e6, 0xFC00),
+        (2.0 ** -14, 0x0400),                       # smallest normal
+        (2.0 ** -14 - 2.0 ** -25, 0x0400),          # subnormal tie 1023.5: up to the even 1024
+        (2.0 ** -24, 0x0001),                       # smallest subnormal
+        (2.0 ** -25, 0x0000),                       # tie with 0: even
+        (1.5 * 2.0 ** -24, 0x0002),                 # tie 1.5: even 2
+        (3.0e-39, 0x0000),                          # fp32 subnormal
+    ]
+    vals = np.float32([v for v, _ in cases])
+    got = orc.round_f16(vals).view(np.uint16)
+    for (v, want), g in zip(cases, got):
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+
+
+def _rn_f16_exact(v: Fraction) -> float:
+    """Exact round-to-nearest-even of v to binary16: binade exponent e >= -14
+    (the subnormals share the quantum 2^-24 of the lowest binade), 11
+    significant bits; results past 65504 overflow to infinity."""
+    a = abs(v)
+    e = -14
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    r = round_half_even(a * Fraction(2) ** (10 - e)) * Fraction(2) ** (e - 10)
+    out = math.inf if r > 65504 else float(r)
+    return -out if v < 0 else out
+
+
+def test_round_f16_matches_exact_rounding(orc):
+    """Against exact rational rounding on a sweep over every binade of fp16
+    (subnormals to overflow), the midpoints between neighbouring fp16 values
+    and the fp32 values next to those midpoints."""
+    rng = np.random.default_rng(17)
+    mags = np.ldexp(rng.uniform(1, 2, 3000), rng.integers(-27, 17, 3000)).astype(np.float32)
+    h = rng.integers(0, 0x7BFF, 500).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = ((lo + hi) / 2).astype(np.float32)  # exact: 12 significant bits
+    vals = np.concatenate([mags, -mags[:500], mids, -mids[:100],
+                           np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))])
+    got = orc.round_f16(vals).astype(np.float64)
+    for v, g in zip(vals, got):
+        want = _rn_f16_exact(frac(v))
+        assert g == want and math.copysign(1, g) == math.copysign(1, want), (v, g, want)
+
+
 # --------------------------------------------------------------------------
 # The layer: 26. ... Step 3 (forward), Step 4 tests; 22. ... Step 1 (grads)
 # --------------------------------------------------------------------------
