@@ -13,6 +13,7 @@ In the same run (reported beside the step):
   dropout      the gate projection with LoRA dropout 0.05 against without
   formats      the gate projection in each storage variant (blocks of 64 or
                128, with or without double quantisation)
+  compute_dtype  the training step with bf16 and with fp16 compute
   decode_gemv  Llama-3-8B attention projection (4096x4096) at M = 1, 4, 16,
                packed-weight GB/s, rotating over 64 weight copies so the
                256 MB Infinity Cache cannot hold them
@@ -39,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s (%MFMA peak); decode GEMV packed-weight GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ROOFLINE_KERNEL = "k_gemm_fwd<256, unsigned short, true>"
+ROOFLINE_KERNEL = "k_gemm_fwd<256, unsigned short, unsigned short, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_fwd_mlp8b_gate.json")
 
 
@@ -256,6 +257,7 @@ def main():
         result["few_tokens"] = bench_few_tokens(q, si, dev)
         result["dropout"] = bench_dropout(q, si, dev)
         result["formats"] = bench_formats(q, si, dev)
+        result["compute_dtype"] = bench_compute_dtype(q, si, dev)
         result["decode_gemv"] = bench_decode(q, si, dev)
         result["quantize"] = bench_quantize(q, si, dev)
         result["optimizer"] = bench_adamw(q, si, dev)
@@ -383,6 +385,57 @@ def bench_formats(q, si, dev):
         log(f"format {key}: {out[key]}")
     del Ws
     del t, y, u, dx, dA, dB, wsf, wsb, wsq
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_compute_dtype(q, si, dev, rounds=3, iters=10):
+    """The 8B-MLP training step (gate, up, down; 2048 tokens, r=16) with bf16
+    and with fp16 compute (activations, dequantised weight and LoRA factors
+    in the dtype, fp32 accumulation).  The two are timed alternately,
+    `rounds` times `iters` steps each; the median per dtype is reported."""
+    c = si.MLP_8B
+    M, r, alpha = c["M"], c["r"], c["alpha"]
+    steps, fl = {}, 0
+    for dt in (torch.bfloat16, torch.float16):
+        projs = []
+        for pi, (name, (N, K)) in enumerate(c["projs"].items()):
+            t = si.linear_inputs(c["config"], M, N, K, r, act_dtype=dt, w_dtype=dt, lora_dtype=dt,
+                                 sub=pi, device=dev)
+            W = q.nf4_quantize(t["W"], double_quant=True)
+            del t["W"]
+            projs.append(dict(t, W=W, y=torch.empty((M, N), dtype=dt, device=dev),
+                              u=torch.empty((M, r), dtype=torch.float32, device=dev),
+                              dx=torch.empty((M, K), dtype=dt, device=dev),
+                              dA=torch.empty((r, K), dtype=torch.float32, device=dev),
+                              dB=torch.empty((N, r), dtype=torch.float32, device=dev),
+                              wsf=q.workspace(q.QL_OP_FWD, M, N, K, r, dev),
+                              wsb=q.workspace(q.QL_OP_BWD, M, N, K, r, dev)))
+            if dt == torch.bfloat16:
+                fl += layer_flops(M, N, K, r)
+
+        def step(projs=projs):
+            for p in projs:
+                q.qlora_linear_fwd(p["x"], p["W"], p["A"], p["B"], alpha, y=p["y"],
+                                   u_save=p["u"], ws=p["wsf"])
+                q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha,
+                                   u_saved=p["u"], dx=p["dx"], dA=p["dA"], dB=p["dB"],
+                                   ws=p["wsb"])
+        steps[dt] = step
+    times = {dt: [] for dt in steps}
+    for dt, fn in steps.items():
+        timed(fn, 3, 2)
+    for _ in range(rounds):
+        for dt, fn in steps.items():
+            times[dt].append(timed(fn, iters, 1))
+    out = {"workload": "8B-MLP training step (gate, up, down fwd + bwd), 2048 tokens, r=16, "
+                       "NF4 + double quant", "unit": "ms"}
+    for dt, ts in times.items():
+        ms = sorted(ts)[len(ts) // 2]
+        key = "bf16" if dt == torch.bfloat16 else "fp16"
+        out[key] = {"ms_per_step": round(ms, 3), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1)}
+        log(f"compute dtype {key}: {out[key]}")
+    del steps
     torch.cuda.empty_cache()
     return out
 

@@ -50,9 +50,15 @@ extern "C" {
 #define QL_EWORKSPACE 5   /* workspace smaller than ql_workspace_bytes() */
 #define QL_EHIP 6         /* the HIP runtime reported an error */
 
-/* Element types of activations, weights to quantise, LoRA factors, outputs. */
+/* Element types of activations, weights to quantise, LoRA factors, outputs.
+ * The compute dtype of the layer is its activation dtype (Gemma lesson 09,
+ * sec. 9.3: the dequantised weight takes the compute dtype, bf16
+ * recommended, fp16 where bf16 is unsupported or misbehaves, fp32 possible
+ * but costly).  A 16-bit LoRA dtype must equal a 16-bit activation dtype
+ * (with fp32 activations it may be QL_BF16). */
 #define QL_F32 0
 #define QL_BF16 1
+#define QL_F16 2 /* IEEE binary16 */
 
 /* Workspace queries (ql_workspace_bytes `op`). */
 #define QL_OP_QUANTIZE 0
@@ -128,7 +134,8 @@ size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
 /*
  * NF4-quantise a weight (Gemma lesson 09, sec. 9.2.1 and 9.2.2; 26. ...,
  * Step 2 nearest codepoint).
- *   w         device, q->rows * q->cols elements of w_dtype (QL_F32/QL_BF16),
+ *   w         device, q->rows * q->cols elements of w_dtype (QL_F32, QL_BF16 or
+ *             QL_F16),
  *             16-byte aligned.
  *   q         host struct describing device outputs: packed and either absmax
  *             (double_quant 0) or absmax_q, absmax_scale, absmax_mean (1).
@@ -148,7 +155,8 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
 
 /*
  * Dequantise a whole NF4 weight to out (device, rows * cols elements of
- * out_dtype; bf16 is the round-to-nearest-even of the fp32 product)
+ * out_dtype: fp32, or bf16 / fp16 as the round-to-nearest-even of the fp32
+ * product)
  * (26. ..., Step 4: table[index] * scale; 22. ..., Step 3: restored to a
  * 16-bit float for the matrix product).  out must be 16-byte aligned.
  * Errors: QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
@@ -159,14 +167,17 @@ int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream);
  * Forward of the layer (26. ..., Step 3):
  *     u = x A^T,   y = x W^^T + s u B^T,   s = fp32(alpha / r)
  * with W^ dequantised on the fly, never stored.
- *   x       device [M, K] act_dtype (QL_BF16, or QL_F32 for the fp32 path)
+ *   x       device [M, K] act_dtype (QL_BF16 or QL_F16, or QL_F32 for the fp32
+ *           path)
  *   W       host struct, rows = N, cols = K, K % W->block == 0
- *   A, B    device [r, K] and [N, r] of lora_dtype (QL_BF16 or QL_F32)
+ *   A, B    device [r, K] and [N, r] of lora_dtype (QL_F32, or the 16-bit
+ *           activation dtype; QL_BF16 with fp32 activations)
  *   r       1..128;  alpha any finite value
  *   y       device [M, N] act_dtype (overwritten)
  *   u_save  device [M, r] fp32 receiving u, or NULL
  *   ws      device workspace of ql_workspace_bytes(QL_OP_FWD, M, N, K, r)
- * bf16 activations multiply in bf16 on the matrix cores with fp32
+ * 16-bit activations multiply on the matrix cores in their own format (W^
+ * dequantised to it, the rank-r operands rounded to it) with fp32
  * accumulation; fp32 activations compute entirely in fp32.
  * All device pointers 16-byte aligned.
  */
@@ -180,11 +191,11 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
  * qlora_linear_fwd on the same x when a forward is recomputed):
  *     y = x W^^T + s u B^T,   s = fp32(alpha / r)
  *   u       device [M, r] fp32, 16-byte aligned
- * Other arguments as for qlora_linear_fwd; no workspace.  With bf16
+ * Other arguments as for qlora_linear_fwd; no workspace.  With 16-bit
  * activations this is a single matrix-core launch, bit-identical to the
  * y of qlora_linear_fwd for M > 16 (for M <= 16 qlora_linear_fwd takes the
- * single-launch decode path, which rounds u to bf16 in registers instead of
- * reading it, so the two agree to within bf16 rounding).
+ * single-launch decode path, which rounds u to 16 bits in registers instead
+ * of reading it, so the two agree to within 16-bit rounding).
  * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
  */
 int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
@@ -238,7 +249,7 @@ int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64
  * Forward with LoRA dropout:  u = xd A^T,  y = x W^^T + s u B^T.
  * Arguments as for qlora_linear_fwd (same workspace size).  u_save receives
  * the u of the dropped input, which is what qlora_linear_bwd_dropout's
- * u_saved expects.  dropout_p > 0 requires bf16 activations (QL_EUNSUPPORTED
+ * u_saved expects.  dropout_p > 0 requires 16-bit activations (QL_EUNSUPPORTED
  * otherwise) and always takes the matrix-core GEMM, also for M <= 16.
  * Errors: as qlora_linear_fwd; QL_EINVAL for dropout_p outside [0, 1).
  */
@@ -253,7 +264,7 @@ int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const 
  *     dA = g^T xd,  dx = dy W^ + d .* (g A).
  * accumulate 0 overwrites dA and dB, 1 adds into them (as
  * qlora_linear_bwd_acc).  Workspace as qlora_linear_bwd.  dropout_p > 0
- * requires bf16 activations and, when dx is wanted, N % 64 == 0 and
+ * requires 16-bit activations and, when dx is wanted, N % 64 == 0 and
  * K % 128 == 0 (QL_EUNSUPPORTED otherwise).
  * Errors: as qlora_linear_bwd; QL_EINVAL for dropout_p outside [0, 1) or
  * accumulate not 0/1.

@@ -1,9 +1,10 @@
 """MI355X (gfx950) QLoRA quantized linear layer.
 
-NF4 block-64 quantisation with 8-bit double quantisation of the block
-constants, and the layer y = x W^T + (alpha/r) (x A^T) B^T with its backward
-(dx, dA, dB), all in hand-written HIP kernels behind the C ABI of
-include/qlora.h.  This package is the thin Python binding.
+NF4 quantisation (blocks of 64 or 128) with 8-bit double quantisation of the
+block constants, and the layer y = x W^T + (alpha/r) (x A^T) B^T with its
+backward (dx, dA, dB) in bf16, fp16 or fp32 compute, all in hand-written HIP
+kernels behind the C ABI of include/qlora.h.  This package is the thin
+Python binding.
 """
 from .binding import (DQ_BLOCK, NF4_BLOCK, QL_OP_BWD, QL_OP_FWD, QL_OP_QUANTIZE, NF4Weight,
                       QLoRAArgumentError, QLoRAError, adamw_step, dropout_mask, lib,

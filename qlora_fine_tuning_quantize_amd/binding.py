@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlora.so")
 
 QL_OK, QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP = range(7)
-QL_F32, QL_BF16 = 0, 1
+QL_F32, QL_BF16, QL_F16 = 0, 1, 2
 QL_OP_QUANTIZE, QL_OP_FWD, QL_OP_BWD = 0, 1, 2
 NF4_BLOCK, NF4_BLOCK_LARGE, DQ_BLOCK = 64, 128, 256
 
@@ -109,6 +109,8 @@ def _check(status: int, what: str):
 def _dtype_code(t: torch.dtype) -> int:
     if t == torch.bfloat16:
         return QL_BF16
+    if t == torch.float16:
+        return QL_F16
     if t == torch.float32:
         return QL_F32
     raise ValueError(f"unsupported dtype {t}")

@@ -16,7 +16,9 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int check_dtype(int32_t d) { return (d == QL_F32 || d == QL_BF16) ? QL_OK : QL_EINVAL; }
+int check_dtype(int32_t d) {
+  return (d == QL_F32 || d == QL_BF16 || d == QL_F16) ? QL_OK : QL_EINVAL;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -105,6 +107,9 @@ int check_linear_common(int32_t act_dtype, int64_t M, const ql_nf4 *W, const voi
   int st = check_nf4(W);
   if (st) return st;
   if (check_dtype(act_dtype) || check_dtype(lora_dtype)) return QL_EINVAL;
+  // 16-bit activations: the LoRA factors are fp32 or of the same format
+  if (act_dtype != QL_F32 && lora_dtype != QL_F32 && lora_dtype != act_dtype)
+    return QL_EUNSUPPORTED;
   if (M <= 0 || r <= 0) return QL_EINVAL;
   if (r > 128) return QL_EUNSUPPORTED;
   if (W->cols % W->block != 0) return QL_ESHAPE;  // blocks never straddle weight rows
@@ -130,7 +135,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 104; }
+int ql_abi_version(void) { return 105; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -212,7 +217,7 @@ int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) 
                                (hipStream_t)stream);
 }
 
-// drop: LoRA dropout of the bypass input (bf16 activations only), with
+// drop: LoRA dropout of the bypass input (16-bit activations only), with
 // dscale = 1 / (1 - p); NULL for none.
 static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
                       const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
@@ -220,7 +225,7 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
                       size_t ws_bytes, void *stream) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
-  if (drop && act_dtype != QL_BF16) return QL_EUNSUPPORTED;
+  if (drop && act_dtype == QL_F32) return QL_EUNSUPPORTED;
   if (!x || !y) return QL_EINVAL;
   if (!aligned16(x) || !aligned16(y) || (u_save && !aligned16(u_save))) return QL_EALIGN;
   const int64_t N = W->rows, K = W->cols;
@@ -233,15 +238,15 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype == QL_BF16 && M <= 16 && !drop)  // decode: one launch computes u and y
-    return launch_gemv_fwd((const uint16_t *)x, M, W->packed, sc, N, K, A, B, lora_dtype, r,
-                           sc_lora, (uint16_t *)y, u_save, s);
+  if (act_dtype != QL_F32 && M <= 16 && !drop)  // decode: one launch computes u and y
+    return launch_gemv_fwd(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y,
+                           u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
                            rows_partial, s, nullptr, drop);
   if (st) return st;
-  if (act_dtype == QL_BF16)
-    return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
-                           sc_lora, (uint16_t *)y, s, rows_partial);
+  if (act_dtype != QL_F32)
+    return launch_gemm_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
+                           s, rows_partial);
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
 }
@@ -277,9 +282,9 @@ int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype == QL_BF16)
-    return launch_gemm_fwd((const uint16_t *)x, M, W->packed, sc, N, K, u, B, lora_dtype, r,
-                           sc_lora, (uint16_t *)y, s, nullptr);
+  if (act_dtype != QL_F32)
+    return launch_gemm_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
+                           s, nullptr);
   return launch_simple_fwd(x, act_dtype, M, W->packed, sc, N, K, u, B, lora_dtype, r, sc_lora, y,
                            s);
 }
@@ -291,7 +296,7 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
                       const Dropout *drop = nullptr, float dscale = 1.0f) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
-  if (drop && (act_dtype != QL_BF16 || (dx && !gemm_dx_supported(W->rows, W->cols))))
+  if (drop && (act_dtype == QL_F32 || (dx && !gemm_dx_supported(W->rows, W->cols))))
     return QL_EUNSUPPORTED;
   if (!dy || !x || !dA || !dB) return QL_EINVAL;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(dA) || !aligned16(dB) ||
@@ -327,9 +332,9 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
                         accumulate, drop);
   if (st) return st;
   if (!dx) return QL_OK;
-  if (act_dtype == QL_BF16 && gemm_dx_supported(N, K))
-    return launch_gemm_dx((const uint16_t *)dy, M, W->packed, sc, N, K, g, A, lora_dtype, r,
-                          (uint16_t *)dx, s, rows_partial, drop, dscale);
+  if (act_dtype != QL_F32 && gemm_dx_supported(N, K))
+    return launch_gemm_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s,
+                          rows_partial, drop, dscale);
   return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
 }
 

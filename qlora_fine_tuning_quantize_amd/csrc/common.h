@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/qlora.h"
 
 namespace qlora {
@@ -60,6 +62,66 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
   return __builtin_bit_cast(uint16_t, (__bf16)a);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The two 16-bit formats of activations, outputs and matrix-core operands,
+// named by their storage type: uint16_t holds bf16 bit patterns, _Float16
+// IEEE binary16.  Conversions from fp32 round to nearest even (fp16
+// overflows to infinity past its largest finite value, 65504).  The
+// matrix-core ops multiply two operands of the format with fp32
+// accumulation; operand layouts are the same for both formats.
+template <typename H>
+struct Half;
+
+template <>
+struct Half<uint16_t> {
+  __device__ static __forceinline__ uint16_t bits(float a) { return f32_to_bf16_bits(a); }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  // the value in the low / high half of a 32-bit word
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return __uint_as_float(w & 0xFFFF0000u);
+  }
+  __device__ static __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b,
+                                                  const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b,
+                                                 const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Half<_Float16> {
+  __device__ static __forceinline__ uint16_t bits(float a) {
+    return __builtin_bit_cast(uint16_t, (_Float16)a);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  __device__ static __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b,
+                                                  const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b,
+                                                 const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T *p, int64_t i);
 template <>
@@ -69,6 +131,10 @@ __device__ __forceinline__ float load_as_f32<float>(const float *p, int64_t i) {
 template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_t i) {
   return bf16_bits_to_f32(p[i]);
+}
+template <>
+__device__ __forceinline__ float load_as_f32<_Float16>(const _Float16 *p, int64_t i) {
+  return (float)p[i];
 }
 
 template <typename T>
@@ -81,6 +147,27 @@ template <>
 __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p, int64_t i, float v) {
   p[i] = f32_to_bf16_bits(v);
 }
+template <>
+__device__ __forceinline__ void store_from_f32<_Float16>(_Float16 *p, int64_t i, float v) {
+  p[i] = (_Float16)v;
+}
+
+// Host-side dispatch on a dtype: calls f with a null pointer of its storage
+// type.  with_half: QL_F16 -> _Float16 *, otherwise uint16_t * (bf16);
+// with_type: also QL_F32 -> float *.
+template <typename F>
+inline void with_half(int dtype, F &&f) {
+  if (dtype == QL_F16) f((_Float16 *)nullptr);
+  else f((uint16_t *)nullptr);
+}
+template <typename F>
+inline void with_type(int dtype, F &&f) {
+  if (dtype == QL_F32) f((float *)nullptr);
+  else with_half(dtype, f);
+}
+// the storage type named by such a pointer
+template <typename P>
+using elem_of = typename std::remove_pointer<P>::type;
 
 // The block constants of an NF4 weight: stored fp32 absmax, or rebuilt
 // from their 8-bit codes with one rounding.  Kernels address them by the
@@ -139,7 +226,7 @@ __device__ __forceinline__ uint32_t dropout_keep4(const Dropout &d, uint64_t e) 
          ((uint32_t)(w[2] >= d.thr) << 2) | ((uint32_t)(w[3] >= d.thr) << 3);
 }
 
-// 8 bf16 values (elements e .. e + 7 in order, e % 4 == 0) with the dropped
+// 8 16-bit values (elements e .. e + 7 in order, e % 4 == 0) with the dropped
 // ones set to zero
 __device__ __forceinline__ u32x4 dropout_mask8(const Dropout &d, uint64_t e, u32x4 v) {
   const uint32_t bits = dropout_keep4(d, e) | (dropout_keep4(d, e + 4) << 4);

@@ -1,5 +1,5 @@
-// gemm.hip -- matrix-core (bf16 MFMA, fp32 accumulate) products of the QLoRA
-// layer for many tokens:
+// gemm.hip -- matrix-core (16-bit MFMA, fp32 accumulate) products of the
+// QLoRA layer for many tokens:
 //
 //   forward:        y  = x W^^T + s u B^T   (26. QLoRA and 4bit Quantization, Step 3)
 //   input gradient: dx = dy W^  + g A       (22. QLoRA and 4bit Quantization, Step 1:
@@ -7,10 +7,12 @@
 //
 // W^ is never materialised: each workgroup dequantises the NF4 tile it needs
 // (26. ..., Step 4: table[index] * scale; 22. ..., Step 3: restored to a 16-bit
-// float for the product) straight into LDS as bf16 and feeds the matrix
-// cores from there.  The rank-r bypass is folded into the same accumulators
-// as extra 16-deep MFMA steps (u and g are fp32 in memory and are rounded to
-// bf16 for those steps).
+// float for the product) straight into LDS in the compute format and feeds
+// the matrix cores from there.  The compute format is the activations'
+// 16-bit format AT (bf16, or fp16: Gemma lesson 09, sec. 9.3, compute
+// dtype); every kernel is written once for both through Half<AT>.  The
+// rank-r bypass is folded into the same accumulators as extra 16-deep MFMA
+// steps (u and g are fp32 in memory and are rounded to AT for those steps).
 //
 // Tiles: 256 tokens x BN outputs per workgroup (BN = 256 or 128), contraction
 // step 64 (= one 64-element chunk of every weight row in the forward: one
@@ -19,14 +21,14 @@
 // accumulator tiles.  LDS is double-buffered: while the matrix cores work on
 // step k, the registers loaded during step k-1 (step k+1's tiles) are written
 // to the other buffer and step k+2's global loads are issued; one barrier
-// per step.  LDS rows are 64 bf16 = 8 chunks of 16 bytes.  gfx950 serves a
+// per step.  LDS rows are 64 16-bit values = 8 chunks of 16 bytes.  gfx950 serves a
 // 16-byte-per-lane LDS read 16 lanes per pass over 64 banks (256 bytes), so
 // the 16 rows one pass touches must land on 16 distinct 16-byte bank slots:
 // chunk c of row r is stored at position c ^ ((r >> 1) & 7); with the row
 // parity choosing the bank half this spreads any 16 consecutive rows read at
 // the same logical chunk over all 64 banks.
 //
-// v_mfma_f32_32x32x16_bf16 layout (gfx950): A lane l holds A[l % 32][8*(l/32)
+// v_mfma_f32_32x32x16_{bf16,f16} layout (gfx950): A lane l holds A[l % 32][8*(l/32)
 // .. +8], B lane l holds B[8*(l/32) .. +8][l % 32], result register v of lane
 // l is D[8*(v/4) + 4*(l/32) + v%4][l % 32].
 //
@@ -42,15 +44,15 @@ namespace qlora {
 constexpr int kBM = 256;
 constexpr int kBK = 64;
 constexpr int kThreads = 512;
-constexpr int kRowBytes = 128;  // 64 bf16 per LDS row
+constexpr int kRowBytes = 128;  // 64 16-bit values per LDS row
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
+template <typename AT>
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  return Half<AT>::mfma32(a, b, c);
 }
 
 // Workgroup -> tile.  Consecutive workgroup ids are spread round-robin over
@@ -76,39 +78,9 @@ __device__ __forceinline__ void tile_of(int64_t mt_count, int64_t nt_count, int6
   }
 }
 
-// Eight consecutive entries j0..j0+7 of a length-r row (zero past r), scaled, as bf16.
-template <typename T>
-__device__ __forceinline__ u32x4 lora_row8(const T *row, int j0, int r, float scale) {
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (j0 + e < r) ? scale * load_as_f32(row, j0 + e) : 0.0f;
-  return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-               pack_bf16x2(v[6], v[7])};
-}
-
-// 256 rows x 64 bf16 activation tile: 4 chunks of 16 B per lane.
+// 256 rows x 64 16-bit activation tile in registers: 4 chunks of 16 B per lane.
 struct ActStage {
   u32x4 v[4];
-  __device__ __forceinline__ void load(const uint16_t *__restrict__ src, int64_t ld, int64_t r0,
-                                       int64_t rows, int64_t c0, int t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      const int row = id >> 3, c = id & 7;
-      const int64_t rr = r0 + row;
-      if (rr < rows)
-        v[i] = *reinterpret_cast<const u32x4 *>(src + rr * ld + c0 + 8 * c);
-      else
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t *lds, int t) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kThreads * i;
-      *reinterpret_cast<u32x4 *>(lds + swz(id >> 3, id & 7)) = v[i];
-    }
-  }
 };
 
 __device__ __forceinline__ void zero_acc(f32x16 *acc, int n) {
@@ -117,12 +89,12 @@ __device__ __forceinline__ void zero_acc(f32x16 *acc, int n) {
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 }
 
-// Store a wave's transposed accumulators as bf16: register v of
+// Store a wave's transposed accumulators in format AT: register v of
 // accumulator (i, j) in lane l is out[row][col], row = row_base + 32 i +
 // l % 32, col = col_base + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4.  Full
 // tiles use 8-byte stores; a tile crossing the last column stores element
 // by element.
-template <int MI, int NJ>
+template <typename AT, int MI, int NJ>
 __device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t ld, int64_t rows,
                                              int64_t cols, int64_t row_base, int64_t col_base,
                                              const f32x16 (&acc)[MI][NJ], int lane) {
@@ -139,13 +111,13 @@ __device__ __forceinline__ void store_tile_t(uint16_t *__restrict__ out, int64_t
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<u32x2 *>(p + 32 * j + 8 * q) =
-              u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                    pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+              u32x2{Half<AT>::pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                    Half<AT>::pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
     } else {
       for (int j = 0; j < NJ; ++j)
         for (int v = 0; v < 16; ++v) {
           const int c = 32 * j + 8 * (v >> 2) + (v & 3);
-          if (col_base + 4 * lk + c < cols) p[c] = f32_to_bf16_bits(acc[i][j][v]);
+          if (col_base + 4 * lk + c < cols) p[c] = Half<AT>::bits(acc[i][j][v]);
         }
     }
   }
@@ -183,8 +155,9 @@ __device__ __forceinline__ void store_tile_f32(float *__restrict__ out, int64_t 
   }
 }
 
-// out[e] = bf16(sum_s part[s][e]), s in increasing order; 4 elements per lane
+// out[e] = AT(sum_s part[s][e]), s in increasing order; 4 elements per lane
 // (count % 4 == 0).
+template <typename AT>
 __global__ __launch_bounds__(256) void k_reduce_split(const float *__restrict__ part, int S,
                                                       int64_t count, uint16_t *__restrict__ out) {
   const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
@@ -195,17 +168,17 @@ __global__ __launch_bounds__(256) void k_reduce_split(const float *__restrict__ 
     acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
   }
   *reinterpret_cast<u32x2 *>(out + e) =
-      u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      u32x2{Half<AT>::pack2(acc[0], acc[1]), Half<AT>::pack2(acc[2], acc[3])};
 }
 
-// Rank-r operand tiles are staged once per 16-rank chunk into LDS as bf16
+// Rank-r operand tiles are staged once per 16-rank chunk into LDS in format AT
 // rows of 16 values with a 48-byte stride (the 16 rows one 16-byte-per-lane
 // read pass touches then start on 16 distinct 4-bank groups).
 constexpr int kLoraStride = 48;
 
 // rows x 16 slice [j0, j0 + 16) of a row-major [*, r] factor, times scale,
-// rounded to bf16; rows past `valid` and ranks past r are zero.
-template <int ROWS, int NT, typename T>
+// rounded to AT; rows past `valid` and ranks past r are zero.
+template <int ROWS, int NT, typename AT, typename T>
 __device__ __forceinline__ void stage_lora(uint8_t *dst, const T *__restrict__ src, int64_t row0,
                                            int64_t valid, int32_t r, int j0, float scale, int t) {
   for (int e = t; e < ROWS * 16; e += NT) {
@@ -213,21 +186,21 @@ __device__ __forceinline__ void stage_lora(uint8_t *dst, const T *__restrict__ s
     const int64_t gr = row0 + row;
     float v = 0.0f;
     if (gr < valid && j0 + jj < r) v = scale * load_as_f32(src, gr * r + j0 + jj);
-    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = f32_to_bf16_bits(v);
+    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = Half<AT>::bits(v);
   }
 }
 
 // ROWS x 16 slice of the transpose of a row-major [r, ld] factor: staged
 // row `row` holds src[(j0 + jj) * ld + col0 + row], jj = 0..15 (lanes walk
 // along a source row, so the loads are coalesced).
-template <int ROWS, int NT, typename T>
+template <int ROWS, int NT, typename AT, typename T>
 __device__ __forceinline__ void stage_lora_t(uint8_t *dst, const T *__restrict__ src, int64_t ld,
                                              int64_t col0, int32_t r, int j0, int t) {
   for (int e = t; e < ROWS * 16; e += NT) {
     const int jj = e / ROWS, row = e % ROWS;
     float v = 0.0f;
     if (j0 + jj < r) v = load_as_f32(src, (int64_t)(j0 + jj) * ld + col0 + row);
-    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = f32_to_bf16_bits(v);
+    *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = Half<AT>::bits(v);
   }
 }
 
@@ -239,7 +212,7 @@ __device__ __forceinline__ u32x4 lora_frag(const uint8_t *src, int row, int lk) 
 // wave-private LDS slice of 32 rows, so every global store instruction
 // writes whole 16-byte pieces of 64 / (TN / 8) consecutive rows.  Needs a
 // full tile in the column direction and ld % 8 == 0.
-template <int MI, int NJ>
+template <typename AT, int MI, int NJ>
 __device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64_t ld,
                                                int64_t rows, int64_t row_base, int64_t col_base,
                                                const f32x16 (&acc)[MI][NJ], uint8_t *slice,
@@ -256,8 +229,8 @@ __device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x2 *>(slice + lr * OS + 2 * (32 * j + 8 * q + 4 * lk)) =
-            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            u32x2{Half<AT>::pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                  Half<AT>::pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
 #pragma unroll
     for (int it = 0; it < 32 / RPI; ++it) {
       const int row = it * RPI + lane / CPR, c = lane % CPR;
@@ -271,7 +244,7 @@ __device__ __forceinline__ void store_tile_lds(uint16_t *__restrict__ out, int64
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int BN, typename LT, bool DQ>
+template <int BN, typename AT, typename LT, bool DQ>
 __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restrict__ x, int64_t M,
                                                        const uint8_t *__restrict__ packed,
                                                        BlockScales sc, int64_t N, int64_t K,
@@ -355,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
     for (int e = 0; e < BPQ; ++e) {
       const int bi = BPQ * qq + e;
       const float2 p = lut[(wr[bi >> 2] >> (8 * (bi & 3))) & 0xFF];
-      d[e] = pack_bf16x2(p.x * wa, p.y * wa);
+      d[e] = Half<AT>::pack2(p.x * wa, p.y * wa);
     }
     if constexpr (BPQ == 4) {
       *reinterpret_cast<u32x4 *>(ws[buf] + swz(w_row, 4 * w_part + qq)) =
@@ -381,8 +354,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   // main loop by the first contraction slice; staged here so that its loads
   // overlap the first tile loads
   if (split == 0) {
-    stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, 0, s, t);
-    stage_lora<BN, kThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
+    stage_lora<kBM, kThreads, AT>(ls_u, u, m0, M, r, 0, s, t);
+    stage_lora<BN, kThreads, AT>(ls_b, B, n0, N, r, 0, 1.0f, t);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
@@ -423,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(b[cb][j], a[cb][i], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(b[cb][j], a[cb][i], acc[i][j]);
     }
     __syncthreads();
   }
@@ -434,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
   for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora<kBM, kThreads>(ls_u, u, m0, M, r, j0, s, t);
-      stage_lora<BN, kThreads>(ls_b, B, n0, N, r, j0, 1.0f, t);
+      stage_lora<kBM, kThreads, AT>(ls_u, u, m0, M, r, j0, s, t);
+      stage_lora<BN, kThreads, AT>(ls_b, B, n0, N, r, j0, 1.0f, t);
       __syncthreads();
     }
     u32x4 ua[4], bb[NJ];
@@ -446,16 +419,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(bb[j], ua[i], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(bb[j], ua[i], acc[i][j]);
   }
   if (nsplit > 1)
     store_tile_f32<4, NJ>(part + (int64_t)split * M * N, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc,
                        lane);
   else if (n0 + BN <= N && N % 8 == 0)
-    store_tile_lds<4, NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
+    store_tile_lds<AT, 4, NJ>(y, N, M, m0 + 128 * wm, n0 + TN * wn, acc,
                        &xs[0][0] + wave * 32 * (2 * TN + 16), lane);
   else
-    store_tile_t<4, NJ>(y, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc, lane);
+    store_tile_t<AT, 4, NJ>(y, N, M, N, m0 + 128 * wm, n0 + TN * wn, acc, lane);
 }
 
 // ===========================================================================
@@ -477,7 +450,7 @@ constexpr int kSmBM = 64;
 constexpr int kSmBN = 128;
 constexpr int kSmThreads = 256;
 
-template <typename LT, bool DQ>
+template <typename AT, typename LT, bool DQ>
 __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
     int64_t N, int64_t K, const float *__restrict__ u, const LT *__restrict__ B, int32_t r,
@@ -550,8 +523,8 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   load_x(ks0, 1);
   load_w(ks0);
   if (split == 0) {
-    stage_lora<kSmBM, kSmThreads>(ls_u, u, m0, M, r, 0, s, t);
-    stage_lora<kSmBN, kSmThreads>(ls_b, B, n0, N, r, 0, 1.0f, t);
+    stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, 0, s, t);
+    stage_lora<kSmBN, kSmThreads, AT>(ls_b, B, n0, N, r, 0, 1.0f, t);
   }
   store_x(0, 0);
   store_x(0, 1);
@@ -586,7 +559,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const float2 p = lut[(wv[kk] >> (8 * bb)) & 0xFF];
-        wop[bb] = pack_bf16x2(p.x * wa, p.y * wa);
+        wop[bb] = Half<AT>::pack2(p.x * wa, p.y * wa);
       }
       // staging of step k + 1 into the other buffer, one piece per op, each
       // register refilled for step k + 2 right after it was stored
@@ -598,7 +571,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
         load_w(pf);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i][0] = mfma32(wop, xa[cb][i], acc[i][0]);
+      for (int i = 0; i < 2; ++i) acc[i][0] = mfma32<AT>(wop, xa[cb][i], acc[i][0]);
     }
     __syncthreads();
   }
@@ -607,21 +580,21 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora<kSmBM, kSmThreads>(ls_u, u, m0, M, r, j0, s, t);
-      stage_lora<kSmBN, kSmThreads>(ls_b, B, n0, N, r, j0, 1.0f, t);
+      stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, j0, s, t);
+      stage_lora<kSmBN, kSmThreads, AT>(ls_b, B, n0, N, r, j0, 1.0f, t);
       __syncthreads();
     }
     const u32x4 bb = lora_frag(ls_b, my_row, lk);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = mfma32(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
+    for (int i = 0; i < 2; ++i) acc[i][0] = mfma32<AT>(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
   }
   const int64_t col = n0 + 32 * wave;
   if (nsplit > 1)
     store_tile_f32<2, 1>(part + (int64_t)split * M * N, N, M, N, m0, col, acc, lane);
   else if (n0 + kSmBN <= N && N % 8 == 0)  // per-wave slices of 32 rows in a dead staging buffer
-    store_tile_lds<2, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
+    store_tile_lds<AT, 2, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
   else
-    store_tile_t<2, 1>(y, N, M, N, m0, col, acc, lane);
+    store_tile_t<AT, 2, 1>(y, N, M, N, m0, col, acc, lane);
 }
 
 // ===========================================================================
@@ -671,7 +644,7 @@ struct DxShape {
   static constexpr int LPR = NT / kDxBC;            // staging lanes per weight row
 };
 
-template <int BM, int BX, typename LT, bool DQ, bool DROP>
+template <int BM, int BX, typename AT, typename LT, bool DQ, bool DROP>
 __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__restrict__ dy, int64_t M,
                                                       const uint8_t *__restrict__ packed,
                                                       BlockScales sc, int64_t N, int64_t K,
@@ -685,11 +658,11 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
   constexpr int TM = 32 * MI;  // tokens per wave
   constexpr int TX = BX / 4;
   constexpr int NJ = TX / 32;
-  constexpr int NU = BX / (8 * LPR);  // 32-bit code words (= 16-byte bf16 chunks) per lane per step
+  constexpr int NU = BX / (8 * LPR);  // 32-bit code words (= 16-byte 16-bit chunks) per lane per step
   static_assert(XC == 2 || XC == 4, "dy staging is split into 2 or 4 chunks");
   static_assert(NU == 2 || NU == 4, "a lane stages 2 or 4 code words per step");
-  __shared__ __attribute__((aligned(16))) uint8_t ds[2][BM * kRowBytes];  // dy [m][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];  // W^ [n][k] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t ds[2][BM * kRowBytes];  // dy [m][n], AT
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2][kDxBC * 2 * BX];  // W^ [n][k], AT
   __shared__ __attribute__((aligned(16))) uint8_t ls_g[BM * kLoraStride];
   __shared__ __attribute__((aligned(16))) uint8_t ls_a[BX * kLoraStride];
   __shared__ float2 lut[256];
@@ -761,7 +734,7 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
       for (int bb = 0; bb < 4; ++bb) {
         // byte bb holds codes 2bb (high nibble) and 2bb+1 of the word
         const float2 pv = lut[(wr[u] >> (8 * bb)) & 0xFF];
-        o[bb] = pack_bf16x2(pv.x * wa, pv.y * wa);
+        o[bb] = Half<AT>::pack2(pv.x * wa, pv.y * wa);
       }
       *reinterpret_cast<u32x4 *>(wt[buf] + wswz<BX>(wrow, (wk >> 3) + u)) = o;
     }
@@ -794,8 +767,8 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
   // and A^T), used after the main loop by the first contraction slice;
   // staged here so that its loads overlap the first tile loads
   if (split == 0) {
-    stage_lora<BM, NT>(ls_g, g, m0, M, r, 0, 1.0f, t);
-    stage_lora_t<BX, NT>(ls_a, A, K, k0, r, 0, t);
+    stage_lora<BM, NT, AT>(ls_g, g, m0, M, r, 0, 1.0f, t);
+    stage_lora_t<BX, NT, AT>(ls_a, A, K, k0, r, 0, t);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_quarter(0, i);
@@ -814,8 +787,8 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
       for (int j0 = 0; j0 < r; j0 += 16) {
         if (j0 > 0) {
           __syncthreads();
-          stage_lora<BM, NT>(ls_g, g, m0, M, r, j0, 1.0f, t);
-          stage_lora_t<BX, NT>(ls_a, A, K, k0, r, j0, t);
+          stage_lora<BM, NT, AT>(ls_g, g, m0, M, r, j0, 1.0f, t);
+          stage_lora_t<BX, NT, AT>(ls_a, A, K, k0, r, j0, t);
           __syncthreads();
         }
         u32x4 ga[MI], ab[NJ];
@@ -826,7 +799,7 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(ab[j], ga[i], acc[i][j]);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -874,7 +847,7 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(b[cb][j], a[cb][i], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(b[cb][j], a[cb][i], acc[i][j]);
     }
     __syncthreads();
   }
@@ -884,8 +857,8 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
   for (int j0 = 0; j0 < (split == 0 && !DROP ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora<BM, NT>(ls_g, g, m0, M, r, j0, 1.0f, t);
-      stage_lora_t<BX, NT>(ls_a, A, K, k0, r, j0, t);
+      stage_lora<BM, NT, AT>(ls_g, g, m0, M, r, j0, 1.0f, t);
+      stage_lora_t<BX, NT, AT>(ls_a, A, K, k0, r, j0, t);
       __syncthreads();
     }
     u32x4 ga[MI], ab[NJ];
@@ -896,14 +869,14 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(ab[j], ga[i], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(ab[j], ga[i], acc[i][j]);
   }
   // K % 128 == 0 here, so every tile is full in the column direction
   if (nsplit > 1)
     store_tile_f32<MI, NJ>(part + (int64_t)split * M * K, K, M, K, m0 + TM * wm, k0 + TX * wn,
                            acc, lane);
   else  // per-wave slices of 32 rows in a dead staging buffer
-    store_tile_lds<MI, NJ>(dx, K, M, m0 + TM * wm, k0 + TX * wn, acc,
+    store_tile_lds<AT, MI, NJ>(dx, K, M, m0 + TM * wm, k0 + TX * wn, acc,
                            (BM == 256 ? &ds[0][0] : &wt[0][0]) + wave * 32 * (2 * TX + 16), lane);
 }
 
@@ -978,65 +951,80 @@ size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? (size_t)S * (size_t)M * (size_t)K : 0;
 }
 
-static int reduce_split(const float *part, int S, int64_t count, uint16_t *out,
+static int reduce_split(int act_dtype, const float *part, int S, int64_t count, uint16_t *out,
                         hipStream_t stream) {
   const int64_t n4 = count / 4;
-  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     part, S, count, out);
+  with_half(act_dtype, [&](auto *tag) {
+    hipLaunchKernelGGL((k_reduce_split<elem_of<decltype(tag)>>), dim3((unsigned)((n4 + 255) / 256)),
+                       dim3(256), 0, stream, part, S, count, out);
+  });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }
 
-int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, hipStream_t stream, float *part) {
+// A 16-bit LoRA factor has the activations' format (checked by the caller):
+// LT is float or AT.
+int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
+                    BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,
+                    int lora_dtype, int32_t r, float s, void *yv, hipStream_t stream,
+                    float *part) {
+  const uint16_t *x = (const uint16_t *)xv;
+  uint16_t *y = (uint16_t *)yv;
+  const bool dq = sc.absmax == nullptr;
   if (M <= kFwdSmallM) {
     const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
     const int S = part ? fwd_split(M, N, K) : 1;
-    const bool dq = sc.absmax == nullptr;
 #define QL_FWS(LT, DQV)                                                                          \
-  hipLaunchKernelGGL((k_gemm_fwd_small<LT, DQV>), dim3((unsigned)G, (unsigned)S),               \
+  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV>), dim3((unsigned)G, (unsigned)S),           \
                      dim3(kSmThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, \
                      y, part, S)
-    if (lora_dtype == QL_BF16) {
-      if (dq) QL_FWS(uint16_t, true); else QL_FWS(uint16_t, false);
-    } else {
-      if (dq) QL_FWS(float, true); else QL_FWS(float, false);
-    }
+    with_half(act_dtype, [&](auto *tag) {
+      using AT = elem_of<decltype(tag)>;
+      if (lora_dtype == QL_F32) {
+        if (dq) QL_FWS(float, true); else QL_FWS(float, false);
+      } else {
+        if (dq) QL_FWS(AT, true); else QL_FWS(AT, false);
+      }
+    });
 #undef QL_FWS
     QL_HIP_CHECK_LAUNCH();
-    if (S > 1) return reduce_split(part, S, M * N, y, stream);
+    if (S > 1) return reduce_split(act_dtype, part, S, M * N, y, stream);
     return QL_OK;
   }
   const int bn = pick_width(M, N, 1);
   const int64_t G = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
   const int S = part ? fwd_split(M, N, K) : 1;
-  const bool dq = sc.absmax == nullptr;
 #define QL_FWD(BNV, LT, DQV)                                                                     \
-  hipLaunchKernelGGL((k_gemm_fwd<BNV, LT, DQV>), dim3((unsigned)G, (unsigned)S), dim3(kThreads), \
-                     0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, y, part, S)
+  hipLaunchKernelGGL((k_gemm_fwd<BNV, AT, LT, DQV>), dim3((unsigned)G, (unsigned)S),            \
+                     dim3(kThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s,  \
+                     y, part, S)
 #define QL_FWD_DQ(BNV, LT) \
   do { if (dq) QL_FWD(BNV, LT, true); else QL_FWD(BNV, LT, false); } while (0)
-  if (bn == 256) {
-    if (lora_dtype == QL_BF16) QL_FWD_DQ(256, uint16_t);
-    else QL_FWD_DQ(256, float);
-  } else {
-    if (lora_dtype == QL_BF16) QL_FWD_DQ(128, uint16_t);
-    else QL_FWD_DQ(128, float);
-  }
+  with_half(act_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (bn == 256) {
+      if (lora_dtype == QL_F32) QL_FWD_DQ(256, float);
+      else QL_FWD_DQ(256, AT);
+    } else {
+      if (lora_dtype == QL_F32) QL_FWD_DQ(128, float);
+      else QL_FWD_DQ(128, AT);
+    }
+  });
 #undef QL_FWD_DQ
 #undef QL_FWD
   QL_HIP_CHECK_LAUNCH();
-  if (S > 1) return reduce_split(part, S, M * N, y, stream);
+  if (S > 1) return reduce_split(act_dtype, part, S, M * N, y, stream);
   return QL_OK;
 }
 
 bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 == 0; }
 
-int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
-                   int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream, float *part, const Dropout *drop,
-                   float drop_scale) {
+int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *packed,
+                   BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
+                   int lora_dtype, int32_t r, void *dxv, hipStream_t stream, float *part,
+                   const Dropout *drop, float drop_scale) {
+  const uint16_t *dy = (const uint16_t *)dyv;
+  uint16_t *dx = (uint16_t *)dxv;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const bool small = M <= kDxSmallM;
   const int bm = small ? 64 : kBM;
@@ -1045,7 +1033,7 @@ int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockSc
   const int S = part ? dx_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
 #define QL_DX(BMV, BXV, LT, DQV, DRV)                                                            \
-  hipLaunchKernelGGL((k_gemm_dx<BMV, BXV, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),       \
+  hipLaunchKernelGGL((k_gemm_dx<BMV, BXV, AT, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),   \
                      dim3(DxShape<BMV>::NT), 0, stream, dy, M, packed, sc, N, K, g, (const LT *)A, \
                      r, dx, part, S, dr, drop_scale)
 #define QL_DX_DR(BMV, BXV, LT, DQV) \
@@ -1053,16 +1041,19 @@ int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockSc
 #define QL_DX_DQ(BMV, BXV, LT) \
   do { if (dq) QL_DX_DR(BMV, BXV, LT, true); else QL_DX_DR(BMV, BXV, LT, false); } while (0)
 #define QL_DX_LT(BMV, BXV) \
-  do { if (lora_dtype == QL_BF16) QL_DX_DQ(BMV, BXV, uint16_t); else QL_DX_DQ(BMV, BXV, float); } while (0)
-  if (small) QL_DX_LT(64, 128);
-  else if (bx == 256) QL_DX_LT(256, 256);
-  else QL_DX_LT(256, 128);
+  do { if (lora_dtype == QL_F32) QL_DX_DQ(BMV, BXV, float); else QL_DX_DQ(BMV, BXV, AT); } while (0)
+  with_half(act_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (small) QL_DX_LT(64, 128);
+    else if (bx == 256) QL_DX_LT(256, 256);
+    else QL_DX_LT(256, 128);
+  });
 #undef QL_DX_LT
 #undef QL_DX_DQ
 #undef QL_DX_DR
 #undef QL_DX
   QL_HIP_CHECK_LAUNCH();
-  if (S > 1) return reduce_split(part, S, M * K, dx, stream);
+  if (S > 1) return reduce_split(act_dtype, part, S, M * K, dx, stream);
   return QL_OK;
 }
 

@@ -1,5 +1,6 @@
-// gemv.hip -- decode-sized forward of the QLoRA layer (M <= 16 tokens, bf16),
-// one kernel launch per call:
+// gemv.hip -- decode-sized forward of the QLoRA layer (M <= 16 tokens, 16-bit
+// activations: bf16, or fp16 as the compute dtype of Gemma lesson 09, sec.
+// 9.3), one kernel launch per call:
 //
 //   u = x A^T,   y = x W^^T + s u B^T     (26. QLoRA and 4bit Quantization, Step 3)
 //
@@ -12,20 +13,20 @@
 // matrix-core operand layout.  The round's block constants (absmax, or the
 // double-quantised form q * sigma + mu) are resolved once into an LDS table.
 //
-// The 16x16x32 bf16 matrix-core op multiplies the activations by the
+// The 16x16x32 16-bit matrix-core op multiplies the activations by the
 // *unscaled* codebook values of one 64-element chunk (16 rows x 32 columns
 // per op, two ops per chunk; a chunk lies inside one NF4 block of 64 or 128);
 // the block's fp32 constant is then applied to the 4 partial sums each lane
 // holds (26. ..., Step 4: table[index] * scale, with the scale taken out of
 // the 64-term sum it multiplies).  The codebook lookup
-// goes through a byte -> bf16x2 table in LDS built from immediates.
+// goes through a byte -> 2 x 16-bit table in LDS built from immediates.
 //
 // The rank-r pre-product u = x A^T is recomputed by every workgroup from the
 // activation operand it already holds (extra 16x16x32 ops against rows of A,
 // read from L2), so decode needs no second kernel and no grid-wide
 // dependency.  Workgroup 0 stores u when the caller asks for it.
 //
-// Operand layout of v_mfma_f32_16x16x32_bf16 (gfx950): A lane l holds
+// Operand layout of v_mfma_f32_16x16x32_{bf16,f16} (gfx950): A lane l holds
 // A[l % 16][8*(l/16) .. +8], B lane l holds B[8*(l/16) .. +8][l % 16], and the
 // result lane l holds D[4*(l/16) .. +4][l % 16].  All operands use the same
 // permutation of K within a block: op c of block b covers
@@ -45,11 +46,11 @@ constexpr int kGemvRowStride = kGemvRound * 32 + 16;
 constexpr int kGemvChunks = kGemvRows * kGemvRound * 2 / kGemvThreads;
 // NF4 block constants per lane per round
 constexpr int kGemvScales = kGemvRows * kGemvRound / kGemvThreads;
-// LDS stride of one staged activation row (a round of bf16 values + 16 bytes)
+// LDS stride of one staged activation row (a round of 16-bit values + 16 bytes)
 constexpr int kGemvXStride = kGemvRound * 128 + 16;
 
 // Blocks whose activation and A loads are in flight together: 8 for a
-// 16-wide rank tile in bf16, fewer as the per-block register footprint grows.
+// 16-wide rank tile in 16 bits, fewer as the per-block register footprint grows.
 template <typename LT, int JT>
 constexpr int gemv_batch() {
   constexpr int w = JT * (int)(sizeof(LT) / 2);
@@ -64,20 +65,20 @@ __device__ __forceinline__ float nf4_immediate(int i) {
   return v;
 }
 
-// 16 consecutive LoRA-A values of one rank row, kept raw until use.
-template <typename LT>
-struct ARaw;
-template <>
-struct ARaw<uint16_t> {
+// 16 consecutive LoRA-A values of one rank row, kept raw until use; half(c)
+// gives values 8c .. 8c + 7 as a matrix-core operand in format AT.  LT is
+// AT (used as loaded) or float.
+template <typename AT, typename LT>
+struct ARaw {
   u32x4 v[2];
-  __device__ __forceinline__ void load(const uint16_t *p) {
+  __device__ __forceinline__ void load(const LT *p) {
     v[0] = reinterpret_cast<const u32x4 *>(p)[0];
     v[1] = reinterpret_cast<const u32x4 *>(p)[1];
   }
   __device__ __forceinline__ u32x4 half(int c) const { return v[c]; }
 };
-template <>
-struct ARaw<float> {
+template <typename AT>
+struct ARaw<AT, float> {
   float4 v[4];
   __device__ __forceinline__ void load(const float *p) {
 #pragma unroll
@@ -85,23 +86,23 @@ struct ARaw<float> {
   }
   __device__ __forceinline__ u32x4 half(int c) const {
     const float4 a = v[2 * c], b = v[2 * c + 1];
-    return u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                 pack_bf16x2(b.z, b.w)};
+    return u32x4{Half<AT>::pack2(a.x, a.y), Half<AT>::pack2(a.z, a.w), Half<AT>::pack2(b.x, b.y),
+                 Half<AT>::pack2(b.z, b.w)};
   }
 };
 
 // Per-block register operands of one lane: 2 x 8 activations and JT x 16 A values.
-template <typename LT, int JT>
+template <typename AT, typename LT, int JT>
 struct GemvBlock {
   u32x4 x0, x1;
-  ARaw<LT> a[JT];
+  ARaw<AT, LT> a[JT];
 };
 
 // XM > 0: the round's activations of all M <= XM token rows are staged in
 // LDS once per workgroup (the operand layout repeats a token row across the
 // 16 lanes of a lane group, which would otherwise be 16 / M copies of the
 // same bytes through the load path); XM = 0: read in operand layout.
-template <typename LT, int JT, bool DQ, int XM>
+template <typename AT, typename LT, int JT, bool DQ, int XM>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
                                                            const uint8_t *__restrict__ packed,
                                                            BlockScales sc, int64_t N, int64_t K,
@@ -150,14 +151,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     bv[i] = load_as_f32(B, nn * r + (j < r ? j : r - 1));
   }
   if (t < 256) {
-    const uint16_t hi = f32_to_bf16_bits(nf4_immediate(t >> 4));
-    const uint16_t lo = f32_to_bf16_bits(nf4_immediate(t & 15));
+    const uint16_t hi = Half<AT>::bits(nf4_immediate(t >> 4));
+    const uint16_t lo = Half<AT>::bits(nf4_immediate(t & 15));
     lut[t] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
 
   constexpr int kBatch = gemv_batch<LT, JT>();
   constexpr int kWaveBlocks = kGemvRound / kGemvWaves;  // blocks per wave per full round
-  GemvBlock<LT, JT> bl[kBatch];
+  GemvBlock<AT, LT, JT> bl[kBatch];
   // loads of blocks first .. first + kBatch - 1 of the round, clamped to its last block
   auto load_batch = [&](int64_t rb0, int first, int RB) {
 #pragma unroll
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     // the first batch's loads go out before the staging stores wait for the
     // weight slice (at rank tile 8 after them: the registers are needed)
     // A full round with activations in LDS and one load batch (one 16-rank
-    // tile in bf16) issues its A loads only after the staging barrier and
+    // tile in 16 bits) issues its A loads only after the staging barrier and
     // runs all weight ops first: the staging stores then wait for the
     // weight slice alone, and the A loads fly during the weight ops.
     const bool late_a = XM > 0 && kBatch == kWaveBlocks && JT < 8 && cnt == kWaveBlocks;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
 
     // one block, weight part: 2 ops against the unscaled codes, then the
     // block constant; returns the activation operand in xr0, xr1
-    auto wpart = [&](const GemvBlock<LT, JT> &g, int bb, u32x4 &xr0, u32x4 &xr1) {
+    auto wpart = [&](const GemvBlock<AT, LT, JT> &g, int bb, u32x4 &xr0, u32x4 &xr1) {
       const u32x2 w =
           *reinterpret_cast<const u32x2 *>(wt + nl * kGemvRowStride + 32 * bb + 8 * q);
       u32x4 wb0v, wb1v;
@@ -279,12 +280,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
         xr1 = g.x1;
       }
       f32x4 part = {0.f, 0.f, 0.f, 0.f};
-      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr0),
-                                                     __builtin_bit_cast(bf16x8, wb0v), part, 0,
-                                                     0, 0);
-      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr1),
-                                                     __builtin_bit_cast(bf16x8, wb1v), part, 0,
-                                                     0, 0);
+      part = Half<AT>::mfma16(xr0, wb0v, part);
+      part = Half<AT>::mfma16(xr1, wb1v, part);
       // part[v] = sum over the block of x[4q+v][k] * cb[idx[n][k]] for column n = n0 + nl
       const float a = scl[nl][bb];
 #pragma unroll
@@ -292,19 +289,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     };
     // one block, bypass part: 2 JT ops against A (at one rank tile, two
     // accumulator chains)
-    auto upart = [&](const GemvBlock<LT, JT> &g, const u32x4 &xr0, const u32x4 &xr1) {
+    auto upart = [&](const GemvBlock<AT, LT, JT> &g, const u32x4 &xr0, const u32x4 &xr1) {
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
-        uacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xr0), __builtin_bit_cast(bf16x8, g.a[jt].half(0)),
-            uacc[jt], 0, 0, 0);
+        uacc[jt] = Half<AT>::mfma16(xr0, g.a[jt].half(0), uacc[jt]);
         f32x4 &u1 = JT == 1 ? uacc1[jt] : uacc[jt];
-        u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xr1), __builtin_bit_cast(bf16x8, g.a[jt].half(1)), u1, 0,
-            0, 0);
+        u1 = Half<AT>::mfma16(xr1, g.a[jt].half(1), u1);
       }
     };
-    auto block = [&](const GemvBlock<LT, JT> &g, int bb) {
+    auto block = [&](const GemvBlock<AT, LT, JT> &g, int bb) {
       u32x4 xr0, xr1;
       wpart(g, bb, xr0, xr1);
       upart(g, xr0, xr1);
@@ -363,50 +356,60 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
       for (int w = 0; w < kGemvWaves; ++w) sum += red[w][mo][no];
       float l = 0.0f;
       for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[mo][j], bs[no][j], l);
-      y[(int64_t)mo * N + nn] = f32_to_bf16_bits(__builtin_fmaf(s, l, sum));
+      y[(int64_t)mo * N + nn] = Half<AT>::bits(__builtin_fmaf(s, l, sum));
     }
   }
 }
 
-template <typename LT, int JT, int XM>
+template <typename AT, typename LT, int JT, int XM>
 static void launch_xm(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
   if (sc.absmax == nullptr)
-    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, true, XM>), grid, dim3(kGemvThreads), 0, stream, x, M,
-                       packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, true, XM>), grid, dim3(kGemvThreads), 0, stream,
+                       x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
   else
-    hipLaunchKernelGGL((k_gemv_fwd<LT, JT, false, XM>), grid, dim3(kGemvThreads), 0, stream, x, M,
-                       packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, false, XM>), grid, dim3(kGemvThreads), 0, stream,
+                       x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
 }
 
-template <typename LT, int JT>
+template <typename AT, typename LT, int JT>
 static void launch_jt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
-  if (M == 1) launch_xm<LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else if (M <= 4) launch_xm<LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else launch_xm<LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  if (M == 1)
+    launch_xm<AT, LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else if (M <= 4)
+    launch_xm<AT, LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else
+    launch_xm<AT, LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
 }
 
-template <typename LT>
+template <typename AT, typename LT>
 static void launch_lt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
-  if (r <= 16) launch_jt<LT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else if (r <= 32) launch_jt<LT, 2>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else if (r <= 64) launch_jt<LT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else launch_jt<LT, 8>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  if (r <= 16) launch_jt<AT, LT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else if (r <= 32) launch_jt<AT, LT, 2>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else if (r <= 64) launch_jt<AT, LT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+  else launch_jt<AT, LT, 8>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
 }
 
-int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const void *A, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, float *u_save, hipStream_t stream) {
+// A 16-bit LoRA factor has the activations' format (checked by the caller).
+int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
+                    BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
+                    int lora_dtype, int32_t r, float s, void *yv, float *u_save,
+                    hipStream_t stream) {
+  const uint16_t *x = (const uint16_t *)xv;
+  uint16_t *y = (uint16_t *)yv;
   const dim3 grid((unsigned)((N + kGemvRows - 1) / kGemvRows));
-  if (lora_dtype == QL_BF16)
-    launch_lt<uint16_t>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else
-    launch_lt<float>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
+  with_half(act_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (lora_dtype == QL_F32)
+      launch_lt<AT, float>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
+    else
+      launch_lt<AT, AT>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
+  });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

@@ -44,25 +44,27 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
                      int lora_dtype, int32_t r, void *dx, hipStream_t stream);
 
-// gemv.hip: decode-sized forward (M <= 16, bf16 activations), one launch:
+// gemv.hip: decode-sized forward (M <= 16, 16-bit activations), one launch:
 // computes u = x A^T itself and writes it to u_save when non-null.
-int launch_gemv_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const void *A, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, float *u_save, hipStream_t stream);
+int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
+                    BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
+                    int lora_dtype, int32_t r, float s, void *y, float *u_save,
+                    hipStream_t stream);
 
-// gemm.hip: matrix-core forward and input-gradient products (bf16).  part:
-// fp32 workspace of gemm_*_partial_floats floats for split-K launches, or
-// NULL (no split).
+// gemm.hip: matrix-core forward and input-gradient products for 16-bit
+// activations (act_dtype QL_BF16 or QL_F16; a 16-bit lora_dtype equals it).
+// part: fp32 workspace of gemm_*_partial_floats floats for split-K
+// launches, or NULL (no split).
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
 size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K);
-int launch_gemm_fwd(const uint16_t *x, int64_t M, const uint8_t *packed, BlockScales sc,
-                    int64_t N, int64_t K, const float *u, const void *B, int lora_dtype, int32_t r,
-                    float s, uint16_t *y, hipStream_t stream, float *part);
+int launch_gemm_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
+                    BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,
+                    int lora_dtype, int32_t r, float s, void *y, hipStream_t stream, float *part);
 bool gemm_dx_supported(int64_t N, int64_t K);
-int launch_gemm_dx(const uint16_t *dy, int64_t M, const uint8_t *packed, BlockScales sc,
-                   int64_t N, int64_t K, const float *g, const void *A, int lora_dtype, int32_t r,
-                   uint16_t *dx, hipStream_t stream, float *part, const Dropout *drop = nullptr,
-                   float drop_scale = 1.0f);
+int launch_gemm_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *packed,
+                   BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
+                   int lora_dtype, int32_t r, void *dx, hipStream_t stream, float *part,
+                   const Dropout *drop = nullptr, float drop_scale = 1.0f);
 // dropout.hip: the keep mask of the LoRA dropout as bytes (0/1), [M, K]
 int launch_dropout_mask(int64_t M, int64_t K, const Dropout &d, uint8_t *keep,
                         hipStream_t stream);

@@ -72,9 +72,9 @@ __global__ __launch_bounds__(256) void k_lora_rows(const void *__restrict__ P, i
 }
 
 // ---------------------------------------------------------------------------
-// rows on the matrix cores (bf16 P): v_mfma_f32_16x16x32_bf16 with
+// rows on the matrix cores (16-bit P): v_mfma_f32_16x16x32_{bf16,f16} with
 // A = 16 rows of P x 32 contraction values (read straight from global, 16 B
-// per lane) and B = the LoRA factor slice staged in LDS as bf16 [j][c].
+// per lane) and B = the LoRA factor slice staged in LDS in P's format [j][c].
 // Wave w of the workgroup owns rows 16w..16w+15 of a 64-row tile and all JT
 // 16-wide rank tiles; the workgroup covers one CS-wide slice of the
 // contraction in a single round trip, with every trip count fixed at
@@ -95,7 +95,7 @@ enum { kQRowJ = 0, kQRowC = 1, kQElem = 2 };
 
 template <typename QT>
 constexpr int rows_cs_of(int jt) {
-  // bounds the staged factor to 8 (bf16) or 4 (fp32) 8-value loads per lane
+  // bounds the staged factor to 8 (16-bit) or 4 (fp32) 8-value loads per lane
   return (sizeof(QT) == 2 ? 1024 : 512) / jt > 512 ? 512 : (sizeof(QT) == 2 ? 1024 : 512) / jt;
 }
 
@@ -105,19 +105,18 @@ static int rows_jt(int32_t r) {
 }
 static int rows_cs(int32_t r, int q_dtype) {
   const int jt = rows_jt(r);
-  return q_dtype == QL_BF16 ? rows_cs_of<uint16_t>(jt) : rows_cs_of<float>(jt);
+  return q_dtype == QL_F32 ? rows_cs_of<float>(jt) : rows_cs_of<uint16_t>(jt);
 }
 
-// 8 consecutive values of a factor row as fp32 (zero where !ok)
+// 8 consecutive values of a factor row as fp32 (zero where !ok); QT is
+// float or a 16-bit storage type
 template <typename QT>
-struct Vec8;
-template <>
-struct Vec8<uint16_t> {
+struct Vec8 {
   u32x4 w;
-  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void load(const QT *p) { w = *reinterpret_cast<const u32x4 *>(p); }
   __device__ __forceinline__ float get(int e, bool ok) const {
     const uint32_t h = w[e >> 1];
-    return ok ? __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16)) : 0.0f;
+    return ok ? ((e & 1) ? Half<QT>::hi(h) : Half<QT>::lo(h)) : 0.0f;
   }
 };
 template <>
@@ -132,10 +131,11 @@ struct Vec8<float> {
   }
 };
 
-// DROP: P is the activation x of the LoRA dropout; its dropped elements
-// are zeroed as loaded (the 1/(1-p) scale is applied by the reduction).
-template <int CS, int JT, typename QT, int QMODE, bool DROP>
-__global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ P, int64_t M,
+// AT: the 16-bit format of P and of the matrix-core operands.  DROP: P is
+// the activation x of the LoRA dropout; its dropped elements are zeroed as
+// loaded (the 1/(1-p) scale is applied by the reduction).
+template <int CS, int JT, typename AT, typename QT, int QMODE, bool DROP>
+__global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int64_t M,
                                                    int64_t C, const QT *__restrict__ Q,
                                                    int64_t ldq_j, int64_t ldq_c, int32_t r,
                                                    float *__restrict__ partial, Dropout dr) {
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
 
   // ---- P loads: row mrow, contraction c0 + 32 i + 8 q ----
   const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + li;
-  const uint16_t *prow = P + (mrow < M ? mrow : M - 1) * C;
+  const AT *prow = P + (mrow < M ? mrow : M - 1) * C;
   u32x4 a[CS / 32];
 #pragma unroll
   for (int i = 0; i < CS / 32; ++i) {
@@ -197,17 +197,17 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
     }
   }
 
-  // ---- factor slice to LDS, bf16 [j][c] ----
+  // ---- factor slice to LDS, 16-bit [j][c] ----
   if constexpr (QMODE == kQRowJ) {
 #pragma unroll
     for (int b = 0; b < NV; ++b) {
       const int e = t + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
       const bool ok = j < r && c0 + 8 * c8 + 8 <= C;
       *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) =
-          u32x4{pack_bf16x2(qv[b].get(0, ok), qv[b].get(1, ok)),
-                pack_bf16x2(qv[b].get(2, ok), qv[b].get(3, ok)),
-                pack_bf16x2(qv[b].get(4, ok), qv[b].get(5, ok)),
-                pack_bf16x2(qv[b].get(6, ok), qv[b].get(7, ok))};
+          u32x4{Half<AT>::pack2(qv[b].get(0, ok), qv[b].get(1, ok)),
+                Half<AT>::pack2(qv[b].get(2, ok), qv[b].get(3, ok)),
+                Half<AT>::pack2(qv[b].get(4, ok), qv[b].get(5, ok)),
+                Half<AT>::pack2(qv[b].get(6, ok), qv[b].get(7, ok))};
     }
   } else if constexpr (QMODE == kQRowC) {
 #pragma unroll
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
         *reinterpret_cast<uint16_t *>(qs + (8 * j8 + jj) * QST + 2 * cc) =
-            f32_to_bf16_bits(qv[b].get(jj, ok));
+            Half<AT>::bits(qv[b].get(jj, ok));
     }
   } else {
 #pragma unroll
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
       const int e = t + 256 * b;
       int j, cc;
       if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
-      *reinterpret_cast<uint16_t *>(qs + j * QST + 2 * cc) = f32_to_bf16_bits(qe[b]);
+      *reinterpret_cast<uint16_t *>(qs + j * QST + 2 * cc) = Half<AT>::bits(qe[b]);
     }
   }
   __syncthreads();
@@ -239,9 +239,7 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const uint16_t *__restrict__ 
     for (int jt = 0; jt < JT; ++jt) {
       const u32x4 b = *reinterpret_cast<const u32x4 *>(qs + (16 * jt + li) * QST +
                                                        2 * (32 * i + 8 * q));
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                        __builtin_bit_cast(bf16x8, b), acc[jt],
-                                                        0, 0, 0);
+      acc[jt] = Half<AT>::mfma16(a[i], b, acc[jt]);
     }
   }
   const int64_t mbase = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + 4 * q;
@@ -293,7 +291,7 @@ static int mrows_slices(int64_t C, int32_t r, int q_dtype) {
   return (int)((C + rows_cs(r, q_dtype) - 1) / rows_cs(r, q_dtype));
 }
 
-static bool rows_use_mfma(int p_dtype, int64_t C) { return p_dtype == QL_BF16 && C % 8 == 0; }
+static bool rows_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
 
 size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r) {
   const int64_t s1 = rows_slices(M, C), s2 = mrows_slices(C, r, QL_F32);
@@ -319,9 +317,9 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     if (ldq_c == 1 && C % 8 == 0 && ldq_j % 8 == 0 && C >= 8) mode = kQRowJ;
     else if (ldq_j == 1 && r % 8 == 0 && ldq_c % 8 == 0) mode = kQRowC;
 #define QL_ROWS_M(JTV, QT, MODEV, DRV)                                                           \
-  hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, QT, MODEV, DRV>), grid, dim3(256),   \
-                     0, stream, (const uint16_t *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r, partial, \
-                     dr)
+  hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, AT, QT, MODEV, DRV>), grid,          \
+                     dim3(256), 0, stream, (const AT *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r,  \
+                     partial, dr)
 #define QL_ROWS_Q(JTV, QT)                                                                       \
   do {                                                                                           \
     if (drop) QL_ROWS_M(JTV, QT, kQRowJ, true);                                                  \
@@ -330,11 +328,15 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     else QL_ROWS_M(JTV, QT, kQElem, false);                                                      \
   } while (0)
 #define QL_ROWS_JT(JTV) \
-  do { if (q_dtype == QL_BF16) QL_ROWS_Q(JTV, uint16_t); else QL_ROWS_Q(JTV, float); } while (0)
-    if (jt == 1) QL_ROWS_JT(1);
-    else if (jt == 2) QL_ROWS_JT(2);
-    else if (jt == 4) QL_ROWS_JT(4);
-    else QL_ROWS_JT(8);
+  do { if (q_dtype == QL_F32) QL_ROWS_Q(JTV, float); else QL_ROWS_Q(JTV, AT); } while (0)
+    // a 16-bit factor has the activations' format (checked by the caller)
+    with_half(p_dtype, [&](auto *tag) {
+      using AT = elem_of<decltype(tag)>;
+      if (jt == 1) QL_ROWS_JT(1);
+      else if (jt == 2) QL_ROWS_JT(2);
+      else if (jt == 4) QL_ROWS_JT(4);
+      else QL_ROWS_JT(8);
+    });
 #undef QL_ROWS_JT
 #undef QL_ROWS_Q
 #undef QL_ROWS_M
@@ -343,14 +345,12 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     int64_t slice = (C + S - 1) / S;
     slice = (slice + kRowsChunk - 1) / kRowsChunk * kRowsChunk;
     const dim3 grid((unsigned)((M + kRowsTM - 1) / kRowsTM), (unsigned)S);
-#define QL_ROWS(PT, QT)                                                                        \
-  hipLaunchKernelGGL((k_lora_rows<PT, QT>), grid, dim3(256), 0, stream, P, M, C, Q, ldq_j,   \
-                     ldq_c, r, slice, partial)
-    if (p_dtype == QL_BF16 && q_dtype == QL_BF16) QL_ROWS(uint16_t, uint16_t);
-    else if (p_dtype == QL_BF16) QL_ROWS(uint16_t, float);
-    else if (q_dtype == QL_BF16) QL_ROWS(float, uint16_t);
-    else QL_ROWS(float, float);
-#undef QL_ROWS
+    with_type(p_dtype, [&](auto *pt) {
+      with_type(q_dtype, [&](auto *qt) {
+        hipLaunchKernelGGL((k_lora_rows<elem_of<decltype(pt)>, elem_of<decltype(qt)>>), grid,
+                           dim3(256), 0, stream, P, M, C, Q, ldq_j, ldq_c, r, slice, partial);
+      });
+    });
   }
   QL_HIP_CHECK_LAUNCH();
   if (slices) *slices = S;
@@ -412,12 +412,12 @@ __global__ __launch_bounds__(256) void k_lora_cols(const float *__restrict__ R, 
 }
 
 // ---------------------------------------------------------------------------
-// cols on the matrix cores (bf16 P): D[j][c] = sum_m R^T[j][m] P[m][c] with
-// v_mfma_f32_16x16x32_bf16.  The workgroup owns 64 columns (wave w: columns
+// cols on the matrix cores (16-bit P): D[j][c] = sum_m R^T[j][m] P[m][c] with
+// v_mfma_f32_16x16x32_{bf16,f16}.  The workgroup owns 64 columns (wave w: columns
 // 16w..16w+15, all JT rank tiles) and one TM-token slice, in one round trip
 // with compile-time trip counts: the loads of R (fp32, 4 ranks per load when
 // r % 4 == 0) and of the P tile (16 bytes per lane) are all issued first,
-// then R^T is written to LDS as bf16 [j][m] and the P tile as [m][c]
+// then R^T is written to LDS in P's format [j][m] and the P tile as [m][c]
 // (128-byte rows), one barrier, the MFMAs, and the fp32 partial sums.  The
 // B operand (8 consecutive tokens of one column) comes from gfx950's
 // transposing LDS read: for a group of 16 lanes naming rows m0..m0+3
@@ -443,11 +443,12 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// DROP: P is the activation x of the LoRA dropout; its dropped elements
-// are zeroed as loaded (the 1/(1-p) scale is applied by the reduction).
-template <int TM, int JT, bool RVEC, bool DROP>
+// AT: the 16-bit format of P and of the matrix-core operands.  DROP: P is
+// the activation x of the LoRA dropout; its dropped elements are zeroed as
+// loaded (the 1/(1-p) scale is applied by the reduction).
+template <int TM, int JT, typename AT, bool RVEC, bool DROP>
 __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
-                                                   int32_t r, const uint16_t *__restrict__ P,
+                                                   int32_t r, const AT *__restrict__ P,
                                                    int64_t C, float *__restrict__ partial,
                                                    Dropout dr) {
   constexpr int JW = JT * 16;
@@ -505,13 +506,13 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         *reinterpret_cast<uint16_t *>(rs + (4 * j4 + jj) * RST + 2 * mm) =
-            f32_to_bf16_bits(ok ? rv[b][jj] : 0.0f);
+            Half<AT>::bits(ok ? rv[b][jj] : 0.0f);
     }
   } else {
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
       const int e = t + 256 * b, mm = e / JW, j = e % JW;
-      *reinterpret_cast<uint16_t *>(rs + j * RST + 2 * mm) = f32_to_bf16_bits(re[b]);
+      *reinterpret_cast<uint16_t *>(rs + j * RST + 2 * mm) = Half<AT>::bits(re[b]);
     }
   }
 #pragma unroll
@@ -536,9 +537,7 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
     for (int jt = 0; jt < JT; ++jt) {
       const u32x4 a =
           *reinterpret_cast<const u32x4 *>(rs + (16 * jt + li) * RST + 2 * (kk + 8 * q));
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, b), acc[jt],
-                                                        0, 0, 0);
+      acc[jt] = Half<AT>::mfma16(a, b, acc[jt]);
     }
   }
   const int64_t c = ct0 + 16 * wave + li;
@@ -593,7 +592,7 @@ static int cols_slices(int64_t M, int64_t C) {
 // Token slices of the matrix-core cols kernel: one per TM tokens.
 static int mcols_slices(int64_t M) { return (int)((M + kMColsTM - 1) / kMColsTM); }
 
-static bool cols_use_mfma(int p_dtype, int64_t C) { return p_dtype == QL_BF16 && C % 8 == 0; }
+static bool cols_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
 
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
   const int64_t s1 = cols_slices(M, C), s2 = mcols_slices(M);
@@ -611,31 +610,32 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
     S = mcols_slices(M);
     const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
     const bool rvec = r % 4 == 0;
-#define QL_COLS_M(JTV, RV, DRV)                                                                  \
-  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, RV, DRV>), grid, dim3(256), 0, stream, R, M, r, \
-                     (const uint16_t *)P, C, partial, dr)
+#define QL_COLS_M(JTV, RV, DRV)                                                               \
+  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, AT, RV, DRV>), grid, dim3(256), 0, stream, R, \
+                     M, r, (const AT *)P, C, partial, dr)
 #define QL_COLS_JT(JTV)                                                                          \
   do {                                                                                           \
     if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \
     else { if (drop) QL_COLS_M(JTV, false, true); else QL_COLS_M(JTV, false, false); }           \
   } while (0)
     const int jt = rows_jt(r);
-    if (jt == 1) QL_COLS_JT(1);
-    else if (jt == 2) QL_COLS_JT(2);
-    else if (jt == 4) QL_COLS_JT(4);
-    else QL_COLS_JT(8);
+    with_half(p_dtype, [&](auto *tag) {
+      using AT = elem_of<decltype(tag)>;
+      if (jt == 1) QL_COLS_JT(1);
+      else if (jt == 2) QL_COLS_JT(2);
+      else if (jt == 4) QL_COLS_JT(4);
+      else QL_COLS_JT(8);
+    });
 #undef QL_COLS_JT
 #undef QL_COLS_M
   } else {
     S = cols_slices(M, C);
     const int64_t slice = (M + S - 1) / S;
     const dim3 grid((unsigned)((C + kColsTC - 1) / kColsTC), (unsigned)S);
-    if (p_dtype == QL_BF16)
-      hipLaunchKernelGGL(k_lora_cols<uint16_t>, grid, dim3(256), 0, stream, R, M, r, P, C, slice,
-                         partial);
-    else
-      hipLaunchKernelGGL(k_lora_cols<float>, grid, dim3(256), 0, stream, R, M, r, P, C, slice,
-                         partial);
+    with_type(p_dtype, [&](auto *pt) {
+      hipLaunchKernelGGL((k_lora_cols<elem_of<decltype(pt)>>), grid, dim3(256), 0, stream, R, M,
+                         r, P, C, slice, partial);
+    });
   }
   QL_HIP_CHECK_LAUNCH();
   const int64_t count = (int64_t)r * C;

@@ -142,12 +142,12 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, i
     if (n < 8) {  // uniform: too short for any 8-element load
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
-    } else if constexpr (sizeof(T) == 2) {
+    } else if constexpr (sizeof(T) == 2) {  // bf16 or fp16: widening is exact
       const u32x4 raw = *reinterpret_cast<const u32x4 *>(w + ec);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[j][2 * i] = __uint_as_float(raw[i] << 16);
-        v[j][2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+        v[j][2 * i] = Half<T>::lo(raw[i]);
+        v[j][2 * i + 1] = Half<T>::hi(raw[i]);
       }
     } else {
       const f32x4 a = *reinterpret_cast<const f32x4 *>(w + ec);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void k_dq_codes(const float *__restrict__ a, i
 }
 
 // ---------------------------------------------------------------------------
-// K4: dequantisation.  Every store is 16 bytes per lane (E = 8 bf16 or 4
+// K4: dequantisation.  Every store is 16 bytes per lane (E = 8 bf16 / fp16 or 4
 // fp32 elements) and every wave instruction covers one contiguous span: a
 // wave owns 4 x 64 x E consecutive elements and lane l takes elements
 // l E .. l E + E - 1 of each of its 4 runs of 64 E.  The E / 2 packed bytes
@@ -356,8 +356,8 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t *__restric
       }
       if constexpr (E == 8) {
         *reinterpret_cast<u32x4 *>(out + e[i]) =
-            u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                  pack_bf16x2(o[6], o[7])};
+            u32x4{Half<OutT>::pack2(o[0], o[1]), Half<OutT>::pack2(o[2], o[3]),
+                  Half<OutT>::pack2(o[4], o[5]), Half<OutT>::pack2(o[6], o[7])};
       } else {
         *reinterpret_cast<f32x4 *>(out + e[i]) = f32x4{o[0], o[1], o[2], o[3]};
       }
@@ -387,6 +387,8 @@ int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_
                      packed, absmax, th)
   if (w_dtype == QL_BF16) {
     if (block == 128) QL_QUANT(uint16_t, 128); else QL_QUANT(uint16_t, 64);
+  } else if (w_dtype == QL_F16) {
+    if (block == 128) QL_QUANT(_Float16, 128); else QL_QUANT(_Float16, 64);
   } else {
     if (block == 128) QL_QUANT(float, 128); else QL_QUANT(float, 64);
   }
@@ -413,13 +415,16 @@ int launch_double_quant(const float *absmax, int64_t nb, double *partial, int8_t
 int launch_nf4_dequantize(const uint8_t *packed, int64_t n, BlockScales sc, void *out,
                           int out_dtype, hipStream_t stream) {
   if (n <= 0) return QL_OK;
-  // one wave per 4 x 64 x E elements (E = 8 for bf16, 4 for fp32 output)
-  const int64_t per_wave = out_dtype == QL_BF16 ? 2048 : 1024;
+  // one wave per 4 x 64 x E elements (E = 8 for 16-bit, 4 for fp32 output)
+  const int64_t per_wave = out_dtype == QL_F32 ? 1024 : 2048;
   const int64_t waves = (n + per_wave - 1) / per_wave;
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (out_dtype == QL_BF16)
     hipLaunchKernelGGL(k_nf4_dequantize<uint16_t>, grid, dim3(256), 0, stream, packed, n, sc,
                        (uint16_t *)out);
+  else if (out_dtype == QL_F16)
+    hipLaunchKernelGGL(k_nf4_dequantize<_Float16>, grid, dim3(256), 0, stream, packed, n, sc,
+                       (_Float16 *)out);
   else
     hipLaunchKernelGGL(k_nf4_dequantize<float>, grid, dim3(256), 0, stream, packed, n, sc,
                        (float *)out);

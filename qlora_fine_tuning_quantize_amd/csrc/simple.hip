@@ -162,24 +162,16 @@ __global__ __launch_bounds__(256) void k_simple_dx(const void *__restrict__ dy, 
   }
 }
 
-#define QL_DISPATCH2(act, lora, KERNEL, ...)                                              \
-  do {                                                                                    \
-    if ((act) == QL_BF16 && (lora) == QL_BF16)                                            \
-      hipLaunchKernelGGL((KERNEL<uint16_t, uint16_t>), __VA_ARGS__);                      \
-    else if ((act) == QL_BF16)                                                            \
-      hipLaunchKernelGGL((KERNEL<uint16_t, float>), __VA_ARGS__);                         \
-    else if ((lora) == QL_BF16)                                                           \
-      hipLaunchKernelGGL((KERNEL<float, uint16_t>), __VA_ARGS__);                         \
-    else                                                                                  \
-      hipLaunchKernelGGL((KERNEL<float, float>), __VA_ARGS__);                            \
-  } while (0)
-
 int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                       BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,
                       int lora_dtype, int32_t r, float s, void *y, hipStream_t stream) {
   const dim3 grid((unsigned)((N + kT - 1) / kT), (unsigned)((M + kT - 1) / kT));
-  QL_DISPATCH2(act_dtype, lora_dtype, k_simple_fwd, grid, dim3(256), 0, stream, x, M, packed, sc,
-               N, K, u, B, r, s, y);
+  with_type(act_dtype, [&](auto *at) {
+    with_type(lora_dtype, [&](auto *lt) {
+      hipLaunchKernelGGL((k_simple_fwd<elem_of<decltype(at)>, elem_of<decltype(lt)>>), grid,
+                         dim3(256), 0, stream, x, M, packed, sc, N, K, u, B, r, s, y);
+    });
+  });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }
@@ -188,8 +180,12 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
                      int lora_dtype, int32_t r, void *dx, hipStream_t stream) {
   const dim3 grid((unsigned)(K / kT), (unsigned)((M + kT - 1) / kT));
-  QL_DISPATCH2(act_dtype, lora_dtype, k_simple_dx, grid, dim3(256), 0, stream, dy, M, packed, sc,
-               N, K, g, A, r, dx);
+  with_type(act_dtype, [&](auto *at) {
+    with_type(lora_dtype, [&](auto *lt) {
+      hipLaunchKernelGGL((k_simple_dx<elem_of<decltype(at)>, elem_of<decltype(lt)>>), grid,
+                         dim3(256), 0, stream, dy, M, packed, sc, N, K, g, A, r, dx);
+    });
+  });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

@@ -10,7 +10,8 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """Host numpy view of a tensor; bf16 becomes uint16 bit patterns."""
+    """Host numpy view of a tensor; bf16 becomes uint16 bit patterns (fp16
+    stays numpy float16)."""
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
     return t.contiguous().cpu().numpy()
@@ -26,6 +27,7 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 BF16_TOL = 2e-2        # bf16 activations: max rel error against the fp64 oracle
+F16_TOL = 2.5e-3       # fp16 activations: BF16_TOL x 2^-11 / 2^-8 (the unit roundoff ratio)
 F32_ATOL = 1e-5        # fp32 activations: |d| <= atol + rtol |ref| (allclose defaults)
 F32_RTOL = 1e-5
 

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 104
+    assert L.ql_abi_version() == 105
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -111,6 +111,9 @@ def test_quantize_rejects_bad_buffers():
     d = _desc()
     assert L.nf4_quantize(None, b.QL_BF16, ctypes.byref(d), None, 0, None) == b.QL_EINVAL
     assert L.nf4_quantize(ctypes.c_void_p(FAKE), 5, ctypes.byref(d), None, 0, None) == b.QL_EINVAL
+    assert L.nf4_quantize(ctypes.c_void_p(FAKE + 2), b.QL_F16, ctypes.byref(d), None, 0,
+                          None) == b.QL_EALIGN  # fp16 weights are accepted up to alignment
+    assert L.nf4_dequantize(ctypes.byref(d), ctypes.c_void_p(FAKE), 3, None) == b.QL_EINVAL
     assert L.nf4_quantize(ctypes.c_void_p(FAKE + 2), b.QL_BF16, ctypes.byref(d), None, 0,
                           None) == b.QL_EALIGN
     d1 = _desc(dq=1)
@@ -136,6 +139,12 @@ def test_linear_fwd_rejects_bad_arguments():
     assert _fwd(L, r=129) == b.QL_EUNSUPPORTED
     assert _fwd(L, act=3) == b.QL_EINVAL
     assert _fwd(L, lora=9) == b.QL_EINVAL
+    # a 16-bit LoRA dtype must match 16-bit activations (fp16 compute with
+    # bf16 factors, or the reverse, is not a combination the layer runs)
+    assert _fwd(L, act=b.QL_F16, lora=b.QL_BF16) == b.QL_EUNSUPPORTED
+    assert _fwd(L, act=b.QL_BF16, lora=b.QL_F16) == b.QL_EUNSUPPORTED
+    assert _fwd(L, act=b.QL_F16, lora=b.QL_F16, M=0) == b.QL_EINVAL  # fp16 itself is accepted
+    assert _fwd(L, act=b.QL_F16, lora=b.QL_F32, ws=0) == b.QL_EWORKSPACE
     assert _fwd(L, alpha=float("inf")) == b.QL_EINVAL
     assert _fwd(L, alpha=float("nan")) == b.QL_EINVAL
     assert _fwd(L, x=0) == b.QL_EINVAL
@@ -241,7 +250,7 @@ def test_dropout_entry_points_reject_bad_arguments():
         assert fwd(p=p) == b.QL_EINVAL
         assert bwd(p=p) == b.QL_EINVAL
         assert L.ql_dropout_mask(4, 4, p, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
-    assert fwd(act=b.QL_F32) == b.QL_EUNSUPPORTED   # dropout runs on the bf16 path only
+    assert fwd(act=b.QL_F32) == b.QL_EUNSUPPORTED   # dropout runs on the 16-bit paths only
     assert fwd(M=0) == b.QL_EINVAL
     assert fwd(ws_bytes=255) == b.QL_EWORKSPACE
     assert bwd(act=b.QL_F32) == b.QL_EUNSUPPORTED

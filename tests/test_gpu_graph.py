@@ -13,20 +13,24 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("M,N,K,r,dropout,block", [
-    (300, 384, 640, 16, 0.0, 64),   # 256-token GEMMs
-    (8, 256, 512, 8, 0.0, 64),      # decode GEMV forward
-    (64, 256, 1024, 16, 0.0, 64),   # 64-token forward tiles with split-K
-    (300, 384, 640, 16, 0.1, 64),   # LoRA dropout, forward and backward
-    (64, 256, 1024, 16, 0.0, 128),  # blocks of 128
+@pytest.mark.parametrize("M,N,K,r,dropout,block,act", [
+    (300, 384, 640, 16, 0.0, 64, torch.bfloat16),   # 256-token GEMMs
+    (8, 256, 512, 8, 0.0, 64, torch.bfloat16),      # decode GEMV forward
+    (64, 256, 1024, 16, 0.0, 64, torch.bfloat16),   # 64-token forward tiles with split-K
+    (300, 384, 640, 16, 0.1, 64, torch.bfloat16),   # LoRA dropout, forward and backward
+    (64, 256, 1024, 16, 0.0, 128, torch.bfloat16),  # blocks of 128
+    (300, 384, 640, 16, 0.1, 64, torch.float16),    # fp16 compute with dropout
+    (8, 256, 512, 8, 0.0, 64, torch.float16),       # fp16 decode GEMV
 ])
-def test_graph_replay_matches_eager(M, N, K, r, dropout, block):
-    print(f"graph replay M={M} N={N} K={K} r={r} dropout={dropout} block={block}", flush=True)
-    t = {k: v.to(DEV) for k, v in si.linear_inputs(92, M, N, K, r, sub=M).items()}
+def test_graph_replay_matches_eager(M, N, K, r, dropout, block, act):
+    print(f"graph replay M={M} N={N} K={K} r={r} dropout={dropout} block={block} act={act}",
+          flush=True)
+    t = {k: v.to(DEV) for k, v in si.linear_inputs(92, M, N, K, r, act_dtype=act, w_dtype=act,
+                                                   lora_dtype=act, sub=M).items()}
     W = q.nf4_quantize(t["W"], double_quant=True, block=block)
-    bufs = dict(y=torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
+    bufs = dict(y=torch.empty((M, N), dtype=act, device=DEV),
                 u=torch.empty((M, r), dtype=torch.float32, device=DEV),
-                dx=torch.empty((M, K), dtype=torch.bfloat16, device=DEV),
+                dx=torch.empty((M, K), dtype=act, device=DEV),
                 dA=torch.empty((r, K), dtype=torch.float32, device=DEV),
                 dB=torch.empty((N, r), dtype=torch.float32, device=DEV))
     wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, DEV)
@@ -56,7 +60,7 @@ def test_graph_replay_matches_eager(M, N, K, r, dropout, block):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    other = torch.randn((M, K), device=DEV).to(torch.bfloat16)
+    other = torch.randn((M, K), device=DEV).to(act)
     for rep in range(3):
         for v in bufs.values():
             v.fill_(float("nan"))
