@@ -192,10 +192,13 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
  *     y = x W^^T + s u B^T,   s = fp32(alpha / r)
  *   u       device [M, r] fp32, 16-byte aligned
  * Other arguments as for qlora_linear_fwd; no workspace.  With 16-bit
- * activations this is a single matrix-core launch, bit-identical to the
- * y of qlora_linear_fwd for M > 16 (for M <= 16 qlora_linear_fwd takes the
- * single-launch decode path, which rounds u to 16 bits in registers instead
- * of reading it, so the two agree to within 16-bit rounding).
+ * activations this is a single matrix-core launch that never splits the
+ * contraction.  It is bit-identical to the y of qlora_linear_fwd for M > 16
+ * whenever that call does not split the contraction either; where it does
+ * (a shape-dependent choice: few output tiles, or tiles that fill the chip
+ * better when split), or for M <= 16 (the single-launch decode path, which
+ * rounds u to 16 bits in registers instead of reading it), the two agree to
+ * within 16-bit rounding.
  * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
  */
 int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,

@@ -880,26 +880,16 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
                            (BM == 256 ? &ds[0][0] : &wt[0][0]) + wave * 32 * (2 * TX + 16), lane);
 }
 
-// Output tile width: 256 when that still gives at least ~1.5 workgroups per
-// compute unit, else 128.
-static int pick_width(int64_t M, int64_t cols, int64_t divisor_ok) {
-  const int64_t mt = (M + kBM - 1) / kBM;
-  const int64_t tiles256 = mt * ((cols + 255) / 256);
-  if (divisor_ok && tiles256 >= 384) return 256;
-  return 128;
-}
-
 // Split-K: a launch with fewer tiles than the chip runs at once (a few
 // token tiles) leaves units idle while each workgroup walks the whole
 // contraction.  Its contraction is then split into S slices (grid rows) that
-// write fp32 partial tiles, summed in fixed order by k_reduce_split.  S
-// minimises (waves of `slots` workgroups: 256 for the 256-token kernels, one
-// per compute unit; 512 for the few-token forward, which runs up to four per
-// unit but gains little past two) x (steps per slice + ~4 steps of prologue
-// and epilogue), keeps >= 8 steps per slice
-// and the partial buffer <= 64 MB, and prefers the smaller S on ties; it
+// write fp32 partial tiles, summed in fixed order by k_reduce_split.  For the
+// few-token kernels S minimises (waves of `slots` workgroups: 512 for them,
+// as they run up to four per unit but gain little past two) x (steps per
+// slice + ~4 steps of prologue and epilogue), keeps >= 8 steps per slice and
+// the partial buffer <= 64 MB, and prefers the smaller S on ties; it
 // depends only on the shape.
-static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols, int64_t slots = 256) {
+static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols, int64_t slots) {
   if (tiles >= slots || tiles <= 0 || cols % 4 != 0) return 1;
   int64_t smax = steps / 8;
   if (smax > 16) smax = 16;
@@ -919,26 +909,70 @@ static int split_count(int64_t tiles, int64_t steps, int64_t M, int64_t cols, in
   return best;
 }
 
+// Plan of a 256-token launch: output tile width bn (256, or 128) and
+// split-K count S, from a cost model in units of one contraction step of a
+// 256 x 256 tile:
+//     waves(tiles(bn) S / 256) (steps / S  c(bn) + 4)
+//   + [S > 1] 8 M cols S / kPartialBytesPerStep
+// c(256) = 1 and c(128) = 0.62 are the measured per-step times of the two
+// tiles relative to each other (1.9 and 1.2 us on the 8B MLP shapes: the
+// wider tile does twice the work per step for 1.6x the time); the second
+// term is the fp32 partial tiles of a split launch, written and read back
+// (8 bytes per output per slice), at ~7.7 MB per step unit (~4 TB/s over a
+// 1.9 us step).  Slices keep >= 8 steps each and the partial buffer stays
+// <= 256 MB.  The smallest cost wins; ties go to the wider tile and the
+// smaller S.  It depends only on the shape (and on whether splitting is
+// allowed), so the workspace query and the launch agree.
+struct TilePlan {
+  int bn, S;
+};
+constexpr double kPartialBytesPerStep = 7.7e6;
+
+static TilePlan plan_tiles(int64_t M, int64_t cols, int64_t steps, bool wide_ok, bool split_ok) {
+  const int64_t mt = (M + kBM - 1) / kBM;
+  TilePlan best{128, 1};
+  double best_cost = 1e300;
+  for (int bn = 256; bn >= 128; bn -= 128) {
+    if (bn == 256 && !wide_ok) continue;
+    const double c = bn == 256 ? 1.0 : 0.62;
+    const int64_t tiles = mt * ((cols + bn - 1) / bn);
+    int64_t smax = (split_ok && cols % 4 == 0) ? steps / 8 : 1;
+    if (smax > 16) smax = 16;
+    const int64_t per = M * cols * 4;
+    const int64_t cap = (int64_t)256 << 20;
+    if (per > 0 && smax > cap / per) smax = cap / per;
+    if (smax < 1) smax = 1;
+    for (int64_t S = 1; S <= smax; ++S) {
+      const double waves = (double)((tiles * S + 255) / 256);
+      double cost = waves * ((double)steps / (double)S * c + 4.0);
+      if (S > 1) cost += 8.0 * (double)M * (double)cols * (double)S / kPartialBytesPerStep;
+      if (cost < best_cost * (1.0 - 1e-9)) {
+        best_cost = cost;
+        best = TilePlan{bn, (int)S};
+      }
+    }
+  }
+  return best;
+}
+
 // Forward tile: 64 tokens x 128 outputs (k_gemm_fwd_small) up to kFwdSmallM
-// tokens, else 256 tokens x pick_width outputs (measured on the 8B MLP
+// tokens, else 256 tokens x the planned width (measured on the 8B MLP
 // shapes: the small tile is faster up to 128 tokens, slower at 256).
 constexpr int64_t kFwdSmallM = 128;
 
 static int fwd_split(int64_t M, int64_t N, int64_t K) {
   if (M <= kFwdSmallM)
     return split_count(((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN), K >> 6, M, N, 512);
-  const int bn = pick_width(M, N, 1);
-  return split_count(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn), K >> 6, M, N);
+  return plan_tiles(M, N, K >> 6, true, true).S;
 }
 
 // Input-gradient tile: 64 tokens x 128 columns up to kDxSmallM tokens, else
-// 256 tokens x pick_width columns.
+// 256 tokens x the planned width (256 needs K % 256 == 0).
 constexpr int64_t kDxSmallM = 128;
 
 static int dx_split(int64_t M, int64_t N, int64_t K) {
   if (M <= kDxSmallM) return split_count(((M + 63) / 64) * (K / 128), N / kDxBC, M, K, 512);
-  const int bx = pick_width(M, K, K % 256 == 0);
-  return split_count(((M + kBM - 1) / kBM) * (K / bx), N / kDxBC, M, K);
+  return plan_tiles(M, K, N / kDxBC, K % 256 == 0, true).S;
 }
 
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K) {
@@ -991,9 +1025,9 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
     if (S > 1) return reduce_split(act_dtype, part, S, M * N, y, stream);
     return QL_OK;
   }
-  const int bn = pick_width(M, N, 1);
+  const TilePlan pl = plan_tiles(M, N, K >> 6, true, part != nullptr);
+  const int bn = pl.bn, S = pl.S;
   const int64_t G = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
-  const int S = part ? fwd_split(M, N, K) : 1;
 #define QL_FWD(BNV, LT, DQV)                                                                     \
   hipLaunchKernelGGL((k_gemm_fwd<BNV, AT, LT, DQV>), dim3((unsigned)G, (unsigned)S),            \
                      dim3(kThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s,  \
@@ -1028,9 +1062,10 @@ int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *pac
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const bool small = M <= kDxSmallM;
   const int bm = small ? 64 : kBM;
-  const int bx = small ? 128 : pick_width(M, K, K % 256 == 0);
+  const TilePlan pl = small ? TilePlan{128, part ? dx_split(M, N, K) : 1}
+                            : plan_tiles(M, K, N / kDxBC, K % 256 == 0, part != nullptr);
+  const int bx = pl.bn, S = pl.S;
   const int64_t G = ((M + bm - 1) / bm) * (K / bx);
-  const int S = part ? dx_split(M, N, K) : 1;
   const bool dq = sc.absmax == nullptr;
 #define QL_DX(BMV, BXV, LT, DQV, DRV)                                                            \
   hipLaunchKernelGGL((k_gemm_dx<BMV, BXV, AT, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),   \

@@ -403,12 +403,12 @@ def test_mlp8b_config_full_size_sampled(orc, proj):
         assert e <= BF16_TOL, (k, e)
 
 
-@pytest.mark.parametrize("M", [128, 512])
+@pytest.mark.parametrize("M", [128, 512, 1024])
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_mlp8b_shape_few_tokens_sampled(orc, proj, M):
-    """8B-shaped MLP projection at 128 and 512 tokens (the split-K launches:
-    too few token tiles to fill the chip unsplit): y and dx on 32 sampled
-    token rows, dA and dB in full."""
+    """8B-shaped MLP projection at 128, 512 and 1024 tokens (the split-K
+    launches, and at 1024 the 256-wide tiles with and without split-K): y
+    and dx on 32 sampled token rows, dA and dB in full."""
     c = si.MLP_8B
     N, K = c["projs"][proj]
     r = c["r"]
