@@ -212,8 +212,11 @@ def main():
 
     # ---------------- every row of the path, per projection -------------------
     # Each row is timed through the entry points alone (HIP events, 30 calls):
-    #   a5 forward GEMM      = qlora_linear_fwd_u (one launch)
-    #   a4 u = x A^T         = qlora_linear_fwd - qlora_linear_fwd_u
+    #   a4 u = x A^T         = qlora_linear_bwd(u recomputed, dx = NULL)
+    #                          - qlora_linear_bwd(u_saved, dx = NULL)
+    #                          (the same u kernels as the forward's)
+    #   a5 forward GEMM      = qlora_linear_fwd - a4 (the GEMM launches, with
+    #                          its split-K sum where the shape splits)
     #   a6 LoRA gradients    = qlora_linear_bwd(u_saved, dx = NULL)   (g, dB, dA)
     #   a7 input gradient    = qlora_linear_bwd(u_saved) - the above
     # against MFMA peak (a5, a7) or HBM peak (a4, a6: bytes of x / dy read).
@@ -222,20 +225,22 @@ def main():
         N, K = p["N"], p["K"]
         t_fwd = timed(lambda: q.qlora_linear_fwd(p["x"], p["W"], p["A"], p["B"], alpha, y=p["y"],
                                                  u_save=p["u"], ws=p["wsf"]), 30, 3)
-        t_fwdu = timed(lambda: q.qlora_linear_fwd_u(p["x"], p["W"], p["u"], p["B"], alpha,
-                                                    y=p["y"]), 30, 3)
         t_bwd = timed(lambda: q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha,
                                                  u_saved=p["u"], dx=p["dx"], dA=p["dA"],
                                                  dB=p["dB"], ws=p["wsb"]), 30, 3)
         t_lora = timed(lambda: q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"], alpha,
                                                   u_saved=p["u"], need_dx=False, dA=p["dA"],
                                                   dB=p["dB"], ws=p["wsb"]), 30, 3)
+        t_lora_u = timed(lambda: q.qlora_linear_bwd(p["dy"], p["x"], p["W"], p["A"], p["B"],
+                                                    alpha, need_dx=False, dA=p["dA"], dB=p["dB"],
+                                                    ws=p["wsb"]), 30, 3)
+        t_u = t_lora_u - t_lora
         a5 = 2 * M * N * K + 2 * M * r * N
         a7 = 2 * M * N * K + 2 * M * r * K
         by_x, by_dy = M * K * 2, M * N * 2
         rec = {
-            "a4_u": {"us": round((t_fwd - t_fwdu) * 1e3, 2), "bytes": by_x},
-            "a5_fwd_gemm": {"us": round(t_fwdu * 1e3, 2), "flop": a5},
+            "a4_u": {"us": round(t_u * 1e3, 2), "bytes": by_x},
+            "a5_fwd_gemm": {"us": round((t_fwd - t_u) * 1e3, 2), "flop": a5},
             "a6_lora_grads": {"us": round(t_lora * 1e3, 2), "bytes": by_x + 2 * by_dy},
             "a7_dx_gemm": {"us": round((t_bwd - t_lora) * 1e3, 2), "flop": a7},
         }
