@@ -446,11 +446,21 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
 // AT: the 16-bit format of P and of the matrix-core operands.  DROP: P is
 // the activation x of the LoRA dropout; its dropped elements are zeroed as
 // loaded (the 1/(1-p) scale is applied by the reduction).
+// ColsOut: with a single token slice (gridDim.y == 1) the workgroup writes
+// the finished result itself, with the arithmetic of k_reduce_cols for one
+// slice (out = scale * (0 + sum), or out += that, [r][C] or transposed);
+// otherwise out is NULL and the slice's partial sums go to `partial`.
+struct ColsOut {
+  float *out;
+  float scale;
+  int c_major, accumulate;
+};
+
 template <int TM, int JT, typename AT, bool RVEC, bool DROP>
 __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
                                                    int32_t r, const AT *__restrict__ P,
                                                    int64_t C, float *__restrict__ partial,
-                                                   Dropout dr) {
+                                                   Dropout dr, ColsOut co) {
   constexpr int JW = JT * 16;
   constexpr int RST = 2 * TM + 16;  // bytes per staged rank row
   __shared__ __attribute__((aligned(16))) uint8_t ps[TM * 128];
@@ -547,7 +557,15 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * jt + 4 * q + v;
-        if (j < r) partial[((int64_t)blockIdx.y * r + j) * C + c] = acc[jt][v];
+        if (j >= r) continue;
+        if (co.out) {
+#pragma clang fp contract(off)
+          const float sum = 0.0f + acc[jt][v];  // k_reduce_cols' sum over one slice
+          const int64_t o = co.c_major ? c * r + j : (int64_t)j * C + c;
+          co.out[o] = co.accumulate ? co.out[o] + co.scale * sum : co.scale * sum;
+        } else {
+          partial[((int64_t)blockIdx.y * r + j) * C + c] = acc[jt][v];
+        }
       }
     }
   }
@@ -609,10 +627,12 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   if (cols_use_mfma(p_dtype, C)) {
     S = mcols_slices(M);
     const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
+    // one token slice: the kernel writes the result, no reduction launch
+    const ColsOut co{S == 1 ? out : nullptr, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0};
     const bool rvec = r % 4 == 0;
 #define QL_COLS_M(JTV, RV, DRV)                                                               \
   hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, AT, RV, DRV>), grid, dim3(256), 0, stream, R, \
-                     M, r, (const AT *)P, C, partial, dr)
+                     M, r, (const AT *)P, C, partial, dr, co)
 #define QL_COLS_JT(JTV)                                                                          \
   do {                                                                                           \
     if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \
@@ -628,6 +648,8 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
     });
 #undef QL_COLS_JT
 #undef QL_COLS_M
+    QL_HIP_CHECK_LAUNCH();
+    if (S == 1) return QL_OK;
   } else {
     S = cols_slices(M, C);
     const int64_t slice = (M + S - 1) / S;
