@@ -79,8 +79,10 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   return w;
 }
 
+// dB's and dA's slice partials have regions of their own (cols, cols2): their
+// two reductions run as one launch after both products.
 struct BwdWs {
-  size_t u, g, rows, cols, total;
+  size_t u, g, rows, cols, cols2, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w;
@@ -91,10 +93,8 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   size_t rows_f2 = lora_rows_partial_floats(M, N, r);
   if (rows_f2 > rows_f) rows_f = rows_f2;
   w.cols = w.rows + round_up(rows_f * 4);
-  size_t cols_f = lora_cols_partial_floats(M, K, r);
-  size_t cols_f2 = lora_cols_partial_floats(M, N, r);
-  if (cols_f2 > cols_f) cols_f = cols_f2;
-  w.total = w.cols + round_up(cols_f * 4);
+  w.cols2 = w.cols + round_up(lora_cols_partial_floats(M, N, r) * 4);
+  w.total = w.cols2 + round_up(lora_cols_partial_floats(M, K, r) * 4);
   if (gemm_dx_supported(N, K)) {
     const size_t gemm_end = w.rows + round_up(gemm_dx_partial_floats(M, N, K) * 4);
     if (gemm_end > w.total) w.total = gemm_end;
@@ -311,6 +311,7 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   float *g = (float *)(base + L.g);
   float *rows_partial = (float *)(base + L.rows);
   float *cols_partial = (float *)(base + L.cols);
+  float *cols_partial2 = (float *)(base + L.cols2);
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
@@ -325,11 +326,15 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   st = launch_lora_rows_ws(dy, act_dtype, M, N, B, lora_dtype, 1, r, r, sc_lora, g, rows_partial, s);
   if (st) return st;
   // dB[n][j] = s sum_m dy[m][n] u[m][j]
-  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s, accumulate);
+  ColsReduce red_dB, red_dA;
+  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s, accumulate,
+                        nullptr, &red_dB);
   if (st) return st;
   // dA[j][k] = sum_m g[m][j] x[m][k] (x after dropout: keep / (1 - p) times x)
-  st = launch_lora_cols(g, M, r, x, act_dtype, K, drop ? dscale : 1.0f, false, dA, cols_partial, s,
-                        accumulate, drop);
+  st = launch_lora_cols(g, M, r, x, act_dtype, K, drop ? dscale : 1.0f, false, dA, cols_partial2,
+                        s, accumulate, drop, &red_dA);
+  if (st) return st;
+  st = launch_reduce_cols(red_dB, red_dA, s);
   if (st) return st;
   if (!dx) return QL_OK;
   if (act_dtype != QL_F32 && gemm_dx_supported(N, K))

@@ -30,11 +30,27 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
                         float *out, float *partial, hipStream_t stream, int *slices = nullptr,
                         const Dropout *drop = nullptr);
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r);
-// accumulate: out += result instead of out = result
+// A fixed-order sum of cols partial slices still to be launched (S == 0:
+// none needed): out = scale * sum over S slices, [r][C] or transposed, or
+// added into out (accumulate).
+struct ColsReduce {
+  const float *partial;
+  int S;
+  int32_t r;
+  int64_t C;
+  float scale;
+  int c_major, accumulate;
+  float *out;
+};
+// accumulate: out += result instead of out = result.  pending: if non-NULL,
+// the slice reduction (when one is needed) is not launched but described
+// there, for launch_reduce_cols.
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
                      hipStream_t stream, bool accumulate = false,
-                     const Dropout *drop = nullptr);
+                     const Dropout *drop = nullptr, ColsReduce *pending = nullptr);
+// one launch for up to two pending reductions (empty ones are skipped)
+int launch_reduce_cols(const ColsReduce &a, const ColsReduce &b, hipStream_t stream);
 
 // simple.hip: fp32-accumulating tiled kernels for any activation dtype.
 int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,

@@ -573,28 +573,45 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
 
 // out = scale * sum_s partial[s][j][c] (s in increasing order, 8 slices per
 // batch loaded before they are added); written as [r][C] or transposed [C][r],
-// or added to what out holds (accumulate != 0, one fp32 addition).
-__global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ partial, int S,
-                                                     int32_t r, int64_t C, float scale,
-                                                     int c_major, int accumulate,
-                                                     float *__restrict__ out) {
+// or added to what out holds (accumulate != 0, one fp32 addition).  One
+// launch serves one or two such sums (jobs a and b, b empty when b.S == 0):
+// blocks [0, blocks(a)) take a, the rest b.
+__device__ __forceinline__ void reduce_cols_one(const ColsReduce &jb, int64_t e) {
   // accumulation is the product scale * s, rounded, then one addition
 #pragma clang fp contract(off)
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t count = (int64_t)r * C;
+  const int64_t count = (int64_t)jb.r * jb.C;
   if (e >= count) return;
   float s = 0.0f;
-  for (int i0 = 0; i0 < S; i0 += 8) {
+  for (int i0 = 0; i0 < jb.S; i0 += 8) {
     float v[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) v[b] = i0 + b < S ? partial[(int64_t)(i0 + b) * count + e] : 0.0f;
+    for (int b = 0; b < 8; ++b)
+      v[b] = i0 + b < jb.S ? jb.partial[(int64_t)(i0 + b) * count + e] : 0.0f;
 #pragma unroll
     for (int b = 0; b < 8; ++b)
-      if (i0 + b < S) s += v[b];
+      if (i0 + b < jb.S) s += v[b];
   }
-  const int64_t j = e / C, c = e % C;
-  const int64_t o = c_major ? c * r + j : e;
-  out[o] = accumulate ? out[o] + scale * s : scale * s;
+  const int64_t j = e / jb.C, c = e % jb.C;
+  const int64_t o = jb.c_major ? c * jb.r + j : e;
+  jb.out[o] = jb.accumulate ? jb.out[o] + jb.scale * s : jb.scale * s;
+}
+
+static int64_t reduce_cols_blocks(const ColsReduce &jb) {
+  return jb.S > 0 ? ((int64_t)jb.r * jb.C + 255) / 256 : 0;
+}
+
+__global__ __launch_bounds__(256) void k_reduce_cols(ColsReduce a, ColsReduce b, int64_t blocks_a) {
+  const int64_t blk = blockIdx.x;
+  if (blk < blocks_a) reduce_cols_one(a, blk * 256 + threadIdx.x);
+  else reduce_cols_one(b, (blk - blocks_a) * 256 + threadIdx.x);
+}
+
+int launch_reduce_cols(const ColsReduce &a, const ColsReduce &b, hipStream_t stream) {
+  const int64_t na = reduce_cols_blocks(a), nb = reduce_cols_blocks(b);
+  if (na + nb == 0) return QL_OK;
+  hipLaunchKernelGGL(k_reduce_cols, dim3((unsigned)(na + nb)), dim3(256), 0, stream, a, b, na);
+  QL_HIP_CHECK_LAUNCH();
+  return QL_OK;
 }
 
 static int cols_slices(int64_t M, int64_t C) {
@@ -619,7 +636,9 @@ size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
 
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
-                     hipStream_t stream, bool accumulate, const Dropout *drop) {
+                     hipStream_t stream, bool accumulate, const Dropout *drop,
+                     ColsReduce *pending) {
+  if (pending) pending->S = 0;
   if (C <= 0) return QL_OK;
   int S;
   if (drop && !cols_use_mfma(p_dtype, C)) return QL_EUNSUPPORTED;
@@ -660,11 +679,12 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
     });
   }
   QL_HIP_CHECK_LAUNCH();
-  const int64_t count = (int64_t)r * C;
-  hipLaunchKernelGGL(k_reduce_cols, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
-                     partial, S, r, C, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0, out);
-  QL_HIP_CHECK_LAUNCH();
-  return QL_OK;
+  const ColsReduce job{partial, S, r, C, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0, out};
+  if (pending) {  // the caller launches it, possibly together with another
+    *pending = job;
+    return QL_OK;
+  }
+  return launch_reduce_cols(job, ColsReduce{nullptr, 0, 0, 0, 0.0f, 0, 0, nullptr}, stream);
 }
 
 }  // namespace qlora
