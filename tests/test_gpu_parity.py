@@ -267,6 +267,38 @@ def test_layer_parity_block128(orc, M, N, K, r, dq, act):
             assert rel_err(got[k], ref[k]) <= BF16_TOL, k
 
 
+# Degenerate shapes: one or a few outputs (N < 8 sends g and dB to the
+# element-wise rows/cols kernels and dx to the fp32-path kernel), rank 1,
+# a single token, K of one block.
+DEGENERATE_CASES = [
+    # M, N, K, r
+    (1, 1, 64, 1),
+    (5, 3, 64, 2),
+    (300, 7, 128, 1),
+    (17, 1, 128, 16),
+    (300, 1, 64, 128),
+    (2, 9, 64, 3),
+    (129, 5, 192, 7),
+]
+
+
+@pytest.mark.parametrize("act", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("M,N,K,r", DEGENERATE_CASES)
+def test_layer_degenerate_shapes(orc, M, N, K, r, act):
+    _say(f"degenerate M={M} N={N} K={K} r={r} act={act}")
+    lora = torch.float32 if act == torch.float32 else act
+    got, ref = _layer_case(orc, M, N, K, r, True, act, lora)
+    if act == torch.float32:
+        for k in ("y", "u", "dx", "dA", "dB"):
+            assert_f32_close(got[k], ref[k], k)
+        return
+    tol = F16_TOL if act == torch.float16 else BF16_TOL
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
 # fp16 compute (Gemma lesson 09, sec. 9.3: the dequantised weight and the
 # products take the compute dtype; fp16 where bf16 is unavailable): every
 # kernel path with fp16 activations, W^ dequantised to fp16 and fp16 (or
