@@ -189,8 +189,8 @@ class NF4Weight:
 
 def nf4_quantize(w: torch.Tensor, double_quant: bool = True, out: NF4Weight | None = None,
                  ws: torch.Tensor | None = None, block: int = NF4_BLOCK) -> NF4Weight:
-    """NF4-quantise a 2-D weight [N, K] (bf16 or fp32, on the GPU) with blocks
-    of `block` (64 or 128) weights."""
+    """NF4-quantise a 2-D weight [N, K] (bf16, fp16 or fp32, on the GPU) with
+    blocks of `block` (64 or 128) weights."""
     assert w.dim() == 2 and w.is_contiguous() and w.is_cuda
     N, K = w.shape
     q = out or NF4Weight.empty(N, K, double_quant, w.device, block)
@@ -216,7 +216,9 @@ def qlora_linear_fwd(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Te
                      alpha: float, y: torch.Tensor | None = None,
                      u_save: torch.Tensor | None = None,
                      ws: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x W^T + (alpha/r) (x A^T) B^T  with x [M, K], A [r, K], B [N, r]."""
+    """y = x W^T + (alpha/r) (x A^T) B^T  with x [M, K], A [r, K], B [N, r].
+    The compute dtype is x's (bf16, fp16 or fp32); A and B are fp32 or of
+    x's 16-bit dtype (bf16 factors also with fp32 x)."""
     assert x.dim() == 2 and x.is_contiguous() and A.is_contiguous() and B.is_contiguous()
     M, K = x.shape
     r = A.shape[0]
