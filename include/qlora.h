@@ -25,7 +25,8 @@
  *  - The caller owns and allocates every buffer, including the workspace.
  *    The library never allocates or frees device memory and keeps no state
  *    between calls apart from read-only kernel code.
- *  - Outputs are overwritten (never accumulated into).
+ *  - Outputs are overwritten, except dA and dB of the accumulating backward
+ *    entry points, which say so.
  *  - Arguments are checked on the host before anything is enqueued; a failed
  *    check returns a non-zero status and enqueues nothing.  A launch error
  *    reported by the runtime returns QL_EHIP.  No C++ exception crosses the
@@ -135,8 +136,7 @@ size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
  * NF4-quantise a weight (Gemma lesson 09, sec. 9.2.1 and 9.2.2; 26. ...,
  * Step 2 nearest codepoint).
  *   w         device, q->rows * q->cols elements of w_dtype (QL_F32, QL_BF16 or
- *             QL_F16),
- *             16-byte aligned.
+ *             QL_F16), 16-byte aligned.
  *   q         host struct describing device outputs: packed and either absmax
  *             (double_quant 0) or absmax_q, absmax_scale, absmax_mean (1).
  * Per block (64 or 128 consecutive elements of the flattened weight):
