@@ -1,0 +1,100 @@
+"""A seeded sweep of layer shapes against the CPU oracle (through the C ABI).
+
+Each case draws M (tokens), N (outputs), K (inputs, a multiple of the NF4
+block), the rank r, the activation dtype, the block size, double
+quantisation and LoRA dropout from fixed seeds, so that the kernel-choice
+boundaries (decode GEMV up to 16 tokens, the 64-token kernels up to 128,
+the 256-token GEMMs with their width / split-K plans, ragged N, the
+element-wise LoRA kernels for N not a multiple of 8, the fp32-path dx for N
+not a multiple of 64 or K not a multiple of 128) are crossed in combinations
+the hand-picked cases do not list.  16-bit compute: the parity tests'
+tolerances.  fp32 compute: values here reach ~10, past what a fixed atol of
+1e-5 fits, so each element is held to the probabilistic fp32 rounding bound
+of its chain of operations (helpers.assert_f32_within).
+"""
+import numpy as np
+import pytest
+import torch
+
+import qlora_fine_tuning_quantize_amd as q
+import synth_inputs as si
+from tests.helpers import BF16_TOL, F16_TOL, assert_f32_within, host, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+N_CASES = 48
+
+
+def f32_chain(out, M, N, K, r):
+    """Roundings on the longest path to each fp32 output (sums of n terms
+    count n; scalings and the final additions one each; 4 spare for partial
+    sums scaled before their reduction): u = x A^T, y = x W^T + s u B^T,
+    g = s dy B, dx = dy W + g A, dA = g^T x, dB = s dy^T u."""
+    return {"u": K, "y": K + r + 2, "dx": N + r + 2, "dA": N + 1 + M,
+            "dB": K + M + 1}[out] + 4
+
+
+def _draw(i):
+    rng = np.random.default_rng(1000 + i)
+    act = [torch.bfloat16, torch.float16, torch.float32][int(rng.integers(0, 3)) if i % 6 else 2]
+    block = int(rng.choice([64, 128]))
+    M = int(rng.choice([1, 2, 5, 16, 17, 33, 64, 100, 128, 129, 200, 256, 300, 513]))
+    N = int(rng.choice([1, 7, 8, 24, 64, 96, 200, 256, 384, 640, 1000, 1536]))
+    K = block * int(rng.integers(1, 13))
+    r = int(rng.choice([1, 3, 8, 16, 17, 32, 64, 100, 128]))
+    # scaling s = alpha / r in [0.5, 2], the range of the pages' settings
+    alpha = float(r * rng.choice([0.5, 1.0, 2.0]))
+    dq = bool(rng.integers(0, 2))
+    lora = torch.float32 if (act == torch.float32 or rng.integers(0, 3) == 0) else act
+    # dropout on the 16-bit paths, with dx shapes the matrix-core dx kernel takes
+    drop = 0.0
+    if act != torch.float32 and N % 64 == 0 and K % 128 == 0 and rng.integers(0, 3) == 0:
+        drop = float(rng.choice([0.05, 0.3]))
+    return dict(M=M, N=N, K=K, r=r, alpha=alpha, act=act, lora=lora, block=block, dq=dq, drop=drop)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(orc, i):
+    c = _draw(i)
+    M, N, K, r, act, alpha = c["M"], c["N"], c["K"], c["r"], c["act"], c["alpha"]
+    print(f"random case {i}: {c}", flush=True)
+    t = si.linear_inputs(2000 + i, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=c["lora"],
+                         sub=i)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=c["dq"], block=c["block"])
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    seed = 77 + i
+    if c["drop"] > 0:
+        y = q.qlora_linear_fwd_dropout(d["x"], W, d["A"], d["B"], alpha, c["drop"], seed, u_save=u)
+        dx, dA, dB = q.qlora_linear_bwd_dropout(d["dy"], d["x"], W, d["A"], d["B"], alpha,
+                                                c["drop"], seed, u_saved=u)
+    else:
+        y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], alpha, u_save=u)
+        dx, dA, dB = q.qlora_linear_bwd(d["dy"], d["x"], W, d["A"], d["B"], alpha, u_saved=u)
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(t["W"]), double_quant=c["dq"], block=c["block"])
+    np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
+    w_hat = orc.dequantize(st).reshape(N, K)
+    mult = orc.dropout_mult(M, K, c["drop"], seed) if c["drop"] > 0 else None
+    y_ref, u_ref = orc.linear_fwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), alpha, r,
+                                  drop=mult)
+    dx_ref, dA_ref, dB_ref = orc.linear_bwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]),
+                                            host(t["dy"]), alpha, r, drop=mult)
+    got = {"y": y.float().cpu().numpy(), "u": u.cpu().numpy(), "dx": dx.float().cpu().numpy(),
+           "dA": dA.cpu().numpy(), "dB": dB.cpu().numpy()}
+    ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": dA_ref, "dB": dB_ref}
+    if act == torch.float32:
+        # magnitudes: the same expressions on absolute values (s > 0)
+        ab = lambda a: np.abs(np.asarray(a, np.float64))
+        y_mag, u_mag = orc.linear_fwd(ab(t["x"]), ab(w_hat), ab(t["A"]), ab(t["B"]), alpha, r)
+        dx_mag, dA_mag, dB_mag = orc.linear_bwd(ab(t["x"]), ab(w_hat), ab(t["A"]), ab(t["B"]),
+                                                ab(t["dy"]), alpha, r)
+        mag = {"y": y_mag, "u": u_mag, "dx": dx_mag, "dA": dA_mag, "dB": dB_mag}
+        for k in got:
+            assert_f32_within(got[k], ref[k], mag[k], f32_chain(k, M, N, K, r), k)
+        return
+    tol = F16_TOL if act == torch.float16 else BF16_TOL
+    errs = {k: rel_err(got[k], ref[k]) for k in got}
+    print("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
