@@ -193,12 +193,14 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
  *   u       device [M, r] fp32, 16-byte aligned
  * Other arguments as for qlora_linear_fwd; no workspace.  With 16-bit
  * activations this is a single matrix-core launch that never splits the
- * contraction.  It is bit-identical to the y of qlora_linear_fwd for M > 16
- * whenever that call does not split the contraction either; where it does
- * (a shape-dependent choice: few output tiles, or tiles that fill the chip
- * better when split), or for M <= 16 (the single-launch decode path, which
- * rounds u to 16 bits in registers instead of reading it), the two agree to
- * within 16-bit rounding.
+ * contraction.  It is bit-identical to the y of qlora_linear_fwd whenever
+ * that call takes the matrix-core GEMM without splitting the contraction
+ * either; where it splits (a shape-dependent choice: few output tiles, or
+ * tiles that fill the chip better when split) or takes the single-launch
+ * decode path (M <= 16 on weights of at most 2^25 elements; on larger
+ * weights M = 1, or M <= 4 with at most 4096 rows; that path rounds u to 16
+ * bits in registers instead of reading it), the two agree to within 16-bit
+ * rounding.
  * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
  */
 int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,

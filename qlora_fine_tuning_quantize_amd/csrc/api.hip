@@ -66,6 +66,20 @@ QuantWs quant_ws(int64_t n) {
 
 // The split-K partial tiles of a GEMM start at `rows`: the LoRA partials
 // stored there are dead once the GEMM (issued later on the same stream) runs.
+// The decode forward (one launch that also computes u) or the few-token
+// path (u, then the 64-token GEMM and its split-K sum), by measured cost on
+// MI355X.  The decode kernel's workgroups each own 16 weight rows and
+// recompute u, so its time grows with the weight size times the token
+// count, while the few-token path costs ~19 us for any small weight and
+// grows slowly with it.  Forward, 16 tokens: 4096 x 4096 weight 12.7 against
+// 20.0 us; 14336 x 4096: 40.4 against 28.6 (1 token: 23.0 against 26.1);
+// 4096 x 14336: 4 tokens 24.1 against 30.6, 8 tokens 36.9 against 31.5.
+bool gemv_fwd_preferred(int64_t M, int64_t N, int64_t K) {
+  if (M > 16) return false;
+  if (N * K <= ((int64_t)1 << 25)) return true;  // up to 32 Mi weights
+  return M == 1 || (N <= 4096 && M <= 4);
+}
+
 struct FwdWs {
   size_t u, rows, total;
 };
@@ -238,7 +252,7 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype != QL_F32 && M <= 16 && !drop)  // decode: one launch computes u and y
+  if (act_dtype != QL_F32 && !drop && gemv_fwd_preferred(M, N, K))
     return launch_gemv_fwd(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y,
                            u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,

@@ -50,10 +50,11 @@ constexpr int kGemvScales = kGemvRows * kGemvRound / kGemvThreads;
 constexpr int kGemvXStride = kGemvRound * 128 + 16;
 
 // Blocks whose activation and A loads are in flight together: 8 for a
-// 16-wide rank tile in 16 bits, fewer as the per-block register footprint grows.
-template <typename LT, int JT>
+// 16-wide rank tile in 16 bits at 2 waves per SIMD, fewer as the per-block
+// register footprint grows or as more waves share the registers.
+template <typename LT, int JT, int WPE>
 constexpr int gemv_batch() {
-  constexpr int w = JT * (int)(sizeof(LT) / 2);
+  constexpr int w = JT * (int)(sizeof(LT) / 2) * (WPE / 2);
   return w >= 8 ? 1 : 8 / w;
 }
 
@@ -102,8 +103,13 @@ struct GemvBlock {
 // LDS once per workgroup (the operand layout repeats a token row across the
 // 16 lanes of a lane group, which would otherwise be 16 / M copies of the
 // same bytes through the load path); XM = 0: read in operand layout.
-template <typename AT, typename LT, int JT, bool DQ, int XM>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
+// WPE: waves per SIMD the register allocation must allow.  2 (one workgroup
+// per compute unit) leaves the most registers for loads in flight, which is
+// what a grid of at most one workgroup per unit needs; 4 lets two workgroups
+// share a unit, so that a larger grid overlaps one workgroup's round trips
+// with the other's work.
+template <typename AT, typename LT, int JT, bool DQ, int XM, int WPE>
+__global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
                                                            const uint8_t *__restrict__ packed,
                                                            BlockScales sc, int64_t N, int64_t K,
                                                            const LT *__restrict__ A,
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
     lut[t] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
 
-  constexpr int kBatch = gemv_batch<LT, JT>();
+  constexpr int kBatch = gemv_batch<LT, JT, WPE>();
   constexpr int kWaveBlocks = kGemvRound / kGemvWaves;  // blocks per wave per full round
   GemvBlock<AT, LT, JT> bl[kBatch];
   // loads of blocks first .. first + kBatch - 1 of the round, clamped to its last block
@@ -361,22 +367,42 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_fwd(const uint16_t *__res
   }
 }
 
-template <typename AT, typename LT, int JT, int XM>
+template <typename AT, typename LT, int JT, int XM, int WPE = 2>
 static void launch_xm(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
   if (sc.absmax == nullptr)
-    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, true, XM>), grid, dim3(kGemvThreads), 0, stream,
-                       x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, true, XM, WPE>), grid, dim3(kGemvThreads), 0,
+                       stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
+                       u_save);
   else
-    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, false, XM>), grid, dim3(kGemvThreads), 0, stream,
-                       x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y, u_save);
+    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, false, XM, WPE>), grid, dim3(kGemvThreads), 0,
+                       stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
+                       u_save);
 }
+
+// Compute units of the chip (MI355X): a grid larger than this runs in
+// several rounds of workgroups per unit.
+constexpr unsigned kGemvUnits = 256;
 
 template <typename AT, typename LT, int JT>
 static void launch_jt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
                       const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
+  // More workgroups than units, and a footprint two of which fit a unit's
+  // LDS (rank tiles of 16 or 32, activations staged for one token row or
+  // read in operand layout): two workgroups per unit.  For 2-4 token rows
+  // the one-per-unit form with the rows staged in LDS is faster (14336 x
+  // 4096 weight, 4 rows: 27 against 32 us).
+  if constexpr (JT <= 2) {
+    if (grid.x > kGemvUnits && (M == 1 || M > 4)) {
+      if (M == 1)
+        launch_xm<AT, LT, JT, 1, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+      else
+        launch_xm<AT, LT, JT, 0, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+      return;
+    }
+  }
   if (M == 1)
     launch_xm<AT, LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
   else if (M <= 4)

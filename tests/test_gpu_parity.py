@@ -419,6 +419,51 @@ def test_decode_config_full_size(orc, M):
     assert e <= BF16_TOL
 
 
+# Decode-sized forwards (M <= 16) on larger weights, every output and u.
+# The decode kernel takes M <= 16 on weights of up to 2^25 elements; an
+# 8192 x 4096 weight gives it 512 workgroups of 16 rows, more than the chip's
+# 256 compute units (two workgroups per unit at rank tiles of 16 and 32,
+# except for 2-4 token rows).  On the 8B MLP weights it takes M = 1 (gate:
+# 896 workgroups) and M <= 4 on the down weight (256 workgroups of 3.5
+# contraction rounds); other token counts there take the few-token GEMM
+# with fewer than 17 token rows in its 64-row tile.
+DECODE_LARGE_CASES = [
+    # M, N, K, r, act, lora dtype, double quant
+    (1, 8192, 4096, 16, torch.bfloat16, torch.bfloat16, True),
+    (3, 8192, 4096, 16, torch.bfloat16, torch.bfloat16, True),
+    (8, 8192, 4096, 16, torch.bfloat16, torch.float32, False),
+    (16, 8192, 4096, 32, torch.bfloat16, torch.bfloat16, True),
+    (5, 8192, 4096, 32, torch.float16, torch.float32, True),
+    (16, 8192, 4096, 64, torch.bfloat16, torch.bfloat16, True),  # rank tile 64: one per unit
+    (1, 14336, 4096, 16, torch.bfloat16, torch.bfloat16, True),
+    (1, 14336, 4096, 32, torch.float16, torch.float16, False),
+    (3, 14336, 4096, 16, torch.bfloat16, torch.bfloat16, True),   # few-token GEMM
+    (16, 14336, 4096, 16, torch.float16, torch.float16, True),    # few-token GEMM
+    (4, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),
+    (16, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),  # few-token GEMM
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,act,lora,dq", DECODE_LARGE_CASES)
+def test_decode_large_weights(orc, M, N, K, r, act, lora, dq):
+    _say(f"decode-sized M={M} N={N} K={K} r={r} act={act} lora={lora} dq={dq}")
+    t = si.linear_inputs(97, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora,
+                         with_dy=False, sub=M + r)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=dq)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], 32.0, u_save=u)
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(t["W"]), double_quant=dq)
+    np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
+    y_ref, u_ref = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
+                                  host(t["B"]), 32.0, r)
+    tol = F16_TOL if act == torch.float16 else BF16_TOL
+    ey, eu = rel_err(y.float().cpu().numpy(), y_ref), rel_err(u.cpu().numpy(), u_ref)
+    _say(f"  rel err y {ey:.2e} u {eu:.2e}")
+    assert ey <= tol and eu <= tol
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_mlp8b_config_full_size_sampled(orc, proj):
     """8B-shaped MLP projection at M = 2048 tokens, r 16, alpha 32, NF4 +
