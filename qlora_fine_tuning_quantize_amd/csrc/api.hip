@@ -90,6 +90,10 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   w.total = w.rows + round_up(lora_rows_partial_floats(M, K, r) * 4);
   const size_t gemm_end = w.rows + round_up(gemm_fwd_partial_floats(M, N, K) * 4);
   if (gemm_end > w.total) w.total = gemm_end;
+  if (M <= 16) {  // a decode forward's split partials, in the same region
+    const size_t gemv_end = w.rows + round_up(gemv_fwd_partial_floats(M, N, K, r) * 4);
+    if (gemv_end > w.total) w.total = gemv_end;
+  }
   return w;
 }
 
@@ -254,7 +258,7 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   const BlockScales sc = scales_of(W);
   if (act_dtype != QL_F32 && !drop && gemv_fwd_preferred(M, N, K))
     return launch_gemv_fwd(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y,
-                           u_save, s);
+                           u_save, s, rows_partial);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
                            rows_partial, s, nullptr, drop);
   if (st) return st;

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *
                                                            const LT *__restrict__ A,
                                                            const LT *__restrict__ B, int32_t r,
                                                            float s, uint16_t *__restrict__ y,
-                                                           float *__restrict__ u_save) {
+                                                           float *__restrict__ u_save,
+                                                           float *__restrict__ part) {
   __shared__ uint32_t lut[256];
   __shared__ __attribute__((aligned(16))) uint8_t wt[kGemvRows * kGemvRowStride];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XM > 0 ? XM * kGemvXStride : 16];
@@ -186,7 +187,12 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) uacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t rb0 = 0; rb0 < KB; rb0 += kGemvRound) {
+  // contraction split blockIdx.y of gridDim.y: whole rounds rb_begin .. rb_end
+  const int64_t rounds = (KB + kGemvRound - 1) / kGemvRound;
+  const int64_t per = (rounds + gridDim.y - 1) / gridDim.y;
+  const int64_t rb_begin = (int64_t)blockIdx.y * per * kGemvRound;
+  const int64_t rb_end = rb_begin + per * kGemvRound < KB ? rb_begin + per * kGemvRound : KB;
+  for (int64_t rb0 = rb_begin; rb0 < rb_end; rb0 += kGemvRound) {
     const int RB = KB - rb0 < kGemvRound ? (int)(KB - rb0) : kGemvRound;
     // the round's weight slice: 16 rows x 2 RB chunks of 16 bytes; chunk c is
     // column chunk c % 128 of row c / 128 (chunks past the slice or rows past
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *
       if ((c & 511) < 8 * RB)
         *reinterpret_cast<u32x4 *>(xs + (c >> 9) * kGemvXStride + 16 * (c & 511)) = xv[i];
     }
-    if (rb0 == 0) {
+    if (rb0 == rb_begin) {
 #pragma unroll
       for (int i = 0; i < kBPer; ++i) {
         const int e = t + kGemvThreads * i;
@@ -344,6 +350,33 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *
 #pragma unroll
     for (int v = 0; v < 4; ++v) ured[wave][4 * q + v][16 * jt + nl] = (JT == 1 ? uacc[jt][v] + uacc1[0][v] : uacc[jt][v]);
   __syncthreads();
+  if (part) {
+    // split contraction: this split's sums over its rounds, the bypass term
+    // added by k_gemv_reduce.  part = y partials [S][M][N], then u partials
+    // [S][M][r] (every row group computes the same u; the first stores it).
+    const int64_t sp = blockIdx.y;
+    if (blockIdx.x == 0) {
+      float *pu = part + (int64_t)gridDim.y * M * N;
+      for (int e = t; e < 16 * 16 * JT; e += kGemvThreads) {
+        const int mo = e / (16 * JT), j = e % (16 * JT);
+        float su = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kGemvWaves; ++w) su += ured[w][mo][j];
+        if (mo < M && j < r) pu[(sp * M + mo) * r + j] = su;
+      }
+    }
+    if (t < 256) {
+      const int mo = t >> 4, no = t & 15;
+      const int64_t nn = n0 + no;
+      if (mo < M && nn < N) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kGemvWaves; ++w) sum += red[w][mo][no];
+        part[(sp * M + mo) * N + nn] = sum;
+      }
+    }
+    return;
+  }
   for (int e = t; e < 16 * 16 * JT; e += kGemvThreads) {
     const int mo = e / (16 * JT), j = e % (16 * JT);
     float su = 0.0f;
@@ -367,18 +400,47 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *
   }
 }
 
+// The contraction splits of k_gemv_fwd summed in split order, then the
+// bypass term, as the single-split epilogue forms it: u[m][j] = sum over
+// splits, y[m][n] = RN(fmaf(s, sum_j u[m][j] B[n][j], sum over splits)).
+// Grid (ceil(N / 256), M); the first column of workgroups stores u_save.
+template <typename AT, typename LT>
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int S, int M,
+                                                     int64_t N, int32_t r,
+                                                     const LT *__restrict__ B, float s,
+                                                     uint16_t *__restrict__ y,
+                                                     float *__restrict__ u_save) {
+  __shared__ float us[128];
+  const int m = blockIdx.y, t = threadIdx.x;
+  const float *pu = part + (int64_t)S * M * N;
+  if (t < r) {
+    float su = 0.0f;
+    for (int sp = 0; sp < S; ++sp) su += pu[((int64_t)sp * M + m) * r + t];
+    us[t] = su;
+    if (u_save && blockIdx.x == 0) u_save[(int64_t)m * r + t] = su;
+  }
+  __syncthreads();
+  const int64_t n = (int64_t)blockIdx.x * 256 + t;
+  if (n >= N) return;
+  float sum = 0.0f;
+  for (int sp = 0; sp < S; ++sp) sum += part[((int64_t)sp * M + m) * N + n];
+  float l = 0.0f;
+  for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[j], load_as_f32(B, n * r + j), l);
+  y[(int64_t)m * N + n] = Half<AT>::bits(__builtin_fmaf(s, l, sum));
+}
+
 template <typename AT, typename LT, int JT, int XM, int WPE = 2>
 static void launch_xm(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
+                      const void *B, int32_t r, float s, uint16_t *y, float *u_save, float *part) {
   if (sc.absmax == nullptr)
     hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, true, XM, WPE>), grid, dim3(kGemvThreads), 0,
                        stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
-                       u_save);
+                       u_save, part);
   else
     hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, false, XM, WPE>), grid, dim3(kGemvThreads), 0,
                        stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
-                       u_save);
+                       u_save, part);
 }
 
 // Compute units of the chip (MI355X): a grid larger than this runs in
@@ -388,53 +450,91 @@ constexpr unsigned kGemvUnits = 256;
 template <typename AT, typename LT, int JT>
 static void launch_jt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
+                      const void *B, int32_t r, float s, uint16_t *y, float *u_save,
+                      float *part) {
   // More workgroups than units, and a footprint two of which fit a unit's
   // LDS (rank tiles of 16 or 32, activations staged for one token row or
   // read in operand layout): two workgroups per unit.  For 2-4 token rows
   // the one-per-unit form with the rows staged in LDS is faster (14336 x
   // 4096 weight, 4 rows: 27 against 32 us).
   if constexpr (JT <= 2) {
-    if (grid.x > kGemvUnits && (M == 1 || M > 4)) {
+    if (grid.x * grid.y > kGemvUnits && (M == 1 || M > 4)) {
       if (M == 1)
-        launch_xm<AT, LT, JT, 1, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+        launch_xm<AT, LT, JT, 1, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
       else
-        launch_xm<AT, LT, JT, 0, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+        launch_xm<AT, LT, JT, 0, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
       return;
     }
   }
   if (M == 1)
-    launch_xm<AT, LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+    launch_xm<AT, LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
   else if (M <= 4)
-    launch_xm<AT, LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+    launch_xm<AT, LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
   else
-    launch_xm<AT, LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+    launch_xm<AT, LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
 }
 
 template <typename AT, typename LT>
 static void launch_lt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
                       const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save) {
-  if (r <= 16) launch_jt<AT, LT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else if (r <= 32) launch_jt<AT, LT, 2>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else if (r <= 64) launch_jt<AT, LT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
-  else launch_jt<AT, LT, 8>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save);
+                      const void *B, int32_t r, float s, uint16_t *y, float *u_save,
+                      float *part) {
+  if (r <= 16) launch_jt<AT, LT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
+  else if (r <= 32) launch_jt<AT, LT, 2>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
+  else if (r <= 64) launch_jt<AT, LT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
+  else launch_jt<AT, LT, 8>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
+}
+
+// Workgroups a split contraction aims for: two per compute unit.
+constexpr int64_t kGemvSplitTarget = 2 * kGemvUnits;
+
+// Contraction splits of a decode forward: one unless the row groups leave
+// at least half the units idle and there are rounds to share; no split is
+// left without rounds.  (At 129-256 groups the split's second launch and the
+// smaller register budget cost more than it gains: 4096 x 14336 weight, one
+// token, 23.4 us unsplit against 26.7 split in 2; at 64 groups, 1024 x 14336,
+// 21.0 against 12.6 split in 4.)
+static int gemv_splits(int64_t N, int64_t K) {
+  const int64_t groups = (N + kGemvRows - 1) / kGemvRows;
+  const int64_t rounds = ((K >> 6) + kGemvRound - 1) / kGemvRound;
+  if (rounds < 2 || 2 * groups > kGemvUnits) return 1;
+  int64_t S = (kGemvSplitTarget + groups - 1) / groups;
+  if (S > rounds) S = rounds;
+  if (S < 2) return 1;
+  const int64_t per = (rounds + S - 1) / S;
+  return (int)((rounds + per - 1) / per);
+}
+
+size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r) {
+  const int S = gemv_splits(N, K);
+  return S > 1 ? (size_t)S * M * (N + r) : 0;
 }
 
 // A 16-bit LoRA factor has the activations' format (checked by the caller).
 int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *yv, float *u_save,
-                    hipStream_t stream) {
+                    hipStream_t stream, float *part) {
   const uint16_t *x = (const uint16_t *)xv;
   uint16_t *y = (uint16_t *)yv;
-  const dim3 grid((unsigned)((N + kGemvRows - 1) / kGemvRows));
+  const int S = part ? gemv_splits(N, K) : 1;
+  const dim3 grid((unsigned)((N + kGemvRows - 1) / kGemvRows), (unsigned)S);
+  float *p = S > 1 ? part : nullptr;
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
     if (lora_dtype == QL_F32)
-      launch_lt<AT, float>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
+      launch_lt<AT, float>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save, p);
     else
-      launch_lt<AT, AT>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save);
+      launch_lt<AT, AT>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save, p);
+    if (S > 1) {
+      const dim3 rgrid((unsigned)((N + 255) / 256), (unsigned)M);
+      if (lora_dtype == QL_F32)
+        hipLaunchKernelGGL((k_gemv_reduce<AT, float>), rgrid, dim3(256), 0, stream, p, S, (int)M,
+                           N, r, (const float *)B, s, y, u_save);
+      else
+        hipLaunchKernelGGL((k_gemv_reduce<AT, AT>), rgrid, dim3(256), 0, stream, p, S, (int)M,
+                           N, r, (const AT *)B, s, y, u_save);
+    }
   });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;

@@ -60,12 +60,17 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
                      int lora_dtype, int32_t r, void *dx, hipStream_t stream);
 
-// gemv.hip: decode-sized forward (M <= 16, 16-bit activations), one launch:
-// computes u = x A^T itself and writes it to u_save when non-null.
+// gemv.hip: decode-sized forward (M <= 16, 16-bit activations): computes
+// u = x A^T itself and writes it to u_save when non-null.  One launch, or,
+// when part is non-null and the weight has few row groups and several
+// rounds of 4096 columns, the contraction split over workgroups with fp32
+// partials in part (gemv_fwd_partial_floats floats) and a second launch
+// that sums them.
+size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r);
 int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *y, float *u_save,
-                    hipStream_t stream);
+                    hipStream_t stream, float *part);
 
 // gemm.hip: matrix-core forward and input-gradient products for 16-bit
 // activations (act_dtype QL_BF16 or QL_F16; a 16-bit lora_dtype equals it).

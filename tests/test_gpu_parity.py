@@ -426,7 +426,10 @@ def test_decode_config_full_size(orc, M):
 # except for 2-4 token rows).  On the 8B MLP weights it takes M = 1 (gate:
 # 896 workgroups) and M <= 4 on the down weight (256 workgroups of 3.5
 # contraction rounds); other token counts there take the few-token GEMM
-# with fewer than 17 token rows in its 64-row tile.
+# with fewer than 17 token rows in its 64-row tile.  When the row groups
+# leave half the compute units idle (at most 128 groups of 16 rows) and the
+# contraction has several rounds of 4096 columns, the decode kernel splits
+# the contraction over workgroups.
 DECODE_LARGE_CASES = [
     # M, N, K, r, act, lora dtype, double quant
     (1, 8192, 4096, 16, torch.bfloat16, torch.bfloat16, True),
@@ -441,6 +444,11 @@ DECODE_LARGE_CASES = [
     (16, 14336, 4096, 16, torch.float16, torch.float16, True),    # few-token GEMM
     (4, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),
     (16, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),  # few-token GEMM
+    # decode kernel with the contraction split over workgroups (few row
+    # groups, several rounds of 4096 columns), partials summed by a second launch
+    (2, 2048, 28672, 16, torch.bfloat16, torch.bfloat16, True),   # 7 rounds as 2 + 2 + 2 + 1
+    (1, 1024, 14336, 32, torch.bfloat16, torch.float32, False),   # 4 splits of one round
+    (16, 2048, 16384, 16, torch.float16, torch.float16, True),    # 4 splits, 16 tokens
 ]
 
 
