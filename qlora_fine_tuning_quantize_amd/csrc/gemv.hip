@@ -1,6 +1,6 @@
 // gemv.hip -- decode-sized forward of the QLoRA layer (M <= 16 tokens, 16-bit
 // activations: bf16, or fp16 as the compute dtype of Gemma lesson 09, sec.
-// 9.3), one kernel launch per call:
+// 9.3), one kernel launch per call (two when the contraction is split, below):
 //
 //   u = x A^T,   y = x W^^T + s u B^T     (26. QLoRA and 4bit Quantization, Step 3)
 //
@@ -23,8 +23,14 @@
 //
 // The rank-r pre-product u = x A^T is recomputed by every workgroup from the
 // activation operand it already holds (extra 16x16x32 ops against rows of A,
-// read from L2), so decode needs no second kernel and no grid-wide
-// dependency.  Workgroup 0 stores u when the caller asks for it.
+// read from L2), so decode needs no u kernel and no grid-wide dependency.
+// Workgroup 0 stores u when the caller asks for it.
+//
+// A weight with few row groups and a long contraction would leave most
+// compute units idle; there grid.y splits the contraction into whole rounds,
+// each split writes its fp32 sums of y and u to the caller's workspace, and
+// k_gemv_reduce adds the splits in order and forms y as the single-split
+// epilogue does.
 //
 // Operand layout of v_mfma_f32_16x16x32_{bf16,f16} (gfx950): A lane l holds
 // A[l % 16][8*(l/16) .. +8], B lane l holds B[8*(l/16) .. +8][l % 16], and the
