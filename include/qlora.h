@@ -196,7 +196,7 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
  * contraction.  It is bit-identical to the y of qlora_linear_fwd whenever
  * that call takes the matrix-core GEMM without splitting the contraction
  * either; where it splits (a shape-dependent choice: few output tiles, or
- * tiles that fill the chip better when split) or takes the single-launch
+ * tiles that fill the chip better when split) or takes the
  * decode path (M <= 16 on weights of at most 2^25 elements; on larger
  * weights M = 1, or M <= 4 with at most 4096 rows; that path rounds u to 16
  * bits in registers instead of reading it), the two agree to within 16-bit
