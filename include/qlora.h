@@ -196,11 +196,10 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
  * contraction.  It is bit-identical to the y of qlora_linear_fwd whenever
  * that call takes the matrix-core GEMM without splitting the contraction
  * either; where it splits (a shape-dependent choice: few output tiles, or
- * tiles that fill the chip better when split) or takes the
- * decode path (M <= 16 on weights of at most 2^25 elements; on larger
- * weights M = 1, or M <= 4 with at most 4096 rows; that path rounds u to 16
- * bits in registers instead of reading it), the two agree to within 16-bit
- * rounding.
+ * tiles that fill the chip better when split) or takes the decode path
+ * (M <= 16: the base product and the bypass are summed in fp32 and rounded
+ * once, u is formed in its own summation order), the two agree to within
+ * 16-bit rounding.
  * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EUNSUPPORTED, QL_EHIP.
  */
 int qlora_linear_fwd_u(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
@@ -317,7 +316,10 @@ int ql_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_av
 /* Host only: a static string describing a status code. */
 const char *ql_strerror(int status);
 
-/* Host only: ABI version (major * 100 + minor). */
+/* Host only: ABI version (major * 100 + minor).  The minor version grows
+ * whenever an entry point is added or a workspace size changes.
+ *   106: the decode forward (M <= 16) sizes its workspace for contraction
+ *        slices and u slices on every shape. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

@@ -372,6 +372,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Sets the number of host threads of the parallel loops (timing only: no
+ * result depends on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* One AdamW step over n fp32 parameters, in place.  [gc4] "显存计算实战" and
  * "分页优化器": the LoRA factors are trained with AdamW (torch.optim.AdamW,
  * lr 2e-4) holding fp32 moments, 8 bytes per trainable parameter; [L9] 9.4:

@@ -65,6 +65,7 @@ def _load():
     lib.orc_adamw_step.argtypes = [_p, _p, _p, _p, _p, _i64, _f32, _f32, _f32, _f32, _f32, _f32,
                                    _f32, _f32]
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -78,6 +79,12 @@ def _ptr(a: np.ndarray | None):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads of the oracle's parallel loops (for timing; results do
+    not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------------------

@@ -8,6 +8,7 @@
 
 using namespace qlora;
 
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -66,18 +67,14 @@ QuantWs quant_ws(int64_t n) {
 
 // The split-K partial tiles of a GEMM start at `rows`: the LoRA partials
 // stored there are dead once the GEMM (issued later on the same stream) runs.
-// The decode forward (one launch that also computes u) or the few-token
-// path (u, then the 64-token GEMM and its split-K sum), by measured cost on
-// MI355X.  The decode kernel's workgroups each own 16 weight rows and
-// recompute u, so its time grows with the weight size times the token
-// count, while the few-token path costs ~19 us for any small weight and
-// grows slowly with it.  Forward, 16 tokens: 4096 x 4096 weight 12.7 against
-// 20.0 us; 14336 x 4096: 40.4 against 28.6 (1 token: 23.0 against 26.1);
-// 4096 x 14336: 4 tokens 24.1 against 30.6, 8 tokens 36.9 against 31.5.
+// Token counts up to 16 take the decode forward (a weight-streaming launch
+// that also computes u in a few workgroups of its own, then a launch that
+// sums the contraction slices and adds the bypass); larger ones the
+// matrix-core GEMMs.
 bool gemv_fwd_preferred(int64_t M, int64_t N, int64_t K) {
-  if (M > 16) return false;
-  if (N * K <= ((int64_t)1 << 25)) return true;  // up to 32 Mi weights
-  return M == 1 || (N <= 4096 && M <= 4);
+  (void)N;
+  (void)K;
+  return M <= 16;
 }
 
 struct FwdWs {
@@ -153,7 +150,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 105; }
+int ql_abi_version(void) { return 106; }
 
 const char *ql_strerror(int status) {
   switch (status) {

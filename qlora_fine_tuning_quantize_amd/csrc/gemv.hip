@@ -1,68 +1,56 @@
 // gemv.hip -- decode-sized forward of the QLoRA layer (M <= 16 tokens, 16-bit
 // activations: bf16, or fp16 as the compute dtype of Gemma lesson 09, sec.
-// 9.3), one kernel launch per call (two when the contraction is split, below):
+// 9.3):
 //
 //   u = x A^T,   y = x W^^T + s u B^T     (26. QLoRA and 4bit Quantization, Step 3)
 //
-// Memory-bound: the packed 4-bit weight is the dominant traffic.  Each
-// workgroup owns 16 consecutive weight rows, which are one contiguous span of
-// the packed array.  The contraction runs in rounds of 64 NF4 blocks (4096
-// columns): the round's slice of the 16 rows is read with 16-byte loads, each
-// wave instruction covering half a kilobyte of two rows, and staged in LDS;
-// the 8 waves then split the round's blocks and read their codes back in the
-// matrix-core operand layout.  The round's block constants (absmax, or the
-// double-quantised form q * sigma + mu) are resolved once into an LDS table.
+// Memory-bound: the packed 4-bit weight is the dominant traffic, so the
+// weight is read exactly once, in as many independent streams as the chip
+// can keep in flight, and nothing else competes with it for the load path.
+// Two launches:
 //
-// The 16x16x32 16-bit matrix-core op multiplies the activations by the
-// *unscaled* codebook values of one 64-element chunk (16 rows x 32 columns
-// per op, two ops per chunk; a chunk lies inside one NF4 block of 64 or 128);
-// the block's fp32 constant is then applied to the 4 partial sums each lane
-// holds (26. ..., Step 4: table[index] * scale, with the scale taken out of
-// the 64-term sum it multiplies).  The codebook lookup
-// goes through a byte -> 2 x 16-bit table in LDS built from immediates.
+//  k_dec_main   two kinds of workgroups in one grid.  The first compute
+//               u = x A^T, one 16-rank tile over one slice of the
+//               contraction each (A is read once in total, not once per
+//               weight tile), and write fp32 partial sums.  The others stream the weight: a workgroup
+//               owns 64 consecutive weight rows and one slice of the
+//               contraction; each of its 4 waves owns all 64 rows over a
+//               contiguous run of 128-column chunks and reads them straight
+//               into matrix-core operand registers (no LDS staging, no
+//               barrier until the final cross-wave sum), prefetching the next
+//               chunk while it multiplies the current one.  Each workgroup
+//               writes its fp32 sums of x W^^T for its slice.
+//  k_dec_finish sums the slices in a fixed order and forms
+//               y = RN(fmaf(s, sum_j u_j B_nj, base)), and u_save.
 //
-// The rank-r pre-product u = x A^T is recomputed by every workgroup from the
-// activation operand it already holds (extra 16x16x32 ops against rows of A,
-// read from L2), so decode needs no u kernel and no grid-wide dependency.
-// Workgroup 0 stores u when the caller asks for it.
+// Matrix-core op v_mfma_f32_16x16x32_{bf16,f16} (gfx950): A lane l holds
+// A[l % 16][8*(l/16) .. +8], B lane l holds B[8*(l/16) .. +8][l % 16], result
+// lane l holds D[4*(l/16) .. +4][l % 16].  A = activations (token rows), B =
+// 16 weight rows (columns of D).  For one 128-column chunk, lane group q =
+// l / 16 loads the 16 packed bytes [16 q, 16 q + 16) of the chunk's 64 bytes
+// of its weight row, so a wave load covers 64 contiguous bytes of each of 16
+// rows; op j (j = 0..3) takes the 4-byte word j of those 16 bytes, i.e.
+// columns 32 q + 8 j + 0..7 of the chunk, and the activation operand of op j
+// holds the same columns.
 //
-// A weight with few row groups and a long contraction would leave most
-// compute units idle; there grid.y splits the contraction into whole rounds,
-// each split writes its fp32 sums of y and u to the caller's workspace, and
-// k_gemv_reduce adds the splits in order and forms y as the single-split
-// epilogue does.
-//
-// Operand layout of v_mfma_f32_16x16x32_{bf16,f16} (gfx950): A lane l holds
-// A[l % 16][8*(l/16) .. +8], B lane l holds B[8*(l/16) .. +8][l % 16], and the
-// result lane l holds D[4*(l/16) .. +4][l % 16].  All operands use the same
-// permutation of K within a block: op c of block b covers
-// k = 64 b + 16 q + 8 c + e for lane group q = l / 16 and e = 0..7.
+// The weight operand is the *unscaled* codebook value of each index (26.
+// ..., Step 4 lookup table; a byte -> two 16-bit values table in LDS); the
+// block constant is applied to the op's fp32 sums afterwards (26. ..., Step
+// 4: table[index] * scale, with the scale taken out of the sum it
+// multiplies).  A chunk holds two 64-element blocks per row (lane groups 0-1
+// the first, 2-3 the second), and one op sums over all four lane groups, so
+// each op runs twice: once with the activation operand of lane groups 2-3
+// zeroed (the first block) and once with that of 0-1 zeroed (the second).
+// The zeroed operands are built once per chunk and serve all 64 rows.
 #include "kernels.h"
 
 namespace qlora {
 
-constexpr int kGemvRows = 16;
-constexpr int kGemvWaves = 8;
-constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kGemvRound = 64;  // NF4 blocks per row per round
-// LDS stride of one staged row: 16 bytes of padding put the 8-byte reads of
-// 16 rows x 4 lane groups at the same column offset on distinct banks.
-constexpr int kGemvRowStride = kGemvRound * 32 + 16;
-// 16-byte weight chunks per lane per round (16 rows x 2 KB / 512 lanes)
-constexpr int kGemvChunks = kGemvRows * kGemvRound * 2 / kGemvThreads;
-// NF4 block constants per lane per round
-constexpr int kGemvScales = kGemvRows * kGemvRound / kGemvThreads;
-// LDS stride of one staged activation row (a round of 16-bit values + 16 bytes)
-constexpr int kGemvXStride = kGemvRound * 128 + 16;
-
-// Blocks whose activation and A loads are in flight together: 8 for a
-// 16-wide rank tile in 16 bits at 2 waves per SIMD, fewer as the per-block
-// register footprint grows or as more waves share the registers.
-template <typename LT, int JT, int WPE>
-constexpr int gemv_batch() {
-  constexpr int w = JT * (int)(sizeof(LT) / 2) * (WPE / 2);
-  return w >= 8 ? 1 : 8 / w;
-}
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecRows = 64;   // weight rows per workgroup (4 groups of 16, every wave all of them)
+constexpr int kDecChunk = 128; // columns per chunk: 64 packed bytes per row
+constexpr int kDecUMaxSlices = 16;
 
 __device__ __forceinline__ float nf4_immediate(int i) {
   constexpr float cb[16] = QL_NF4_CODEBOOK_VALUES;
@@ -72,475 +60,454 @@ __device__ __forceinline__ float nf4_immediate(int i) {
   return v;
 }
 
-// 16 consecutive LoRA-A values of one rank row, kept raw until use; half(c)
-// gives values 8c .. 8c + 7 as a matrix-core operand in format AT.  LT is
-// AT (used as loaded) or float.
-template <typename AT, typename LT>
-struct ARaw {
-  u32x4 v[2];
-  __device__ __forceinline__ void load(const LT *p) {
-    v[0] = reinterpret_cast<const u32x4 *>(p)[0];
-    v[1] = reinterpret_cast<const u32x4 *>(p)[1];
-  }
-  __device__ __forceinline__ u32x4 half(int c) const { return v[c]; }
+// One chunk's loads for one lane: activation operand words (4 ops), the 16
+// packed bytes of each of the 4 row groups, and the raw block constants of
+// the chunk's two blocks per row group (int8 code + sigma, or fp32 absmax).
+struct DecChunk {
+  u32x4 xv[4];
+  u32x4 wv[4];
+  int cq[4][2];
+  float cs[4][2];
 };
-template <typename AT>
-struct ARaw<AT, float> {
-  float4 v[4];
-  __device__ __forceinline__ void load(const float *p) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const float4 *>(p)[i];
-  }
-  __device__ __forceinline__ u32x4 half(int c) const {
-    const float4 a = v[2 * c], b = v[2 * c + 1];
+
+// 8 16-bit values of a LoRA-A row as a matrix-core operand in format AT
+template <typename AT, typename LT>
+__device__ __forceinline__ u32x4 lora_op8(const LT *p) {
+  if constexpr (sizeof(LT) == 2) {
+    return *reinterpret_cast<const u32x4 *>(p);
+  } else {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
     return u32x4{Half<AT>::pack2(a.x, a.y), Half<AT>::pack2(a.z, a.w), Half<AT>::pack2(b.x, b.y),
                  Half<AT>::pack2(b.z, b.w)};
   }
-};
+}
 
-// Per-block register operands of one lane: 2 x 8 activations and JT x 16 A values.
-template <typename AT, typename LT, int JT>
-struct GemvBlock {
-  u32x4 x0, x1;
-  ARaw<AT, LT> a[JT];
-};
-
-// XM > 0: the round's activations of all M <= XM token rows are staged in
-// LDS once per workgroup (the operand layout repeats a token row across the
-// 16 lanes of a lane group, which would otherwise be 16 / M copies of the
-// same bytes through the load path); XM = 0: read in operand layout.
-// WPE: waves per SIMD the register allocation must allow.  2 (one workgroup
-// per compute unit) leaves the most registers for loads in flight, which is
-// what a grid of at most one workgroup per unit needs; 4 lets two workgroups
-// share a unit, so that a larger grid overlaps one workgroup's round trips
-// with the other's work.
-template <typename AT, typename LT, int JT, bool DQ, int XM, int WPE>
-__global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv_fwd(const uint16_t *__restrict__ x, int M,
-                                                           const uint8_t *__restrict__ packed,
-                                                           BlockScales sc, int64_t N, int64_t K,
-                                                           const LT *__restrict__ A,
-                                                           const LT *__restrict__ B, int32_t r,
-                                                           float s, uint16_t *__restrict__ y,
-                                                           float *__restrict__ u_save,
-                                                           float *__restrict__ part) {
-  __shared__ uint32_t lut[256];
-  __shared__ __attribute__((aligned(16))) uint8_t wt[kGemvRows * kGemvRowStride];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[XM > 0 ? XM * kGemvXStride : 16];
-  __shared__ float scl[kGemvRows][kGemvRound];
-  __shared__ float red[kGemvWaves][16][16];
-  __shared__ float ured[kGemvWaves][16][16 * JT];
-  __shared__ float us[16][16 * JT];
-  __shared__ float bs[16][16 * JT];
+// u = x A^T, rank tile jt (16 ranks) over the contraction chunks [su uc,
+// su uc + uc), summed over the workgroup's waves: upart[su][m][16 jt + j].
+// red: kDecWaves x 16 x 16 floats of LDS.
+template <typename AT, typename LT>
+__device__ __forceinline__ void dec_u_part(const uint16_t *__restrict__ x, int M, int64_t K,
+                                           const LT *__restrict__ A, int32_t r,
+                                           float *__restrict__ upart, int uc, int su, int jt,
+                                           float *red) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int nl = lane & 15, q = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kGemvRows;
-  // Token rows past M and rank rows past r are clamped to valid ones: they
-  // only produce outputs that are never stored or summed.
   const int m = nl < M ? nl : M - 1;
+  const int64_t col0 = (int64_t)su * uc * kDecChunk;
+  const int64_t col1 = col0 + (int64_t)uc * kDecChunk < K ? col0 + (int64_t)uc * kDecChunk : K;
+  const int nsteps = (int)((col1 - col0) / 32);  // K % 64 == 0
+  const int j = 16 * jt + nl < r ? 16 * jt + nl : r - 1;
+  const uint16_t *xp = x + (int64_t)m * K + col0 + 8 * q;
+  const LT *ap = A + (int64_t)j * K + col0 + 8 * q;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // steps wave, wave + 4, ...: four at a time, all their loads issued
+  // before the first op (clamped to a valid step; extra ones not used)
+  for (int s0 = wave; s0 < nsteps; s0 += 4 * kDecWaves) {
+    u32x4 xo[4], ao[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int st = s0 + kDecWaves * i < nsteps ? s0 + kDecWaves * i : s0;
+      xo[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * st);
+      ao[i] = lora_op8<AT>(ap + 32 * st);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + kDecWaves * i < nsteps) acc = Half<AT>::mfma16(xo[i], ao[i], acc);
+  }
+  // acc[v] = partial u[4q + v][16 jt + nl]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * q + v) * 16 + nl] = acc[v];
+  __syncthreads();
+  if (t < 16 * M) {
+    const int mo = t >> 4, jj = t & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) sum += red[(w * 16 + mo) * 16 + jj];
+    if (16 * jt + jj < r) upart[((int64_t)su * M + mo) * r + 16 * jt + jj] = sum;
+  }
+}
+
+// grid.x = U JT + G S (JT = ceil(r / 16)).  Workgroups [0, U JT): u, rank
+// tile b % JT over contraction slice b / JT of uc chunks, partial sums to
+// upart [U][M][r].  The rest: row set b / S (64 rows), contraction
+// split b % S (cps chunks, waves cpw chunks each), partial sums to part
+// [S][M][N].
+template <typename AT, typename LT, bool DQ, bool EV, bool VC>
+__global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ packed, BlockScales sc,
+    int64_t N, int64_t K, const LT *__restrict__ A, int32_t r, float *__restrict__ part,
+    float *__restrict__ upart, int S, int U, int cpw, int uc) {
+  __shared__ uint32_t lut[256];
+  __shared__ float red[kDecWaves][16][kDecRows];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int nl = lane & 15, q = lane >> 4;
+  const int64_t NC = (K + kDecChunk - 1) / kDecChunk;
+  // token row of this lane's activation operand (rows past M repeat the
+  // last one; their results are never stored)
+  const int m = nl < M ? nl : M - 1;
+
+  const int JT = (r + 15) / 16;
+  if ((int)blockIdx.x < U * JT) {
+    dec_u_part<AT, LT>(x, M, K, A, r, upart, uc, blockIdx.x / JT, blockIdx.x % JT, &red[0][0][0]);
+    return;
+  }
+
+  // ---------------- x W^^T over this workgroup's rows and slice --------------
+  if (t < 256) {
+    const uint16_t lo = Half<AT>::bits(nf4_immediate(t >> 4));
+    const uint16_t hi = Half<AT>::bits(nf4_immediate(t & 15));
+    lut[t] = (uint32_t)lo | ((uint32_t)hi << 16);  // element 2i (high nibble) first
+  }
+  const int64_t b = (int64_t)blockIdx.x - (int64_t)U * JT;
+  const int64_t row0 = (b / S) * kDecRows;
+  const int sp = (int)(b % S);
+  const int64_t cps = VC ? (int64_t)kDecWaves * cpw : (NC + S - 1) / S;
+  const int64_t s_end = (sp + 1) * cps < NC ? (sp + 1) * cps : NC;
+  const int64_t c_begin = sp * cps + (int64_t)wave * cpw;
+  const int64_t c_end = c_begin + cpw < s_end ? c_begin + cpw : s_end;
+  const int nloc = c_end > c_begin ? (int)(c_end - c_begin) : 0;
+
   const int64_t KB = K >> 6;
   const int64_t row_bytes = K >> 1;
-  const uint16_t *xrow = x + (int64_t)m * K + 16 * q;
-  const LT *arow[JT];
+  const uint8_t *wsrc[4];
+  int64_t srow[4];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) {
-    const int j = 16 * jt + nl < r ? 16 * jt + nl : r - 1;
-    arow[jt] = A + (int64_t)j * K + 16 * q;
+  for (int g = 0; g < 4; ++g) {
+    const int64_t n = row0 + 16 * g + nl < N ? row0 + 16 * g + nl : N - 1;
+    wsrc[g] = packed + n * row_bytes;
+    srow[g] = n * KB;
   }
+  const uint16_t *xsrc = x + (int64_t)m * K;
   const float mu = DQ ? sc.mu[0] : 0.0f;
-
-  // Every load below is unconditional, its index clamped into the array:
-  // a load under a branch makes the compiler wait for it at the join, which
-  // would serialise the round trips this kernel overlaps.  Values loaded for
-  // clamped indices are masked where they are stored.
-  // This workgroup's rows of B: loaded first, staged in LDS with the first round.
-  constexpr int kBPer = (16 * 16 * JT + kGemvThreads - 1) / kGemvThreads;
-  float bv[kBPer];
+  const bool lo_lane = q < 2;
+  // VC: the codes of all of this wave's chunks (2 cpw <= 16 bytes per row,
+  // starting at a multiple of 2 cpw) as one aligned 16-byte load per row
+  // group, and their one sigma (the 2 cpw blocks lie in one group of 256)
+  u32x4 cvec[4];
+  float cvs[4];
+  int cvo[4];
+  if constexpr (VC) {
+    const int64_t cb = c_begin < NC ? c_begin : NC - 1;
 #pragma unroll
-  for (int i = 0; i < kBPer; ++i) {
-    const int e = t + kGemvThreads * i;
-    const int row = (e / (16 * JT)) & 15, j = e % (16 * JT);
-    const int64_t nn = n0 + row < N ? n0 + row : N - 1;
-    bv[i] = load_as_f32(B, nn * r + (j < r ? j : r - 1));
+    for (int g = 0; g < 4; ++g) {
+      const int64_t i0 = srow[g] + 2 * cb;
+      cvo[g] = (int)(i0 & 15);
+      cvec[g] = *reinterpret_cast<const u32x4 *>(sc.q + (i0 & ~(int64_t)15));
+      cvs[g] = sc.sigma[i0 >> 8];
+    }
   }
-  if (t < 256) {
-    const uint16_t hi = Half<AT>::bits(nf4_immediate(t >> 4));
-    const uint16_t lo = Half<AT>::bits(nf4_immediate(t & 15));
-    lut[t] = (uint32_t)hi | ((uint32_t)lo << 16);
-  }
-
-  constexpr int kBatch = gemv_batch<LT, JT, WPE>();
-  constexpr int kWaveBlocks = kGemvRound / kGemvWaves;  // blocks per wave per full round
-  GemvBlock<AT, LT, JT> bl[kBatch];
-  // loads of blocks first .. first + kBatch - 1 of the round, clamped to its last block
-  auto load_batch = [&](int64_t rb0, int first, int RB) {
+  // Every load is unconditional, at an index clamped into the array (the
+  // last chunk of a contraction with K % 128 == 64 has only its first block:
+  // lane groups 2-3 re-read the first half and that block's constant is 0).
+  auto load_chunk = [&](int64_t c, DecChunk &R) {
+    const int64_t col = c * kDecChunk;
+    const bool two = EV || col + 64 < K;
+    const int qe = (two || q < 2) ? q : q - 2;
+    const uint16_t *xp = xsrc + col + 32 * qe;
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int64_t b = rb0 + (first + i < RB ? first + i : RB - 1);
-      if constexpr (XM == 0) {
-        const u32x4 *xp = reinterpret_cast<const u32x4 *>(xrow + 64 * b);
-        bl[i].x0 = xp[0];
-        bl[i].x1 = xp[1];
-      }
+    for (int j = 0; j < 4; ++j) R.xv[j] = *reinterpret_cast<const u32x4 *>(xp + 8 * j);
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt) bl[i].a[jt].load(arow[jt] + 64 * b);
-    }
-  };
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 uacc[JT], uacc1[1];
-  uacc1[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < 4; ++g)
+      R.wv[g] = *reinterpret_cast<const u32x4 *>(wsrc[g] + 64 * c + 16 * qe);
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) uacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // contraction split blockIdx.y of gridDim.y: whole rounds rb_begin .. rb_end
-  const int64_t rounds = (KB + kGemvRound - 1) / kGemvRound;
-  const int64_t per = (rounds + gridDim.y - 1) / gridDim.y;
-  const int64_t rb_begin = (int64_t)blockIdx.y * per * kGemvRound;
-  const int64_t rb_end = rb_begin + per * kGemvRound < KB ? rb_begin + per * kGemvRound : KB;
-  for (int64_t rb0 = rb_begin; rb0 < rb_end; rb0 += kGemvRound) {
-    const int RB = KB - rb0 < kGemvRound ? (int)(KB - rb0) : kGemvRound;
-    // the round's weight slice: 16 rows x 2 RB chunks of 16 bytes; chunk c is
-    // column chunk c % 128 of row c / 128 (chunks past the slice or rows past
-    // N re-read the slice's first chunk and are not stored)
-    u32x4 wv[kGemvChunks];
-#pragma unroll
-    for (int i = 0; i < kGemvChunks; ++i) {
-      const int c = t + kGemvThreads * i;
-      const int row = c >> 7, cr = c & 127;
-      const bool ok = cr < 2 * RB && n0 + row < N;
-      wv[i] = *reinterpret_cast<const u32x4 *>(packed + (n0 + (ok ? row : 0)) * row_bytes +
-                                                32 * rb0 + 16 * (ok ? cr : 0));
-    }
-    // the round's block constants: entry e is block e % 64 of row e / 64
-    // (rows past N read the last row), loaded raw and combined only after
-    // every load of the round is out
-    int qv[kGemvScales];
-    float sv[kGemvScales];
-#pragma unroll
-    for (int i = 0; i < kGemvScales; ++i) {
-      const int e = t + kGemvThreads * i;
-      const int row = e >> 6, b = e & 63;
-      const int64_t nn = n0 + row < N ? n0 + row : N - 1;
-      const int64_t g = sc.index(nn * KB + rb0 + (b < RB ? b : RB - 1));
-      qv[i] = DQ ? (int)sc.q[g] : 0;
-      sv[i] = DQ ? sc.sigma[g >> 8] : sc.absmax[g];
-    }
-    // the round's activations (XM > 0): row c >> 9, 16-byte chunk c & 511
-    u32x4 xv[XM > 0 ? XM : 1];
-#pragma unroll
-    for (int i = 0; i < XM; ++i) {
-      const int c = t + kGemvThreads * i;
-      const int row = (c >> 9) < M ? (c >> 9) : M - 1;
-      const int cc = (c & 511) < 8 * RB ? (c & 511) : 8 * RB - 1;
-      xv[i] = *reinterpret_cast<const u32x4 *>(x + (int64_t)row * K + 64 * rb0 + 8 * cc);
-    }
-    // this wave's blocks of the round: wb0 .. wb0 + cnt - 1
-    const int wb0 = wave * kWaveBlocks;
-    const int cnt = RB - wb0 < 0 ? 0 : (RB - wb0 < kWaveBlocks ? RB - wb0 : kWaveBlocks);
-    // the first batch's loads go out before the staging stores wait for the
-    // weight slice (at rank tile 8 after them: the registers are needed)
-    // A full round with activations in LDS and one load batch (one 16-rank
-    // tile in 16 bits) issues its A loads only after the staging barrier and
-    // runs all weight ops first: the staging stores then wait for the
-    // weight slice alone, and the A loads fly during the weight ops.
-    const bool late_a = XM > 0 && kBatch == kWaveBlocks && JT < 8 && cnt == kWaveBlocks;
-    if constexpr (JT < 8)
-      if (!late_a) load_batch(rb0, wb0, RB);
-#pragma unroll
-    for (int i = 0; i < kGemvChunks; ++i) {
-      const int c = t + kGemvThreads * i;
-      if ((c & 127) < 2 * RB)
-        *reinterpret_cast<u32x4 *>(wt + (c >> 7) * kGemvRowStride + 16 * (c & 127)) = wv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kGemvScales; ++i) {
-      const int e = t + kGemvThreads * i;
-      scl[e >> 6][e & 63] = DQ ? __builtin_fmaf((float)qv[i], sv[i], mu) : sv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < XM; ++i) {
-      const int c = t + kGemvThreads * i;
-      if ((c & 511) < 8 * RB)
-        *reinterpret_cast<u32x4 *>(xs + (c >> 9) * kGemvXStride + 16 * (c & 511)) = xv[i];
-    }
-    if (rb0 == rb_begin) {
-#pragma unroll
-      for (int i = 0; i < kBPer; ++i) {
-        const int e = t + kGemvThreads * i;
-        if (e < 16 * 16 * JT)
-          bs[e / (16 * JT)][e % (16 * JT)] = (e % (16 * JT)) < r ? bv[i] : 0.0f;
-      }
-    }
-    if constexpr (JT >= 8) load_batch(rb0, wb0, RB);
-    __syncthreads();
-
-    // one block, weight part: 2 ops against the unscaled codes, then the
-    // block constant; returns the activation operand in xr0, xr1
-    auto wpart = [&](const GemvBlock<AT, LT, JT> &g, int bb, u32x4 &xr0, u32x4 &xr1) {
-      const u32x2 w =
-          *reinterpret_cast<const u32x2 *>(wt + nl * kGemvRowStride + 32 * bb + 8 * q);
-      u32x4 wb0v, wb1v;
-      wb0v.x = lut[w.x & 0xFF];
-      wb0v.y = lut[(w.x >> 8) & 0xFF];
-      wb0v.z = lut[(w.x >> 16) & 0xFF];
-      wb0v.w = lut[w.x >> 24];
-      wb1v.x = lut[w.y & 0xFF];
-      wb1v.y = lut[(w.y >> 8) & 0xFF];
-      wb1v.z = lut[(w.y >> 16) & 0xFF];
-      wb1v.w = lut[w.y >> 24];
-      if constexpr (XM > 0) {
-        const uint8_t *xp = xs + (m < XM ? m : XM - 1) * kGemvXStride + 128 * bb + 32 * q;
-        xr0 = *reinterpret_cast<const u32x4 *>(xp);
-        xr1 = *reinterpret_cast<const u32x4 *>(xp + 16);
-      } else {
-        xr0 = g.x0;
-        xr1 = g.x1;
-      }
-      f32x4 part = {0.f, 0.f, 0.f, 0.f};
-      part = Half<AT>::mfma16(xr0, wb0v, part);
-      part = Half<AT>::mfma16(xr1, wb1v, part);
-      // part[v] = sum over the block of x[4q+v][k] * cb[idx[n][k]] for column n = n0 + nl
-      const float a = scl[nl][bb];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(a, part[v], acc[v]);
-    };
-    // one block, bypass part: 2 JT ops against A (at one rank tile, two
-    // accumulator chains)
-    auto upart = [&](const GemvBlock<AT, LT, JT> &g, const u32x4 &xr0, const u32x4 &xr1) {
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        uacc[jt] = Half<AT>::mfma16(xr0, g.a[jt].half(0), uacc[jt]);
-        f32x4 &u1 = JT == 1 ? uacc1[jt] : uacc[jt];
-        u1 = Half<AT>::mfma16(xr1, g.a[jt].half(1), u1);
-      }
-    };
-    auto block = [&](const GemvBlock<AT, LT, JT> &g, int bb) {
-      u32x4 xr0, xr1;
-      wpart(g, bb, xr0, xr1);
-      upart(g, xr0, xr1);
-    };
-    // A wave with all its blocks present (every full round of 4096 columns)
-    // runs branch-free, so that the compiler overlaps the LDS reads and the
-    // matrix ops of different blocks.
-    const bool full = JT < 8 && cnt == kWaveBlocks;  // (rank tile 8: registers are short)
-    if (late_a) {
-      load_batch(rb0, wb0, RB);
-      u32x4 xk0[kWaveBlocks], xk1[kWaveBlocks];
-#pragma unroll
-      for (int i = 0; i < kWaveBlocks; ++i) wpart(bl[i], wb0 + i, xk0[i], xk1[i]);
-#pragma unroll
-      for (int i = 0; i < kWaveBlocks; ++i) upart(bl[i], xk0[i], xk1[i]);
-    } else {
-#pragma unroll
-      for (int i0 = 0; i0 < kWaveBlocks; i0 += kBatch) {
-        if (i0 > 0) load_batch(rb0, wb0 + i0, RB);
-        if (full) {
-#pragma unroll
-          for (int i = 0; i < kBatch; ++i) block(bl[i], wb0 + i0 + i);
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (VC) {
+      } else if constexpr (EV) {
+        // blocks of 64 and K % 128 == 0: the chunk's two block constants
+        // start at an even index and share one sigma; the two codes as one
+        // 2-byte load
+        const int64_t bi = srow[g] + 2 * c;
+        if constexpr (DQ) {
+          R.cq[g][0] = (int)*reinterpret_cast<const uint16_t *>(sc.q + bi);
+          R.cs[g][0] = sc.sigma[bi >> 8];
         } else {
+          const float2 a = *reinterpret_cast<const float2 *>(sc.absmax + bi);
+          R.cs[g][0] = a.x;
+          R.cs[g][1] = a.y;
+        }
+      } else {
 #pragma unroll
-          for (int i = 0; i < kBatch; ++i)
-            if (i0 + i < cnt) block(bl[i], wb0 + i0 + i);
+        for (int h = 0; h < 2; ++h) {
+          const int64_t bi = sc.index(srow[g] + 2 * c + (two ? h : 0));
+          if constexpr (DQ) {
+            R.cq[g][h] = sc.q[bi];
+            R.cs[g][h] = sc.sigma[bi >> 8];
+          } else {
+            R.cq[g][h] = 0;
+            R.cs[g][h] = sc.absmax[bi];
+          }
         }
       }
     }
-    __syncthreads();  // the next round overwrites the staged slice
+  };
+  // the chunk's two block constants of row group g
+  auto consts = [&](const DecChunk &R, int64_t c, int g, bool two, float &a0, float &a1) {
+    if constexpr (VC) {
+      const int o = cvo[g] + 2 * (int)(c - c_begin);
+      const uint32_t d = cvec[g][o >> 2] >> (8 * (o & 3));
+      a0 = __builtin_fmaf((float)(int8_t)(d & 0xFF), cvs[g], mu);
+      a1 = __builtin_fmaf((float)(int8_t)((d >> 8) & 0xFF), cvs[g], mu);
+    } else if constexpr (EV) {
+      if constexpr (DQ) {
+        a0 = __builtin_fmaf((float)(int8_t)(R.cq[g][0] & 0xFF), R.cs[g][0], mu);
+        a1 = __builtin_fmaf((float)(int8_t)(R.cq[g][0] >> 8), R.cs[g][0], mu);
+      } else {
+        a0 = R.cs[g][0];
+        a1 = R.cs[g][1];
+      }
+    } else {
+      a0 = DQ ? __builtin_fmaf((float)R.cq[g][0], R.cs[g][0], mu) : R.cs[g][0];
+      const float a1h = DQ ? __builtin_fmaf((float)R.cq[g][1], R.cs[g][1], mu) : R.cs[g][1];
+      a1 = two ? a1h : 0.0f;
+    }
+  };
+
+  f32x4 yacc[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) yacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const DecChunk &R, int64_t c) {
+    const bool two = EV || c * kDecChunk + 64 < K;
+    u32x4 xl[4], xh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        xl[j][d] = lo_lane ? R.xv[j][d] : 0u;
+        xh[j][d] = lo_lane ? 0u : R.xv[j][d];
+      }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float a0, a1;
+      consts(R, c, g, two, a0, a1);
+      f32x4 pl = {0.f, 0.f, 0.f, 0.f}, ph = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = R.wv[g][j];
+        const u32x4 wo = {lut[w & 0xFF], lut[(w >> 8) & 0xFF], lut[(w >> 16) & 0xFF], lut[w >> 24]};
+        pl = Half<AT>::mfma16(xl[j], wo, pl);
+        ph = Half<AT>::mfma16(xh[j], wo, ph);
+      }
+      // pl[v] / ph[v]: sum over the chunk's first / second block of
+      // x[4q + v][k] * cb[idx[n][k]], n = row0 + 16 g + nl
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        yacc[g][v] = __builtin_fmaf(a0, pl[v], yacc[g][v]);
+        yacc[g][v] = __builtin_fmaf(a1, ph[v], yacc[g][v]);
+      }
+    }
+  };
+
+  DecChunk R0, R1;
+  if (nloc > 0) load_chunk(c_begin, R0);
+  __syncthreads();  // lut
+  if (nloc == 1) {
+    compute(R0, c_begin);
+  } else if (nloc > 1) {
+    // two register sets: the loads of chunk i + 1 fly while chunk i is
+    // multiplied (the last iteration re-reads the last chunk, from cache)
+    for (int i = 0; i < nloc; i += 2) {
+      load_chunk(c_begin + (i + 1 < nloc ? i + 1 : nloc - 1), R1);
+      compute(R0, c_begin + i);
+      if (i + 1 >= nloc) break;
+      load_chunk(c_begin + (i + 2 < nloc ? i + 2 : nloc - 1), R0);
+      compute(R1, c_begin + i + 1);
+    }
   }
 
-  // D[4q + v][nl]: y partials per (m, n) and u partials per (m, j)
+  // yacc[g][v] = partial y[4q + v][row0 + 16 g + nl]: sum over the waves
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave][4 * q + v][nl] = acc[v];
+  for (int g = 0; g < 4; ++g)
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) ured[wave][4 * q + v][16 * jt + nl] = (JT == 1 ? uacc[jt][v] + uacc1[0][v] : uacc[jt][v]);
+    for (int v = 0; v < 4; ++v) red[wave][4 * q + v][16 * g + nl] = yacc[g][v];
   __syncthreads();
-  if (part) {
-    // split contraction: this split's sums over its rounds, the bypass term
-    // added by k_gemv_reduce.  part = y partials [S][M][N], then u partials
-    // [S][M][r] (every row group computes the same u; the first stores it).
-    const int64_t sp = blockIdx.y;
-    if (blockIdx.x == 0) {
-      float *pu = part + (int64_t)gridDim.y * M * N;
-      for (int e = t; e < 16 * 16 * JT; e += kGemvThreads) {
-        const int mo = e / (16 * JT), j = e % (16 * JT);
-        float su = 0.0f;
+  for (int e = t; e < M * kDecRows; e += kDecThreads) {
+    const int mo = e / kDecRows, n = e % kDecRows;
+    float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kGemvWaves; ++w) su += ured[w][mo][j];
-        if (mo < M && j < r) pu[(sp * M + mo) * r + j] = su;
-      }
-    }
-    if (t < 256) {
-      const int mo = t >> 4, no = t & 15;
-      const int64_t nn = n0 + no;
-      if (mo < M && nn < N) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kGemvWaves; ++w) sum += red[w][mo][no];
-        part[(sp * M + mo) * N + nn] = sum;
-      }
-    }
-    return;
-  }
-  for (int e = t; e < 16 * 16 * JT; e += kGemvThreads) {
-    const int mo = e / (16 * JT), j = e % (16 * JT);
-    float su = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kGemvWaves; ++w) su += ured[w][mo][j];
-    us[mo][j] = su;
-    if (u_save && blockIdx.x == 0 && mo < M && j < r) u_save[mo * r + j] = su;
-  }
-  __syncthreads();
-  if (t < 256) {
-    const int mo = t >> 4, no = t & 15;
-    const int64_t nn = n0 + no;
-    if (mo < M && nn < N) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kGemvWaves; ++w) sum += red[w][mo][no];
-      float l = 0.0f;
-      for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[mo][j], bs[no][j], l);
-      y[(int64_t)mo * N + nn] = Half<AT>::bits(__builtin_fmaf(s, l, sum));
-    }
+    for (int w = 0; w < kDecWaves; ++w) sum += red[w][mo][n];
+    if (row0 + n < N) part[((int64_t)sp * M + mo) * N + row0 + n] = sum;
   }
 }
 
-// The contraction splits of k_gemv_fwd summed in split order, then the
-// bypass term, as the single-split epilogue forms it: u[m][j] = sum over
-// splits, y[m][n] = RN(fmaf(s, sum_j u[m][j] B[n][j], sum over splits)).
-// Grid (ceil(N / 256), M); the first column of workgroups stores u_save.
+// y[m][n] = RN(fmaf(s, sum_j u[m][j] B[n][j], sum over splits of x W^^T)),
+// u[m][j] = sum over the u slices in order.  Grid (ceil(N / 256), M): one
+// thread per output; the workgroups of the first column store u_save.
 template <typename AT, typename LT>
-__global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int S, int M,
-                                                     int64_t N, int32_t r,
-                                                     const LT *__restrict__ B, float s,
-                                                     uint16_t *__restrict__ y,
-                                                     float *__restrict__ u_save) {
+__global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ part, int S,
+                                                    const float *__restrict__ upart, int U, int M,
+                                                    int64_t N, int32_t r,
+                                                    const LT *__restrict__ B, float s,
+                                                    uint16_t *__restrict__ y,
+                                                    float *__restrict__ u_save) {
   __shared__ float us[128];
-  const int m = blockIdx.y, t = threadIdx.x;
-  const float *pu = part + (int64_t)S * M * N;
+  const int t = threadIdx.x;
+  const int mo = blockIdx.y;
+  const int64_t n = (int64_t)blockIdx.x * 256 + t;
+  const int64_t nc = n < N ? n : N - 1;
+  // Every load of the thread is issued before the first sum: the first 8
+  // slice partials of y (and of u for threads t < r) at clamped indices, the
+  // row of B (at most 128 values: 16 pieces of 8); more than 8 slices are
+  // added by a tail loop.
+  const int tj = t < r ? t : r - 1;
+  float pv[8], uv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ii = i < S ? i : S - 1;
+    pv[i] = part[((int64_t)ii * M + mo) * N + nc];
+    const int iu = i < U ? i : U - 1;
+    uv[i] = upart[((int64_t)iu * M + mo) * r + tj];
+  }
+  const LT *bp = B + nc * r;
+  u32x4 bw[16 * sizeof(LT) / 2];
+  const int np = r % 8 == 0 ? r / 8 : 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < np) {
+      if constexpr (sizeof(LT) == 2) {
+        bw[i] = *reinterpret_cast<const u32x4 *>(bp + 8 * i);
+      } else {
+        bw[2 * i] = *reinterpret_cast<const u32x4 *>(bp + 8 * i);
+        bw[2 * i + 1] = *reinterpret_cast<const u32x4 *>(bp + 8 * i + 4);
+      }
+    }
+  float base = 0.0f, su = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < S) base += pv[i];
+    if (i < U) su += uv[i];
+  }
+  for (int i = 8; i < S; ++i) base += part[((int64_t)i * M + mo) * N + nc];
+  for (int i = 8; i < U; ++i) su += upart[((int64_t)i * M + mo) * r + tj];
   if (t < r) {
-    float su = 0.0f;
-    for (int sp = 0; sp < S; ++sp) su += pu[((int64_t)sp * M + m) * r + t];
     us[t] = su;
-    if (u_save && blockIdx.x == 0) u_save[(int64_t)m * r + t] = su;
+    if (u_save && blockIdx.x == 0) u_save[(int64_t)mo * r + t] = su;
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + t;
   if (n >= N) return;
-  float sum = 0.0f;
-  for (int sp = 0; sp < S; ++sp) sum += part[((int64_t)sp * M + m) * N + n];
   float l = 0.0f;
-  for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[j], load_as_f32(B, n * r + j), l);
-  y[(int64_t)m * N + n] = Half<AT>::bits(__builtin_fmaf(s, l, sum));
+  if (np > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < np) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float bv;
+          if constexpr (sizeof(LT) == 2)
+            bv = (e & 1) ? Half<LT>::hi(bw[i][e >> 1]) : Half<LT>::lo(bw[i][e >> 1]);
+          else
+            bv = __uint_as_float(bw[2 * i + (e >> 2)][e & 3]);
+          l = __builtin_fmaf(us[8 * i + e], bv, l);
+        }
+      }
+  } else {
+    for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[j], load_as_f32(B, n * r + j), l);
+  }
+  y[(int64_t)mo * N + n] = Half<AT>::bits(__builtin_fmaf(s, l, base));
 }
 
-template <typename AT, typename LT, int JT, int XM, int WPE = 2>
-static void launch_xm(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
-                      const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save, float *part) {
-  if (sc.absmax == nullptr)
-    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, true, XM, WPE>), grid, dim3(kGemvThreads), 0,
-                       stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
-                       u_save, part);
-  else
-    hipLaunchKernelGGL((k_gemv_fwd<AT, LT, JT, false, XM, WPE>), grid, dim3(kGemvThreads), 0,
-                       stream, x, M, packed, sc, N, K, (const LT *)A, (const LT *)B, r, s, y,
-                       u_save, part);
-}
+// Launch plan of a decode forward.
+struct DecPlan {
+  int S;     // contraction splits of the weight stream
+  int cpw;   // chunks per wave
+  int U;     // u slices
+  int uc;    // chunks per u slice
+  int64_t G; // row sets of 64
+  bool ev;   // blocks of 64 and K % 128 == 0: two block constants per chunk, one sigma
+  bool vc;   // ... with double quantisation and runs of cpw = 2^k <= 8 chunks whose
+             // codes sit at a multiple of 2 cpw: one code load per wave and row group
+};
 
-// Compute units of the chip (MI355X): a grid larger than this runs in
-// several rounds of workgroups per unit.
-constexpr unsigned kGemvUnits = 256;
-
-template <typename AT, typename LT, int JT>
-static void launch_jt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
-                      const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save,
-                      float *part) {
-  // More workgroups than units, and a footprint two of which fit a unit's
-  // LDS (rank tiles of 16 or 32, activations staged for one token row or
-  // read in operand layout): two workgroups per unit.  For 2-4 token rows
-  // the one-per-unit form with the rows staged in LDS is faster (14336 x
-  // 4096 weight, 4 rows: 27 against 32 us).
-  if constexpr (JT <= 2) {
-    if (grid.x * grid.y > kGemvUnits && (M == 1 || M > 4)) {
-      if (M == 1)
-        launch_xm<AT, LT, JT, 1, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-      else
-        launch_xm<AT, LT, JT, 0, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-      return;
+// The weight stream is cut into wave-tasks of cpw consecutive 128-column
+// chunks of 64 rows; a workgroup's 4 waves cover 4 cpw consecutive chunks,
+// so the contraction is split in S slices.  The kernel's register use
+// allows 3 resident workgroups of 4 waves per compute unit (256 units).
+// With double quantisation and K % 128 == 0, cpw is the largest power of
+// two up to 8 that still gives 3 workgroups per unit and keeps each wave's
+// 2 cpw codes inside one aligned 16-byte piece (K / 64 a multiple of 2 cpw,
+// N K / 64 of 16), so a wave loads the block constants of all its chunks at
+// once.  Otherwise cpw stays 1 while the tasks fill the resident
+// workgroups; beyond that each wave takes several consecutive chunks.  In
+// both, a wave's loads of its next chunk are in flight while it multiplies
+// the current one.  u takes one workgroup per 4 chunks, at most 16.
+static DecPlan dec_plan(int64_t N, int64_t K, bool dq, int shift) {
+  DecPlan p;
+  const int64_t NC = (K + kDecChunk - 1) / kDecChunk;
+  const int64_t KB = K >> 6;
+  p.G = (N + kDecRows - 1) / kDecRows;
+  p.ev = K % 128 == 0 && shift == 0;
+  p.vc = false;
+  const int64_t resident = (int64_t)256 * 3;
+  if (p.ev && dq && (N * KB) % 16 == 0) {
+    int c = 8;
+    while (c > 1 && (KB % (2 * c) != 0 ||
+                     p.G * ((NC + kDecWaves * c - 1) / (kDecWaves * c)) < resident))
+      c >>= 1;
+    if (KB % (2 * c) == 0) {
+      p.vc = true;
+      p.cpw = c;
+      p.S = (int)((NC + kDecWaves * c - 1) / (kDecWaves * c));
     }
   }
-  if (M == 1)
-    launch_xm<AT, LT, JT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-  else if (M <= 4)
-    launch_xm<AT, LT, JT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-  else
-    launch_xm<AT, LT, JT, 0>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-}
-
-template <typename AT, typename LT>
-static void launch_lt(dim3 grid, hipStream_t stream, const uint16_t *x, int M,
-                      const uint8_t *packed, BlockScales sc, int64_t N, int64_t K, const void *A,
-                      const void *B, int32_t r, float s, uint16_t *y, float *u_save,
-                      float *part) {
-  if (r <= 16) launch_jt<AT, LT, 1>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-  else if (r <= 32) launch_jt<AT, LT, 2>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-  else if (r <= 64) launch_jt<AT, LT, 4>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-  else launch_jt<AT, LT, 8>(grid, stream, x, M, packed, sc, N, K, A, B, r, s, y, u_save, part);
-}
-
-// Workgroups a split contraction aims for: two per compute unit.
-constexpr int64_t kGemvSplitTarget = 2 * kGemvUnits;
-
-// Contraction splits of a decode forward: one unless the row groups leave
-// at least half the units idle and there are rounds to share; no split is
-// left without rounds.  (At 129-256 groups the split's second launch and the
-// smaller register budget cost more than it gains: 4096 x 14336 weight, one
-// token, 23.4 us unsplit against 26.7 split in 2; at 64 groups, 1024 x 14336,
-// 21.0 against 12.6 split in 4.)
-static int gemv_splits(int64_t N, int64_t K) {
-  const int64_t groups = (N + kGemvRows - 1) / kGemvRows;
-  const int64_t rounds = ((K >> 6) + kGemvRound - 1) / kGemvRound;
-  if (rounds < 2 || 2 * groups > kGemvUnits) return 1;
-  int64_t S = (kGemvSplitTarget + groups - 1) / groups;
-  if (S > rounds) S = rounds;
-  if (S < 2) return 1;
-  const int64_t per = (rounds + S - 1) / S;
-  return (int)((rounds + per - 1) / per);
+  if (!p.vc) {
+    const int64_t tasks = p.G * NC, cap = resident * kDecWaves;
+    p.cpw = (int)(tasks <= cap ? 1 : (tasks + cap - 1) / cap);
+    int64_t S = (NC + (int64_t)kDecWaves * p.cpw - 1) / ((int64_t)kDecWaves * p.cpw);
+    const int64_t cps = (NC + S - 1) / S;
+    p.S = (int)((NC + cps - 1) / cps);
+  }
+  int64_t U = (NC + 3) / 4;
+  if (U > kDecUMaxSlices) U = kDecUMaxSlices;
+  p.uc = (int)((NC + U - 1) / U);
+  p.U = (int)((NC + p.uc - 1) / p.uc);
+  return p;
 }
 
 size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r) {
-  const int S = gemv_splits(N, K);
-  return S > 1 ? (size_t)S * M * (N + r) : 0;
+  // the largest of the plans of the weight's formats
+  const DecPlan p = dec_plan(N, K, false, 0), p2 = dec_plan(N, K, true, 0);
+  if (p2.S > p.S) return (size_t)p2.S * M * N + (size_t)p2.U * M * r;
+  return (size_t)p.S * M * N + (size_t)p.U * M * r;
 }
 
 // A 16-bit LoRA factor has the activations' format (checked by the caller).
+// part: gemv_fwd_partial_floats floats of workspace.
 int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *yv, float *u_save,
                     hipStream_t stream, float *part) {
   const uint16_t *x = (const uint16_t *)xv;
   uint16_t *y = (uint16_t *)yv;
-  const int S = part ? gemv_splits(N, K) : 1;
-  const dim3 grid((unsigned)((N + kGemvRows - 1) / kGemvRows), (unsigned)S);
-  float *p = S > 1 ? part : nullptr;
+  const bool dq = sc.absmax == nullptr;
+  const DecPlan p = dec_plan(N, K, dq, sc.shift);
+  float *upart = part + (size_t)p.S * M * N;
+  const dim3 grid((unsigned)(p.U * ((r + 15) / 16) + p.G * p.S));
+  const dim3 fgrid((unsigned)((N + 255) / 256), (unsigned)M);
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
-    if (lora_dtype == QL_F32)
-      launch_lt<AT, float>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save, p);
-    else
-      launch_lt<AT, AT>(grid, stream, x, (int)M, packed, sc, N, K, A, B, r, s, y, u_save, p);
-    if (S > 1) {
-      const dim3 rgrid((unsigned)((N + 255) / 256), (unsigned)M);
-      if (lora_dtype == QL_F32)
-        hipLaunchKernelGGL((k_gemv_reduce<AT, float>), rgrid, dim3(256), 0, stream, p, S, (int)M,
-                           N, r, (const float *)B, s, y, u_save);
-      else
-        hipLaunchKernelGGL((k_gemv_reduce<AT, AT>), rgrid, dim3(256), 0, stream, p, S, (int)M,
-                           N, r, (const AT *)B, s, y, u_save);
-    }
+    auto go = [&](auto *ltag) {
+      using LT = elem_of<decltype(ltag)>;
+      auto main = [&](auto dqt, auto evt, auto vct) {
+        hipLaunchKernelGGL((k_dec_main<AT, LT, decltype(dqt)::value, decltype(evt)::value,
+                                       decltype(vct)::value>),
+                           grid, dim3(kDecThreads), 0, stream, x, (int)M, packed, sc, N, K,
+                           (const LT *)A, r, part, upart, p.S, p.U, p.cpw, p.uc);
+      };
+      using T = std::true_type;
+      using F = std::false_type;
+      if (p.vc) main(T{}, T{}, T{});
+      else if (dq && p.ev) main(T{}, T{}, F{});
+      else if (dq) main(T{}, F{}, F{});
+      else if (p.ev) main(F{}, T{}, F{});
+      else main(F{}, F{}, F{});
+      hipLaunchKernelGGL((k_dec_finish<AT, LT>), fgrid, dim3(256), 0, stream, part, p.S, upart,
+                         p.U, (int)M, N, r, (const LT *)B, s, y, u_save);
+    };
+    if (lora_dtype == QL_F32) go((float *)nullptr);
+    else go((AT *)nullptr);
   });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;

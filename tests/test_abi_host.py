@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 105
+    assert L.ql_abi_version() == 106
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -70,6 +70,42 @@ def test_workspace_sizes():
     nb = 4096 * 4096 // 64
     assert q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 4096, 4096, 0) >= 4 * nb
     assert q.workspace_bytes(7, 1, 1, 1, 1) == 0
+
+
+def _decode_partial_floats(M, N, K, r):
+    """The decode forward's fp32 partials: S contraction slices of y [M, N]
+    and U slices of u [M, r], for the larger of its launch plans (runs of
+    cpw = 2^k <= 8 chunks for double-quantised weights with K % 128 == 0,
+    else one chunk per wave while 3 x 256 workgroups of 4 waves hold them;
+    4 cpw chunks per workgroup; u slices of 4 chunks, at most 16)."""
+    cdiv = lambda a, b: -(-a // b)
+    G, NC, KB = cdiv(N, 64), cdiv(K, 128), K // 64
+    S = []
+    if K % 128 == 0 and (N * KB) % 16 == 0:
+        c = 8
+        while c > 1 and (KB % (2 * c) != 0 or G * cdiv(NC, 4 * c) < 768):
+            c //= 2
+        if KB % (2 * c) == 0:
+            S.append(cdiv(NC, 4 * c))
+    cpw = 1 if G * NC <= 3 * 256 * 4 else cdiv(G * NC, 3 * 256 * 4)
+    S2 = cdiv(NC, 4 * cpw)
+    S.append(cdiv(NC, cdiv(NC, S2)))
+    U = min(16, cdiv(NC, 4))
+    U = cdiv(NC, cdiv(NC, U))
+    return max(S) * M * N + U * M * r
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 4096, 4096, 16), (16, 4096, 4096, 16),
+                                     (1, 8192, 28672, 64), (16, 14336, 4096, 16),
+                                     (5, 200, 4416, 16), (16, 96, 8192, 128),
+                                     (2, 2048, 28672, 16), (1, 1, 64, 1)])
+def test_workspace_covers_decode_partials(M, N, K, r):
+    """qlora_linear_fwd at M <= 16 writes y and u slice sums into its
+    workspace after the M x r u region; the reported size must hold them."""
+    ws = q.workspace_bytes(q.QL_OP_FWD, M, N, K, r)
+    u_region = -(-(M * r * 4) // 256) * 256
+    assert ws >= u_region + 4 * _decode_partial_floats(M, N, K, r)
+    assert ws % 256 == 0
 
 
 # Argument checks run before any launch.  The pointers below are fake but

@@ -420,16 +420,13 @@ def test_decode_config_full_size(orc, M):
 
 
 # Decode-sized forwards (M <= 16) on larger weights, every output and u.
-# The decode kernel takes M <= 16 on weights of up to 2^25 elements; an
-# 8192 x 4096 weight gives it 512 workgroups of 16 rows, more than the chip's
-# 256 compute units (two workgroups per unit at rank tiles of 16 and 32,
-# except for 2-4 token rows).  On the 8B MLP weights it takes M = 1 (gate:
-# 896 workgroups) and M <= 4 on the down weight (256 workgroups of 3.5
-# contraction rounds); other token counts there take the few-token GEMM
-# with fewer than 17 token rows in its 64-row tile.  When the row groups
-# leave half the compute units idle (at most 128 groups of 16 rows) and the
-# contraction has several rounds of 4096 columns, the decode kernel splits
-# the contraction over workgroups.
+# Every M <= 16 takes the decode path: a weight-streaming launch (64 rows x
+# runs of 128-column chunks per workgroup, the contraction split into
+# slices; double-quantised weights with K % 128 == 0 load each wave's block
+# constants at once) whose first workgroups form u slices, then a launch
+# that sums the slices and adds the bypass.  The cases cover one to 56
+# slices, runs of 1 to 8 chunks, ragged row sets, fp32 and 16-bit factors,
+# both storage forms and both compute formats.
 DECODE_LARGE_CASES = [
     # M, N, K, r, act, lora dtype, double quant
     (1, 8192, 4096, 16, torch.bfloat16, torch.bfloat16, True),
@@ -437,18 +434,17 @@ DECODE_LARGE_CASES = [
     (8, 8192, 4096, 16, torch.bfloat16, torch.float32, False),
     (16, 8192, 4096, 32, torch.bfloat16, torch.bfloat16, True),
     (5, 8192, 4096, 32, torch.float16, torch.float32, True),
-    (16, 8192, 4096, 64, torch.bfloat16, torch.bfloat16, True),  # rank tile 64: one per unit
+    (16, 8192, 4096, 64, torch.bfloat16, torch.bfloat16, True),
     (1, 14336, 4096, 16, torch.bfloat16, torch.bfloat16, True),
     (1, 14336, 4096, 32, torch.float16, torch.float16, False),
-    (3, 14336, 4096, 16, torch.bfloat16, torch.bfloat16, True),   # few-token GEMM
-    (16, 14336, 4096, 16, torch.float16, torch.float16, True),    # few-token GEMM
+    (3, 14336, 4096, 16, torch.bfloat16, torch.bfloat16, True),
+    (16, 14336, 4096, 16, torch.float16, torch.float16, True),
     (4, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),
-    (16, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),  # few-token GEMM
-    # decode kernel with the contraction split over workgroups (few row
-    # groups, several rounds of 4096 columns), partials summed by a second launch
-    (2, 2048, 28672, 16, torch.bfloat16, torch.bfloat16, True),   # 7 rounds as 2 + 2 + 2 + 1
-    (1, 1024, 14336, 32, torch.bfloat16, torch.float32, False),   # 4 splits of one round
-    (16, 2048, 16384, 16, torch.float16, torch.float16, True),    # 4 splits, 16 tokens
+    (16, 4096, 14336, 16, torch.bfloat16, torch.bfloat16, True),
+    (2, 2048, 28672, 16, torch.bfloat16, torch.bfloat16, True),
+    (1, 1024, 14336, 32, torch.bfloat16, torch.float32, False),
+    (16, 2048, 16384, 16, torch.float16, torch.float16, True),
+    (1, 8192, 28672, 64, torch.bfloat16, torch.bfloat16, True),   # 70B down shape, one token
 ]
 
 
@@ -466,6 +462,36 @@ def test_decode_large_weights(orc, M, N, K, r, act, lora, dq):
     np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
     y_ref, u_ref = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
                                   host(t["B"]), 32.0, r)
+    tol = F16_TOL if act == torch.float16 else BF16_TOL
+    ey, eu = rel_err(y.float().cpu().numpy(), y_ref), rel_err(u.cpu().numpy(), u_ref)
+    _say(f"  rel err y {ey:.2e} u {eu:.2e}")
+    assert ey <= tol and eu <= tol
+
+
+# Decode-sized forwards with blocks of 128 (the per-element constant path of
+# the streaming kernel) on long contractions.
+DECODE_BLOCK128_CASES = [
+    # M, N, K, r, act, lora dtype, double quant
+    (2, 2048, 28672, 16, torch.bfloat16, torch.bfloat16, True),
+    (16, 1024, 14336, 64, torch.float16, torch.float16, False),
+    (1, 200, 8192, 5, torch.bfloat16, torch.float32, True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,act,lora,dq", DECODE_BLOCK128_CASES)
+def test_decode_block128_long_contraction(orc, M, N, K, r, act, lora, dq):
+    _say(f"decode block 128 M={M} N={N} K={K} r={r} act={act} lora={lora} dq={dq}")
+    t = si.linear_inputs(98, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora,
+                         with_dy=False, sub=M + r)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    W = q.nf4_quantize(d["W"], double_quant=dq, block=128)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], 16.0, u_save=u)
+    torch.cuda.synchronize()
+    st = orc.quantize_nf4(host(t["W"]), double_quant=dq, block=128)
+    np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
+    y_ref, u_ref = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
+                                  host(t["B"]), 16.0, r)
     tol = F16_TOL if act == torch.float16 else BF16_TOL
     ey, eu = rel_err(y.float().cpu().numpy(), y_ref), rel_err(u.cpu().numpy(), u_ref)
     _say(f"  rel err y {ey:.2e} u {eu:.2e}")

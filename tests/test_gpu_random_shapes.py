@@ -41,6 +41,9 @@ def _draw(i):
     M = int(rng.choice([1, 2, 5, 16, 17, 33, 64, 100, 128, 129, 200, 256, 300, 513]))
     N = int(rng.choice([1, 7, 8, 24, 64, 96, 200, 256, 384, 640, 1000, 1536]))
     K = block * int(rng.integers(1, 13))
+    if M <= 16 and rng.integers(0, 2):
+        # decode sizes also on long contractions (many slices and runs)
+        K = block * int(rng.integers(40, 129))
     r = int(rng.choice([1, 3, 8, 16, 17, 32, 64, 100, 128]))
     # scaling s = alpha / r in [0.5, 2], the range of the pages' settings
     alpha = float(r * rng.choice([0.5, 1.0, 2.0]))
