@@ -186,6 +186,28 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
                      void *y, float *u_save, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The forward of qlora_linear_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it takes no workspace argument, and neither it nor its
+ * kernels allocate.  Its workspace is a fixed array of
+ * QL_NOALLOC_WORKSPACE_BYTES bytes inside the library, one per GPU it runs
+ * on, held until the process ends; its device address is looked up on the
+ * first call on each device.  Arguments and results as qlora_linear_fwd
+ * (bit-identical outputs); calls needing more than
+ * QL_NOALLOC_WORKSPACE_BYTES of workspace (ql_workspace_bytes(QL_OP_FWD,
+ * ...)) return QL_EWORKSPACE and enqueue nothing.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (different streams,
+ * or host threads) race and give wrong results.  Nothing in the array needs
+ * to start at zero (every value is written before it is read).
+ * Errors: as qlora_linear_fwd; QL_EWORKSPACE as above; QL_EUNSUPPORTED for
+ * a device index of 64 or more.
+ */
+#define QL_NOALLOC_WORKSPACE_BYTES (32u << 20)
+int qlora_linear_fwd_noalloc(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                             const void *A, const void *B, int32_t lora_dtype, int32_t r,
+                             float alpha, void *y, float *u_save, void *stream);
+
+/*
  * Forward given the rank-r projection (26. ..., Step 3, with the first
  * bypass product x A^T already at hand, e.g. the u_save of an earlier
  * qlora_linear_fwd on the same x when a forward is recomputed):
@@ -319,7 +341,8 @@ const char *ql_strerror(int status);
 /* Host only: ABI version (major * 100 + minor).  The minor version grows
  * whenever an entry point is added or a workspace size changes.
  *   106: the decode forward (M <= 16) sizes its workspace for contraction
- *        slices and u slices on every shape. */
+ *        slices and u slices on every shape.
+ *   107: qlora_linear_fwd_noalloc. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

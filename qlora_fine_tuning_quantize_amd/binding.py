@@ -23,7 +23,8 @@ NF4_BLOCK, NF4_BLOCK_LARGE, DQ_BLOCK = 64, 128, 256
 
 # every extern "C" symbol declared in include/qlora.h
 EXPORTED = ("ql_nf4_sizes", "ql_nf4_sizes_block", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
-            "qlora_linear_fwd", "qlora_linear_fwd_u", "qlora_linear_bwd", "qlora_linear_bwd_acc",
+            "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_fwd_u", "qlora_linear_bwd",
+            "qlora_linear_bwd_acc",
             "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "ql_dropout_mask",
             "ql_adamw_step", "ql_strerror", "ql_abi_version")
 
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.nf4_dequantize.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, sz, p]
     L.qlora_linear_fwd.restype = ctypes.c_int
+    L.qlora_linear_fwd_noalloc.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p, p]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     L.qlora_linear_fwd_u.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p]
     L.qlora_linear_fwd_u.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [p, p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, p, p, sz, p]
@@ -232,6 +235,30 @@ def qlora_linear_fwd(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Te
                                   _ptr(B), _dtype_code(A.dtype), r, float(alpha), _ptr(y),
                                   _ptr(u_save), _ptr(ws), ws.numel(), _stream(x.device)),
            "qlora_linear_fwd")
+    return y
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20
+
+
+def qlora_linear_fwd_noalloc(x: torch.Tensor, W: NF4Weight, A: torch.Tensor, B: torch.Tensor,
+                             alpha: float, y: torch.Tensor | None = None,
+                             u_save: torch.Tensor | None = None) -> torch.Tensor:
+    """qlora_linear_fwd with the library's own fixed per-GPU workspace (no
+    workspace argument, nothing allocated by the call or its kernels); raises
+    for shapes whose workspace exceeds NOALLOC_WORKSPACE_BYTES.  Calls that
+    overlap on one GPU race."""
+    assert x.dim() == 2 and x.is_contiguous() and A.is_contiguous() and B.is_contiguous()
+    M, K = x.shape
+    r = A.shape[0]
+    assert K == W.cols and A.shape == (r, K) and B.shape == (W.rows, r) and A.dtype == B.dtype
+    if y is None:
+        y = torch.empty((M, W.rows), dtype=x.dtype, device=x.device)
+    st = W.struct()
+    _check(lib().qlora_linear_fwd_noalloc(_ptr(x), _dtype_code(x.dtype), M, ctypes.byref(st),
+                                          _ptr(A), _ptr(B), _dtype_code(A.dtype), r, float(alpha),
+                                          _ptr(y), _ptr(u_save), _stream(x.device)),
+           "qlora_linear_fwd_noalloc")
     return y
 
 

@@ -4,10 +4,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace qlora;
 
+// Workspace of qlora_linear_fwd_noalloc: a fixed device array (one copy per
+// GPU, held until the process ends).  Host code never passes its name to a
+// kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and that
+// address is used instead.
+static __device__ __align__(256) uint8_t scratch[QL_NOALLOC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -150,7 +158,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 106; }
+int ql_abi_version(void) { return 107; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -159,7 +167,9 @@ const char *ql_strerror(int status) {
     case QL_ESHAPE: return "unsupported or inconsistent shape";
     case QL_EALIGN: return "pointer not 16-byte aligned";
     case QL_EUNSUPPORTED: return "unsupported configuration";
-    case QL_EWORKSPACE: return "workspace too small";
+    case QL_EWORKSPACE:
+      return "workspace too small (qlora_linear_fwd_noalloc: the call needs more than its fixed "
+             "workspace of QL_NOALLOC_WORKSPACE_BYTES)";
     case QL_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -271,6 +281,42 @@ int qlora_linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *
                      void *y, float *u_save, void *ws, size_t ws_bytes, void *stream) {
   return linear_fwd(x, act_dtype, M, W, A, B, lora_dtype, r, alpha, nullptr, 1.0f, y, u_save, ws,
                     ws_bytes, stream);
+}
+
+// The device address of `scratch` on the current device, looked up on the
+// first call per device (kMaxDevices at most).
+static constexpr int kMaxDevices = 64;
+static void *g_scratch[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+
+static int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QL_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return QL_EUNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch[dev]) return QL_EHIP;
+  *out = g_scratch[dev];
+  return QL_OK;
+}
+
+int qlora_linear_fwd_noalloc(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
+                             const void *A, const void *B, int32_t lora_dtype, int32_t r,
+                             float alpha, void *y, float *u_save, void *stream) {
+  int st = check_nf4(W);
+  if (st) return st;
+  if (M <= 0 || r <= 0 || r > 128) return QL_EINVAL;
+  const size_t need = fwd_ws(M, W->rows, W->cols, r).total;
+  if (need > (size_t)QL_NOALLOC_WORKSPACE_BYTES) return QL_EWORKSPACE;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return linear_fwd(x, act_dtype, M, W, A, B, lora_dtype, r, alpha, nullptr, 1.0f, y, u_save, ws,
+                    (size_t)QL_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
