@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the training step")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of the step instead of direct launches")
+    ap.add_argument("--only", default="",
+                    help="comma-separated extras to run (default: all), e.g. decode_gemv")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -342,15 +344,22 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        result["mlp_8b"] = bench_mlp8b(q, si, dev, args.steps, args.warmup)
-        result["few_tokens"] = bench_few_tokens(q, si, dev)
-        result["dropout"] = bench_dropout(q, si, dev)
-        result["formats"] = bench_formats(q, si, dev)
-        result["compute_dtype"] = bench_compute_dtype(q, si, dev)
-        result["decode_gemv"] = bench_decode(q, si, dev, with_cpu=not args.no_cpu)
-        result["quantize"] = bench_quantize(q, si, dev, with_cpu=not args.no_cpu)
-        result["small_fp32"] = bench_small_fp32(q, si, dev, with_cpu=not args.no_cpu)
-        result["optimizer"] = bench_adamw(q, si, dev)
+        cpu = not args.no_cpu
+        extras = {
+            "mlp_8b": lambda: bench_mlp8b(q, si, dev, args.steps, args.warmup),
+            "few_tokens": lambda: bench_few_tokens(q, si, dev),
+            "dropout": lambda: bench_dropout(q, si, dev),
+            "formats": lambda: bench_formats(q, si, dev),
+            "compute_dtype": lambda: bench_compute_dtype(q, si, dev),
+            "decode_gemv": lambda: bench_decode(q, si, dev, with_cpu=cpu),
+            "quantize": lambda: bench_quantize(q, si, dev, with_cpu=cpu),
+            "small_fp32": lambda: bench_small_fp32(q, si, dev, with_cpu=cpu),
+            "optimizer": lambda: bench_adamw(q, si, dev),
+        }
+        only = [e for e in args.only.split(",") if e]
+        for name, fn in extras.items():
+            if not only or name in only:
+                result[name] = fn()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(si, c)
     print(json.dumps(result), flush=True)
