@@ -716,8 +716,25 @@ def bench_quantize(q, si, dev, with_cpu=True):
         for qq in q_list:
             q.nf4_dequantize(qq, out=deq[:qq.rows * qq.cols].view(qq.rows, qq.cols))
 
-    qms = timed(quant_all, 3, 1)
-    dms = timed(dequant_all, 3, 1)
+    qms_eager = timed(quant_all, 3, 1)
+    dms_eager = timed(dequant_all, 3, 1)
+    # the same passes replayed from HIP graphs (no per-call host work: 224
+    # launches of a few microseconds each would otherwise be host-bound)
+    graphs = []
+    for fn in (quant_all, dequant_all):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    qms = timed(graphs[0].replay, 5, 1)
+    dms = timed(graphs[1].replay, 5, 1)
+    del graphs
     stored = sum(qq.storage_bytes() for qq in q_list)
     q_bytes = 2 * n_total + stored
     d_bytes = stored + 2 * n_total
@@ -726,11 +743,14 @@ def bench_quantize(q, si, dev, with_cpu=True):
            "params": n_total, "bits_per_param": round(8 * stored / n_total, 5),
            "quantize_ms": round(qms, 3), "quantize_GBps": round(q_bytes / (qms * 1e-3) / 1e9, 1),
            "dequantize_ms": round(dms, 3),
-           "dequantize_GBps": round(d_bytes / (dms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+           "dequantize_GBps": round(d_bytes / (dms * 1e-3) / 1e9, 1), "unit": "GB/s",
+           "launch": "HIP graph replay of each pass (224 calls)",
+           "quantize_ms_eager": round(qms_eager, 3), "dequantize_ms_eager": round(dms_eager, 3)}
     out["quantize_hbm_frac"] = round(out["quantize_GBps"] / PEAK_HBM_GBS, 4)
     out["dequantize_hbm_frac"] = round(out["dequantize_GBps"] / PEAK_HBM_GBS, 4)
     log(f"quantize {qms:.2f} ms ({out['quantize_GBps']} GB/s), dequantize {dms:.2f} ms "
-        f"({out['dequantize_GBps']} GB/s), {out['bits_per_param']} bits/param")
+        f"({out['dequantize_GBps']} GB/s) in graphs; eager {qms_eager:.2f} / {dms_eager:.2f} ms; "
+        f"{out['bits_per_param']} bits/param")
     del ws_list, q_list, deq
     torch.cuda.empty_cache()
     if with_cpu:

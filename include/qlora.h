@@ -128,7 +128,9 @@ int ql_nf4_sizes_block(int64_t rows, int64_t cols, int32_t block, int32_t double
  *   QL_OP_QUANTIZE: M and r ignored, N x K is the weight (double-quant form;
  *                   the single-level form needs none).
  *   QL_OP_FWD / QL_OP_BWD: M tokens, N = out_features, K = in_features, rank r.
- * Returns 0 for invalid sizes.  The workspace never scales with N * K.
+ * Returns 0 for invalid sizes.  The forward and backward workspaces never
+ * scale with N * K; the quantisation one holds the fp32 block constants
+ * (4 bytes per 64 weights) plus a fixed 48 KiB.
  */
 size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
 
@@ -143,7 +145,10 @@ size_t ql_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
  * a = max |w|; v = w / a (correctly rounded fp32 division); the
  * index is the nearest codepoint of v, ties to the lower index; a zero block
  * codes every element as index 7 (the exact zero).  Double quantisation:
- * mu = mean of all a (exact sum, fp64 division, rounded to fp32);
+ * mu = fp32(fp64(S) / nb), where S is the exact sum of all nb constants (an
+ * integer multiple of 2^-149 accumulated in integer arithmetic, so exact for
+ * any spread of magnitudes), fp64(S) its round-to-nearest-even, and the
+ * division correctly rounded;
  * per 256 constants sigma = max|a - mu| / 127 (fp32), code =
  * clamp(round-half-even((a - mu) / sigma), -127, 127), 0 when sigma == 0.
  *   ws, ws_bytes  device workspace of ql_workspace_bytes(QL_OP_QUANTIZE, ...)
@@ -342,7 +347,9 @@ const char *ql_strerror(int status);
  * whenever an entry point is added or a workspace size changes.
  *   106: the decode forward (M <= 16) sizes its workspace for contraction
  *        slices and u slices on every shape.
- *   107: qlora_linear_fwd_noalloc. */
+ *   107: qlora_linear_fwd_noalloc.
+ *   108: the double-quantised nf4_quantize keeps 48 KiB of exact partial sums
+ *        of the block constants in place of fp64 partials. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

@@ -69,7 +69,7 @@ QuantWs quant_ws(int64_t n) {
   QuantWs w;
   w.absmax = 0;
   w.partial = round_up((size_t)nb * 4);
-  w.total = w.partial + round_up(dq_partial_count(nb) * 8);
+  w.total = w.partial + round_up((size_t)kQdMaxGroups * kQdDigits * 8);
   return w;
 }
 
@@ -158,7 +158,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 107; }
+int ql_abi_version(void) { return 108; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -218,7 +218,6 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
   if (!w || check_dtype(w_dtype)) return QL_EINVAL;
   if (!aligned16(w)) return QL_EALIGN;
   const int64_t n = q->rows * q->cols;
-  const int64_t nb = ceil_div(n, q->block);
   hipStream_t s = (hipStream_t)stream;
   if (!q->double_quant)
     return launch_nf4_quantize(w, w_dtype, n, q->block, q->packed, q->absmax, s);
@@ -227,10 +226,9 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
   uint8_t *base = (uint8_t *)ws;
   float *absmax = (float *)(base + L.absmax);
-  double *partial = (double *)(base + L.partial);
-  st = launch_nf4_quantize(w, w_dtype, n, q->block, q->packed, absmax, s);
-  if (st) return st;
-  return launch_double_quant(absmax, nb, partial, q->absmax_q, q->absmax_scale, q->absmax_mean, s);
+  unsigned long long *partial = (unsigned long long *)(base + L.partial);
+  return launch_nf4_quantize_dq(w, w_dtype, n, q->block, q->packed, absmax, partial, q->absmax_q,
+                                q->absmax_scale, q->absmax_mean, s);
 }
 
 int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) {

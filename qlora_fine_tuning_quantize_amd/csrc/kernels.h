@@ -12,9 +12,15 @@ namespace qlora {
 // block: 64 or 128 elements per NF4 block
 int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
                         float *absmax, hipStream_t stream);
-size_t dq_partial_count(int64_t nb);
-int launch_double_quant(const float *absmax, int64_t nb, double *partial, int8_t *q, float *sigma,
-                        float *mean_out, hipStream_t stream);
+// Double-quantised form: quantisation plus exact partial sums of the block
+// constants (at most kQdMaxGroups partials of kQdDigits 64-bit counters),
+// then mu and the 8-bit codes.  nb >= 2^31 constants: QL_EUNSUPPORTED.
+constexpr int kQdMaxGroups = 512;
+constexpr int kQdDigits = 12;    // ten 32-bit digit positions, an infinity count, a pad
+constexpr int kQdInfDigit = 10;
+int launch_nf4_quantize_dq(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
+                           float *absmax, unsigned long long *partial, int8_t *q, float *sigma,
+                           float *mean_out, hipStream_t stream);
 int launch_nf4_dequantize(const uint8_t *packed, int64_t n, BlockScales sc, void *out,
                           int out_dtype, hipStream_t stream);
 

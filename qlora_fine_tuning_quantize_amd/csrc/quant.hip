@@ -10,6 +10,8 @@
 // (26. QLoRA and 4bit Quantization, Step 4).
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace qlora {
@@ -112,16 +114,115 @@ __device__ __forceinline__ float max_lanes(float m) {
 }
 
 // ---------------------------------------------------------------------------
-// K1: a wave owns 2 runs of 512 consecutive elements (8 NF4 blocks of 64,
-// or 4 of 128); in every run lane l takes the 8 elements 8l .. 8l + 7, so
-// each block is held by a group of BLK / 8 lanes and every load and store
-// instruction of the wave covers one contiguous span.  All loads are issued first.  The group
-// reduces |w| (DPP), then each lane finds its 8 indices and packs them into
-// one 32-bit word.  The indices are those of the correctly rounded w / a:
-// each lane takes a reciprocal of a once and the index of w times it; a lane with
-// any element in a guard band (or with a block maximum outside the normal
-// range) redoes its 8 elements with the division.
+// Quantisation proper.  Elements go in runs of 512 consecutive ones (8 NF4
+// blocks of 64, or 4 of 128); in every run lane l takes the 8 elements
+// 8l .. 8l + 7, so each block is held by a group of BLK / 8 lanes and every
+// load and store instruction of the wave covers one contiguous span.  The
+// group reduces |w| (DPP), then each lane finds its 8 indices and packs them
+// into one 32-bit word.  The indices are those of the correctly rounded
+// w / a: each lane takes a reciprocal of a once and the index of w times it;
+// a lane with any element in a guard band (or with a block maximum outside
+// the normal range) redoes its 8 elements with the division.
 // ---------------------------------------------------------------------------
+
+// The raw 16 bytes (16-bit types) or 32 bytes (fp32) of a lane's 8 elements.
+template <typename T>
+struct RunRaw {
+  u32x4 v[sizeof(T) == 2 ? 1 : 2];
+};
+
+// Load the lane's 8 elements of the run starting at e0.  A run that is not
+// whole loads from the start of the weight instead (n >= 8 there) and is
+// reloaded element by element in quant_run; with n < 8 nothing is loaded.
+// CHECKED = false promises e0 + 8 <= n (a straight load, no branch).
+template <typename T, bool CHECKED = true>
+__device__ __forceinline__ void load_run(const T *__restrict__ w, int64_t n, int64_t e0,
+                                         RunRaw<T> &raw) {
+  const int64_t ec = !CHECKED || e0 + 8 <= n ? e0 : 0;
+  if (CHECKED && n < 8) {  // uniform: too short for any 8-element load
+    for (int i = 0; i < (int)(sizeof(raw.v) / 16); ++i) raw.v[i] = u32x4{0u, 0u, 0u, 0u};
+  } else {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(raw.v) / 16); ++i)
+      raw.v[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(w + ec) + 16 * i);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void widen_run(const RunRaw<T> &raw, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {  // bf16 or fp16: widening is exact
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = Half<T>::lo(raw.v[0][i]);
+      v[2 * i + 1] = Half<T>::hi(raw.v[0][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(raw.v[i >> 2][i & 3]);
+  }
+}
+
+// Code the lane's 8 values of a run: returns the packed word (element i in
+// byte i / 2, high nibble for even i) and the group's block maximum in m.
+// Wave-uniform call (the group reduction and the guard ballot span the wave).
+template <int BLK>
+__device__ __forceinline__ uint32_t code_run(const float (&v)[8], const BucketEntry *tab, int lane,
+                                             float &m_out) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = max_lanes<BLK / 8>(m);
+  m_out = m;
+  uint32_t word = 0x77777777u;  // a zero block: every element is the exact zero
+  if (m != 0.0f) {
+    bool slow = !(m >= 0x1p-125f && m <= 0x1p125f);
+    if (!slow) {
+      const float rm = __builtin_amdgcn_rcpf(m);
+      uint64_t near = 0;
+      word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        word |= nf4_index_fast(v[i] * rm, tab, near) << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4);
+      slow = (near >> lane) & 1u;
+    }
+    if (slow) {
+      word = 0;
+      for (int i = 0; i < 8; ++i)
+        word |= nf4_index(v[i] / m, tab) << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4);
+    }
+  }
+  return word;
+}
+
+// Quantise the lane's 8 elements of the run at e0 (lane offset included),
+// with bounds checks: writes the packed word and, from the first lane of each
+// group, the block constant.  Returns the block maximum (0 past the end).
+template <typename T, int BLK>
+__device__ __forceinline__ float quant_run(const T *__restrict__ w, int64_t n, int64_t e0,
+                                           float (&v)[8], const BucketEntry *tab, int lane,
+                                           uint8_t *__restrict__ packed,
+                                           float *__restrict__ absmax) {
+  if (e0 + 8 > n) {  // the ragged end (or past it): elements past n count as 0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < n) ? load_as_f32(w, e0 + i) : 0.0f;
+  }
+  float m;
+  uint32_t word = code_run<BLK>(v, tab, lane, m);
+  if (e0 >= n) return 0.0f;  // lanes past the end only helped the group reduction
+  if (e0 + 8 <= n) {
+    *reinterpret_cast<uint32_t *>(packed + (e0 >> 1)) = word;
+  } else {
+    // nibbles of elements past n are 0
+    for (int i = 0; i < 8; ++i)
+      if (e0 + i >= n) word &= ~(0xFu << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4));
+    for (int b = 0; b < 4; ++b)
+      if (e0 + 2 * b < n) packed[(e0 >> 1) + b] = (uint8_t)(word >> (8 * b));
+  }
+  if ((lane & (BLK / 8 - 1)) == 0) absmax[e0 / BLK] = m;
+  return m;
+}
+
+// Single-level form: a wave owns 2 runs; all loads are issued first.
 template <typename T, int BLK>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, int64_t n,
                                                       uint8_t *__restrict__ packed,
@@ -131,179 +232,295 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, i
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
   constexpr int R = 2;
-  int64_t e0[R];
-  float v[R][8];
+  RunRaw<T> raw[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    e0[j] = wave * (R * 512) + j * 512 + lane * 8;
-    // a run that is not whole loads from the start instead (n >= 8 there)
-    // and is reloaded element by element below
-    const int64_t ec = e0[j] + 8 <= n ? e0[j] : 0;
-    if (n < 8) {  // uniform: too short for any 8-element load
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
-    } else if constexpr (sizeof(T) == 2) {  // bf16 or fp16: widening is exact
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(w + ec);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[j][2 * i] = Half<T>::lo(raw[i]);
-        v[j][2 * i + 1] = Half<T>::hi(raw[i]);
-      }
-    } else {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(w + ec);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(w + ec + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[j][i] = a[i];
-        v[j][4 + i] = b[i];
-      }
-    }
-  }
+  for (int j = 0; j < R; ++j) load_run(w, n, wave * (R * 512) + j * 512 + lane * 8, raw[j]);
   build_buckets(tab, th, threadIdx.x);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if (e0[j] + 8 > n) {  // the ragged end (or past it): elements past n count as 0
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = (e0[j] + i < n) ? load_as_f32(w, e0[j] + i) : 0.0f;
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
-    m = max_lanes<BLK / 8>(m);
-    if (e0[j] >= n) continue;  // after the group reduction: lanes past the end only helped
-    // element i goes to byte i / 2, high nibble for even i
-    uint32_t word = 0x77777777u;  // a zero block: every element is the exact zero
-    if (m != 0.0f) {
-      bool slow = !(m >= 0x1p-125f && m <= 0x1p125f);
-      if (!slow) {
-        const float rm = __builtin_amdgcn_rcpf(m);
-        uint64_t near = 0;
-        word = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          word |= nf4_index_fast(v[j][i] * rm, tab, near)
-                  << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4);
-        slow = (near >> lane) & 1u;
-      }
-      if (slow) {
-        word = 0;
-        for (int i = 0; i < 8; ++i)
-          word |= nf4_index(v[j][i] / m, tab) << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4);
-      }
-    }
-    if (e0[j] + 8 <= n) {
-      *reinterpret_cast<uint32_t *>(packed + (e0[j] >> 1)) = word;
-    } else {
-      // nibbles of elements past n are 0
-      for (int i = 0; i < 8; ++i)
-        if (e0[j] + i >= n) word &= ~(0xFu << ((i & 1) ? 8 * (i >> 1) : 8 * (i >> 1) + 4));
-      for (int b = 0; b < 4; ++b)
-        if (e0[j] + 2 * b < n) packed[(e0[j] >> 1) + b] = (uint8_t)(word >> (8 * b));
-    }
-    if ((lane & (BLK / 8 - 1)) == 0) absmax[e0[j] / BLK] = m;
+    float v[8];
+    widen_run(raw[j], v);
+    quant_run<T, BLK>(w, n, wave * (R * 512) + j * 512 + lane * 8, v, tab, lane, packed, absmax);
   }
 }
 
 // ---------------------------------------------------------------------------
-// K2: fixed-order fp64 partial sums of the block constants, 8192 per
-// workgroup (each lane sums 32 consecutive values in index order, then a
-// fixed binary tree over the 256 lanes).
+// Double-quantised form, pass 1: the quantisation above, plus the exact sum
+// of the block constants (Gemma lesson 09, sec. 9.2.2 centres the constants
+// on their mean).  A block constant a >= 0 is an integer multiple of 2^-149:
+// a = M 2^(e-1) 2^-149 with M its 24-bit significand (hidden bit included)
+// and e its biased exponent (e = 1 for subnormals, M then without the hidden
+// bit), so a 2^149 < 2^277.  The workgroup adds M 2^(e-1) into ten 32-bit
+// digit positions kept as 64-bit counters in LDS (integer atomics: the result
+// does not depend on their order), so the sum is exact whatever the range of
+// the constants; an infinite constant is counted apart.  Each workgroup
+// writes its counters as one partial sum (digit-major: partial[d * grid +
+// workgroup]).  The workgroups walk the runs in a grid-stride loop (grid
+// capped at kQdMaxGroups, so the partials stay few), kQdRuns runs per wave
+// per step.
 // ---------------------------------------------------------------------------
-constexpr int kDqSumChunk = 8192;
+constexpr int kQdThreads = 1024;
+constexpr int kQdRuns = 2;  // runs of 512 elements per wave and step
 
-__global__ __launch_bounds__(256) void k_dq_partial_sums(const float *__restrict__ a, int64_t nb,
-                                                         double *__restrict__ partial) {
-  __shared__ double sh[256];
-  const int64_t base = (int64_t)blockIdx.x * kDqSumChunk + threadIdx.x * 32;
-  float v[32];
-  if (base + 32 <= nb) {  // 8 loads of 16 bytes, all in flight before the sum
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 q = *reinterpret_cast<const f32x4 *>(a + base + 4 * i);
-      v[4 * i] = q[0]; v[4 * i + 1] = q[1]; v[4 * i + 2] = q[2]; v[4 * i + 3] = q[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = base + i < nb ? a[base + i] : 0.0f;
-  }
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) s += (double)v[i];
-  sh[threadIdx.x] = s;
-  __syncthreads();
-  for (int stride = 128; stride > 0; stride >>= 1) {
-    if (threadIdx.x < stride) sh[threadIdx.x] += sh[threadIdx.x + stride];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) partial[blockIdx.x] = sh[0];
+// v 2^sh (in units of 2^-149) into the digit counters; v < 2^64, sh <= 253.
+__device__ __forceinline__ void add_shifted(unsigned long long *dig, uint64_t v, int sh) {
+  const int d = sh >> 5, o = sh & 31;
+  const uint64_t lo = v << o;                 // low 64 bits of v 2^o
+  const uint64_t hi = o ? v >> (64 - o) : 0;  // the bits above them (< 2^31)
+  atomicAdd(&dig[d], lo & 0xFFFFFFFFull);
+  if (lo >> 32) atomicAdd(&dig[d + 1], lo >> 32);
+  if (hi) atomicAdd(&dig[d + 2], hi);
 }
 
-// ---------------------------------------------------------------------------
-// K3: one wave per 256 block constants (4 per lane), 4 waves per workgroup.
-// Every wave first reduces the partial sums in the same fixed order (lane l
-// sums partials l, l + 64, ... in increasing order, then a fixed tree over
-// the 64 lanes whose result lane 0 broadcasts), so all agree on mu.  Then
-// d = a - mu, sigma = max|d| / 127, code = clamp(rint(d / sigma), +-127).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ double shfl_down_f64(double v, int delta) {
-  const int lo = __shfl_down(__double2loint(v), delta, 64);
-  const int hi = __shfl_down(__double2hiint(v), delta, 64);
-  return __hiloint2double(hi, lo);
+// A lane's running sum of the constants it owns, acc 2^base: a constant
+// M 2^sh with base <= sh <= base + 24 adds M << (sh - base) (< 2^48) to acc,
+// which is moved into the digits before it could reach 2^63; the first
+// constant sets base = sh - 8 (so constants 2^8 times smaller still fit),
+// and constants outside the window go to the digits directly.  The
+// constants of one weight rarely span more than a few binades, so the digits
+// (LDS atomics) are touched about once per lane.
+struct LaneSum {
+  uint64_t acc;
+  int base;
+};
+
+__device__ __forceinline__ void lane_add(LaneSum &S, float m, unsigned long long *dig) {
+  const uint32_t u = __float_as_uint(m);
+  const uint32_t e = u >> 23;  // m >= 0: no sign bit
+  if (e == 255u) {
+    atomicAdd(&dig[kQdInfDigit], 1ull);
+    return;
+  }
+  const uint64_t M = e ? ((u & 0x7FFFFFu) | 0x800000u) : (u & 0x7FFFFFu);
+  if (M == 0) return;
+  const int sh = e ? (int)e - 1 : 0;  // m 2^149 = M 2^sh, sh <= 253
+  if (S.base < 0) S.base = sh > 8 ? sh - 8 : 0;
+  const int k = sh - S.base;
+  if (k < 0 || k > 24) {
+    add_shifted(dig, M, sh);
+    return;
+  }
+  if (S.acc >> 62) {
+    add_shifted(dig, S.acc, S.base);
+    S.acc = 0;
+  }
+  S.acc += M << k;
 }
 
-__global__ __launch_bounds__(256) void k_dq_codes(const float *__restrict__ a, int64_t nb,
-                                                  const double *__restrict__ partial, int n_partial,
-                                                  int8_t *__restrict__ q, float *__restrict__ sigma,
-                                                  float *__restrict__ mean_out) {
+template <typename T, int BLK>
+__global__ __launch_bounds__(kQdThreads, 8) void k_nf4_quantize_dq(const T *__restrict__ w, int64_t n,
+                                                                uint8_t *__restrict__ packed,
+                                                                float *__restrict__ absmax,
+                                                                NF4Thresholds th,
+                                                                unsigned long long *__restrict__ partial) {
+  __shared__ BucketEntry tab[kBuckets];
+  __shared__ unsigned long long dig[kQdDigits];
   const int lane = threadIdx.x & 63;
-  const int64_t b2 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // this wave's DQ block
-  const int64_t j0 = b2 * 256 + 4 * lane;
-  // the lane's 4 constants (issued before the partial sums are reduced)
-  float av[4];
-  const bool full = j0 + 4 <= nb;
-  if (full) {
-    const f32x4 t = *reinterpret_cast<const f32x4 *>(a + j0);
-    av[0] = t[0]; av[1] = t[1]; av[2] = t[2]; av[3] = t[3];
-  } else {
+  constexpr int WPG = kQdThreads / 64;
+  constexpr int R = kQdRuns;
+  const int64_t step = (int64_t)gridDim.x * WPG;
+  const int64_t full = n / (R * 512);  // steps wholly inside the weight
+  // the wave's step index, wave-uniform (scalar) for the address math
+  int64_t c = (int64_t)blockIdx.x * WPG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  build_buckets(tab, th, threadIdx.x);
+  if (threadIdx.x < kQdDigits) dig[threadIdx.x] = 0;
+  __syncthreads();
+  LaneSum lsum{0ull, -1};
+  RunRaw<T> raw[R];
+  // Whole steps: all R loads of a step are issued together, then the step is
+  // coded and stored.  (Loads and stores share one completion counter, so a
+  // load issued ahead of a step's stores would be waited for together with
+  // them: the overlap of memory and coding comes from the other waves of the
+  // CU instead.)
+  for (; c < full; c += step) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = j0 + i < nb ? a[j0 + i] : 0.0f;
-  }
-  double s = 0.0;
-  for (int i = lane; i < n_partial; i += 64) s += partial[i];
+    for (int j = 0; j < R; ++j) load_run<T, false>(w, n, c * (R * 512) + j * 512 + lane * 8, raw[j]);
+    uint32_t *pk = reinterpret_cast<uint32_t *>(packed + c * (R * 256)) + lane;
+    float *am = absmax + c * (R * 512 / BLK) + lane / (BLK / 8);
 #pragma unroll
-  for (int delta = 32; delta > 0; delta >>= 1) s += shfl_down_f64(s, delta);
-  s = __hiloint2double(__shfl(__double2hiint(s), 0, 64), __shfl(__double2loint(s), 0, 64));
-  const float mu = (float)(s / (double)nb);
-  if (b2 * 256 >= nb) return;  // after the wave-wide steps: a wave past the end only helped
-  float d[4], amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    d[i] = j0 + i < nb ? av[i] - mu : 0.0f;
-    amax = fmaxf(amax, fabsf(d[i]));
-  }
-#pragma unroll
-  for (int delta = 32; delta > 0; delta >>= 1) amax = fmaxf(amax, __shfl_xor(amax, delta, 64));
-  const float sg = amax / 127.0f;
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float c = 0.0f;
-    if (sg != 0.0f) {
-      c = __builtin_rintf(d[i] / sg);
-      c = fminf(fmaxf(c, -127.0f), 127.0f);
+    for (int j = 0; j < R; ++j) {
+      float v[8], m;
+      widen_run(raw[j], v);
+      pk[j * 64] = code_run<BLK>(v, tab, lane, m);
+      am[j * (512 / BLK)] = m;  // every lane of the group stores the same m
+      if ((lane & (BLK / 8 - 1)) == 0) lane_add(lsum, m, dig);
     }
-    word |= ((uint32_t)(int)c & 0xFFu) << (8 * i);
   }
-  if (full && ((uintptr_t)q & 3u) == 0) {
-    *reinterpret_cast<uint32_t *>(q + j0) = word;
-  } else {  // ragged end, or a code array without 4-byte alignment
-    for (int i = 0; i < 4; ++i)
-      if (j0 + i < nb) q[j0 + i] = (int8_t)(word >> (8 * i));
+  if (c * (R * 512) < n) {  // the ragged last step (c == full), wave-uniform
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int64_t e0 = c * (R * 512) + j * 512 + lane * 8;
+      load_run(w, n, e0, raw[j]);
+      float v[8];
+      widen_run(raw[j], v);
+      const float m = quant_run<T, BLK>(w, n, e0, v, tab, lane, packed, absmax);
+      if ((lane & (BLK / 8 - 1)) == 0 && e0 < n) lane_add(lsum, m, dig);
+    }
   }
-  if (lane == 0) {
-    sigma[b2] = sg;
-    if (b2 == 0) mean_out[0] = mu;
+  if (lsum.acc) add_shifted(dig, lsum.acc, lsum.base);
+  __syncthreads();
+  // digit-major: partial[d * gridDim.x + workgroup]
+  if (threadIdx.x < kQdDigits) partial[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = dig[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// Double-quantised form, pass 2: every workgroup (16 waves) first adds the
+// partial sums digit by digit (64-bit integers: exact), carries them into
+// 32-bit limbs and rounds the exact sum S once to fp64 (nearest, ties to
+// even); mu = fp32(fp64(S) / nb), the fp64 division correctly rounded.  Then
+// each wave takes DQ blocks of 256 constants (4 per lane) in a grid-stride
+// loop: d = a - mu, sigma = max|d| / 127, code = clamp(rint(d / sigma),
+// +-127).  The first block's constants are loaded before the sum.
+// ---------------------------------------------------------------------------
+
+// 64-bit wave sum (shuffles; the value of every lane is the sum).
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int delta = 32; delta > 0; delta >>= 1) v += __shfl_xor(v, delta, 64);
+  return v;
+}
+
+// L[i] of a 10-limb array held in registers (0 past the end).
+__device__ __forceinline__ uint32_t limb(const uint32_t (&L)[10], int i) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) r = k == i ? L[k] : r;
+  return r;
+}
+
+// Bits [lo, lo + 64) of the little-endian limbs L.
+__device__ __forceinline__ uint64_t limb_bits(const uint32_t (&L)[10], int lo) {
+  const int w = lo >> 5, o = lo & 31;
+  const uint64_t low = (uint64_t)limb(L, w) | ((uint64_t)limb(L, w + 1) << 32);
+  const uint64_t high = limb(L, w + 2);
+  return o ? (low >> o) | (high << (64 - o)) : low;
+}
+
+// mu from the digit totals (one thread; the limbs stay in registers).
+__device__ float exact_mean(const unsigned long long *tot, int64_t nb) {
+  if (tot[kQdInfDigit] != 0) return __builtin_huge_valf();
+  uint32_t L[10];
+  uint64_t carry = 0;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const uint64_t t = tot[k] + carry;  // tot[k] < 2^64 - 2^32, carry < 2^32
+    L[k] = (uint32_t)t;
+    carry = t >> 32;
+  }
+  // S < 2^317: the carry out of limb 9 is 0
+  int top = -1;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) top = L[k] ? k : top;
+  double sum = 0.0;
+  if (top >= 0) {
+    int p = 32 * top + 31 - __builtin_clz(limb(L, top));  // leading bit of S
+    if (p < 53) {
+      sum = ldexp((double)limb_bits(L, 0), -149);  // exact
+    } else {
+      uint64_t m = limb_bits(L, p - 52) & ((1ull << 53) - 1);
+      const int rp = p - 53;  // round bit
+      const uint32_t lr = limb(L, rp >> 5);
+      const bool round = (lr >> (rp & 31)) & 1u;
+      bool sticky = (lr & ((1u << (rp & 31)) - 1u)) != 0;
+#pragma unroll
+      for (int k = 0; k < 10; ++k) sticky |= k < (rp >> 5) && L[k] != 0;
+      if (round && (sticky || (m & 1))) {
+        ++m;
+        if (m >> 53) {
+          m >>= 1;
+          ++p;
+        }
+      }
+      sum = ldexp((double)m, p - 52 - 149);
+    }
+  }
+  return (float)(sum / (double)nb);
+}
+
+constexpr int kDcThreads = 1024;
+static_assert(kDcThreads / 64 >= kQdDigits, "one wave per digit counter");
+static_assert(kQdMaxGroups % 64 == 0, "whole partials per lane");
+
+__global__ __launch_bounds__(kDcThreads) void k_dq_codes(const float *__restrict__ a, int64_t nb,
+                                                         const unsigned long long *__restrict__ partial,
+                                                         int n_partial, int8_t *__restrict__ q,
+                                                         float *__restrict__ sigma,
+                                                         float *__restrict__ mean_out) {
+  constexpr int WPG = kDcThreads / 64;
+  __shared__ unsigned long long tot[kQdDigits];
+  __shared__ float s_mu;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nb2 = (nb + 255) / 256;
+  const int64_t step = (int64_t)gridDim.x * WPG;
+  int64_t b2 = (int64_t)blockIdx.x * WPG + wave;
+  auto load4 = [&](int64_t blk, float (&av)[4]) {
+    const int64_t j0 = blk * 256 + 4 * lane;
+    if (j0 + 4 <= nb) {
+      const f32x4 t = *reinterpret_cast<const f32x4 *>(a + j0);
+      av[0] = t[0]; av[1] = t[1]; av[2] = t[2]; av[3] = t[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = j0 + i < nb ? a[j0 + i] : 0.0f;
+    }
+  };
+  float av[4];
+  load4(b2 < nb2 ? b2 : 0, av);
+
+  // wave k < kQdDigits adds digit k of every partial (lane l takes partials
+  // l, l + 64, ...; n_partial <= kQdMaxGroups), then one wave-wide sum;
+  // thread 0 rounds the totals
+  if (wave < kQdDigits) {
+    // at most kQdMaxGroups / 64 partials per lane, all loads in flight at once
+    unsigned long long pk[kQdMaxGroups / 64];
+#pragma unroll
+    for (int i = 0; i < kQdMaxGroups / 64; ++i) {
+      const int p = lane + 64 * i;
+      pk[i] = p < n_partial ? partial[(int64_t)wave * n_partial + p] : 0ull;
+    }
+    unsigned long long dk = 0;
+#pragma unroll
+    for (int i = 0; i < kQdMaxGroups / 64; ++i) dk += pk[i];
+    dk = wave_sum_u64(dk);
+    if (lane == 0) tot[wave] = dk;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_mu = exact_mean(tot, nb);
+    if (blockIdx.x == 0) mean_out[0] = s_mu;
+  }
+  __syncthreads();
+  const float mu = s_mu;
+
+  for (; b2 < nb2; b2 += step) {
+    const int64_t j0 = b2 * 256 + 4 * lane;
+    float d4[4], amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d4[i] = j0 + i < nb ? av[i] - mu : 0.0f;
+      amax = fmaxf(amax, fabsf(d4[i]));
+    }
+    if (b2 + step < nb2) load4(b2 + step, av);  // wave-uniform
+#pragma unroll
+    for (int delta = 32; delta > 0; delta >>= 1) amax = fmaxf(amax, __shfl_xor(amax, delta, 64));
+    const float sg = amax / 127.0f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float c = 0.0f;
+      if (sg != 0.0f) {
+        c = __builtin_rintf(d4[i] / sg);
+        c = fminf(fmaxf(c, -127.0f), 127.0f);
+      }
+      word |= ((uint32_t)(int)c & 0xFFu) << (8 * i);
+    }
+    if (j0 + 4 <= nb && ((uintptr_t)q & 3u) == 0) {
+      *reinterpret_cast<uint32_t *>(q + j0) = word;
+    } else {  // ragged end, or a code array without 4-byte alignment
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < nb) q[j0 + i] = (int8_t)(word >> (8 * i));
+    }
+    if (lane == 0) sigma[b2] = sg;
   }
 }
 
@@ -397,17 +614,31 @@ int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_
   return QL_OK;
 }
 
-size_t dq_partial_count(int64_t nb) { return (size_t)((nb + kDqSumChunk - 1) / kDqSumChunk); }
-
-int launch_double_quant(const float *absmax, int64_t nb, double *partial, int8_t *q, float *sigma,
-                        float *mean_out, hipStream_t stream) {
-  if (nb <= 0) return QL_OK;
-  const int np = (int)dq_partial_count(nb);
-  hipLaunchKernelGGL(k_dq_partial_sums, dim3(np), dim3(256), 0, stream, absmax, nb, partial);
+int launch_nf4_quantize_dq(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
+                           float *absmax, unsigned long long *partial, int8_t *q, float *sigma,
+                           float *mean_out, hipStream_t stream) {
+  if (n <= 0) return QL_OK;
+  const int64_t nb = (n + block - 1) / block;
+  if (nb >= (int64_t(1) << 31)) return QL_EUNSUPPORTED;  // keeps the 64-bit digit sums exact
+  const int64_t chunks = (n + kQdRuns * 512 - 1) / (kQdRuns * 512);
+  const int groups = (int)std::min<int64_t>(kQdMaxGroups, (chunks + kQdThreads / 64 - 1) / (kQdThreads / 64));
+  const NF4Thresholds th = nf4_thresholds();
+#define QL_QUANT(T, BLKV)                                                                        \
+  hipLaunchKernelGGL((k_nf4_quantize_dq<T, BLKV>), dim3(groups), dim3(kQdThreads), 0, stream,     \
+                     (const T *)w, n, packed, absmax, th, partial)
+  if (w_dtype == QL_BF16) {
+    if (block == 128) QL_QUANT(uint16_t, 128); else QL_QUANT(uint16_t, 64);
+  } else if (w_dtype == QL_F16) {
+    if (block == 128) QL_QUANT(_Float16, 128); else QL_QUANT(_Float16, 64);
+  } else {
+    if (block == 128) QL_QUANT(float, 128); else QL_QUANT(float, 64);
+  }
+#undef QL_QUANT
   QL_HIP_CHECK_LAUNCH();
-  const int64_t nb2 = (nb + 255) / 256;  // one wave per DQ block, 4 per workgroup
-  hipLaunchKernelGGL(k_dq_codes, dim3((unsigned)((nb2 + 3) / 4)), dim3(256), 0, stream, absmax, nb,
-                     partial, np, q, sigma, mean_out);
+  const int64_t nb2 = (nb + 255) / 256;  // DQ blocks, one wave each per step
+  const int g2 = (int)std::min<int64_t>(256, (nb2 + 15) / 16);
+  hipLaunchKernelGGL(k_dq_codes, dim3(g2), dim3(kDcThreads), 0, stream, absmax, nb, partial, groups,
+                     q, sigma, mean_out);
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
 }

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 107
+    assert L.ql_abi_version() == 108
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -68,7 +68,9 @@ def test_workspace_sizes():
         assert q.workspace_bytes(op, 0, 4096, 4096, 16) == 0
         assert q.workspace_bytes(op, 16, 4096, 4096, 129) == 0
     nb = 4096 * 4096 // 64
-    assert q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 4096, 4096, 0) >= 4 * nb
+    # the fp32 block constants, then 512 exact partial sums of 12 64-bit counters
+    assert q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 4096, 4096, 0) == 4 * nb + 512 * 12 * 8
+    assert q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 3, 5, 0) == 256 + 512 * 12 * 8
     assert q.workspace_bytes(7, 1, 1, 1, 1) == 0
 
 

@@ -113,9 +113,39 @@ def test_quant_block_maxima_at_the_reciprocal_limits(orc):
         b[31:46] = np.nextafter(b[1:16], np.float32(-np.inf))
         blocks.append(b)
     w = torch.from_numpy(np.concatenate(blocks).reshape(len(blocks), 64))
-    # single-level constants only: a mean over maxima 2^250 apart is not
-    # what the double-quantisation pins are about
     _check_quant(orc, w, False)
+    _check_quant(orc, w, True)  # the mean of maxima 2^250 apart is still the exact one
+
+
+def test_quant_dq_mean_exact_sum_decides_a_tie(orc):
+    """Block maxima 2^60, 2^36, 2^7, 2^-100: the mean is 2^58 + 2^35 only if
+    the sum of the constants is exact (an fp64 running sum gives 2^58)."""
+    rng = np.random.default_rng(5)
+    blocks = []
+    for a in (2.0 ** 60, 2.0 ** 36, 2.0 ** 7, 2.0 ** -100):
+        b = (rng.uniform(-1, 1, 64) * a).astype(np.float32)
+        b[3] = np.float32(a)
+        blocks.append(b)
+    w = torch.from_numpy(np.concatenate(blocks).reshape(4, 64))
+    Wq, _ = _check_quant(orc, w, True)
+    assert host(Wq.absmax_mean)[0] == np.float32(2.0 ** 58 + 2.0 ** 35)
+
+
+@pytest.mark.parametrize("nblocks", [40000, 131072 + 77])
+def test_quant_dq_wide_range_constants(orc, nblocks):
+    """Block maxima spread over 2^-140 .. 2^120 (a range far beyond 2^30),
+    with a few subnormal and zero blocks, over enough blocks that many
+    workgroups contribute partial sums (the larger case also walks several
+    grid-stride steps per wave)."""
+    _say(f"quant dq wide range nblocks={nblocks}")
+    rng = np.random.default_rng(nblocks)
+    e = rng.integers(-140, 120, nblocks).astype(np.float64)
+    amax = (rng.uniform(1, 2, nblocks) * np.exp2(e)).astype(np.float32)
+    amax[7] = np.float32(3 * 2.0 ** -149)
+    amax[11] = 0
+    w = rng.uniform(-1, 1, (nblocks, 64)).astype(np.float32) * amax[:, None]
+    w[np.arange(nblocks), rng.integers(0, 64, nblocks)] = amax
+    _check_quant(orc, torch.from_numpy(w), True)
 
 
 def _bf16_sweep_weights(a_scale_exp: int) -> torch.Tensor:

@@ -261,6 +261,37 @@ def test_dq_mean_is_exact_mean(orc):
     assert orc.dq_mean(a) == np.float32(np.mean(a.astype(np.float64)))
 
 
+def test_dq_mean_exact_sum_decides_a_tie(orc):
+    """Constants 2^60, 2^36, 2^7, 2^-100: the exact mean 2^58 + 2^34 + 2^5 +
+    2^-102 lies just above the fp32 midpoint 2^58 + 2^34, so it rounds up to
+    2^58 + 2^35; the exact sum rounded to fp64 (2^60 + 2^36 + 2^8, the
+    2^-100 breaking the fp64 tie) keeps that.  A plain fp64 running sum drops
+    2^7 at a tie and 2^-100, lands exactly on the fp32 midpoint and rounds
+    down to 2^58: the pin fails an oracle that sums in fp64."""
+    a = np.array([2.0 ** 60, 2.0 ** 36, 2.0 ** 7, 2.0 ** -100], dtype=np.float32)
+    want = np.float32(2.0 ** 58 + 2.0 ** 35)
+    assert orc.dq_mean(a) == want
+    running = 0.0
+    for v in a.tolist():
+        running += v
+    assert np.float32(running / a.size) != want
+    exact = sum((frac(v) for v in a), Fraction(0)) / a.size
+    assert rn32(exact) == want
+
+
+def test_dq_mean_wide_range_matches_exact_rational(orc):
+    """Constants spread over 2^-149 .. 2^120 (subnormals included): the mean
+    is the exact sum rounded to fp64, divided by the count in fp64 and
+    rounded to fp32."""
+    rng = np.random.default_rng(31)
+    e = rng.integers(-149, 120, 3000)
+    a = (rng.uniform(1, 2, 3000) * np.exp2(e.astype(np.float64))).astype(np.float32)
+    a[:5] = np.float32(2.0 ** -149) * np.arange(1, 6, dtype=np.float32)
+    s = sum((frac(v) for v in a), Fraction(0))
+    want = rn32(Fraction(float(Fraction(float(s)) / a.size)))
+    assert orc.dq_mean(a) == want
+
+
 def _dq_brute(absmax, mu, block2):
     q = []
     sig = []
