@@ -12,7 +12,9 @@ import torch
 
 import qlora_fine_tuning_quantize_amd as q
 import synth_inputs as si
-from tests.helpers import BF16_TOL, F16_TOL, assert_f32_close, host, rel_err
+from tests.helpers import (BF16_TOL, F16_TOL, U_BF16, U_F16, assert_f32_close,
+                           assert_layer_within16, host, layer_bounds16,
+                           rel_err)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -220,7 +222,22 @@ def _layer_case(orc, M, N, K, r, dq, act, lora, alpha=32.0, seed_cfg=90, dy_ones
         np.testing.assert_array_equal(dA2.cpu().numpy(), got["dA"])
         np.testing.assert_array_equal(dB2.cpu().numpy(), got["dB"])
     np.testing.assert_array_equal(dx2.float().cpu().numpy()[sel], got["dx"])
+    if act != torch.float32:  # every 16-bit output within its derived per-element bound
+        s = float(np.float32(alpha) / np.float32(r))
+        bounds = layer_bounds16(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), s,
+                                dy=host(t["dy"]), rows=rows)
+        assert_layer_within16(got, ref, bounds, U_F16 if act == torch.float16 else U_BF16)
     return got, ref
+
+
+def _assert_fwd_within16(t, w_hat, alpha, r, act, y, y_ref, u=None, u_ref=None):
+    """The forward's 16-bit y (and fp32 u) within the derived per-element bound."""
+    s = float(np.float32(alpha) / np.float32(r))
+    b = layer_bounds16(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), s)
+    got, ref = {"y": y.float().cpu().numpy()}, {"y": y_ref}
+    if u is not None:
+        got["u"], ref["u"] = u.cpu().numpy(), u_ref
+    assert_layer_within16(got, ref, b, U_F16 if act == torch.float16 else U_BF16)
 
 
 @pytest.mark.parametrize("dy_ones", [False, True])
@@ -426,6 +443,7 @@ def test_forward_given_u(orc, M, N, K, r, act, lora, fwd_splits):
     else:
         tol = F16_TOL if act == torch.float16 else BF16_TOL
         assert rel_err(y_u.float().cpu().numpy(), y_ref) <= tol
+        _assert_fwd_within16(t, w_hat, 32.0, r, act, y_u, y_ref)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
@@ -442,11 +460,12 @@ def test_decode_config_full_size(orc, M):
     st = orc.quantize_nf4(host(t["W"]), double_quant=True)
     np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
     np.testing.assert_array_equal(host(W.absmax_q)[:st["absmax_q"].size], st["absmax_q"])
-    y_ref, _ = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
-                              host(t["B"]), c["alpha"], r)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    y_ref, _ = orc.linear_fwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), c["alpha"], r)
     e = rel_err(y.float().cpu().numpy(), y_ref)
     _say(f"decode M={M}: rel err {e:.2e}")
     assert e <= BF16_TOL
+    _assert_fwd_within16(t, w_hat, c["alpha"], r, torch.bfloat16, y, y_ref)
 
 
 # Decode-sized forwards (M <= 16) on larger weights, every output and u.
@@ -490,12 +509,13 @@ def test_decode_large_weights(orc, M, N, K, r, act, lora, dq):
     torch.cuda.synchronize()
     st = orc.quantize_nf4(host(t["W"]), double_quant=dq)
     np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
-    y_ref, u_ref = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
-                                  host(t["B"]), 32.0, r)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    y_ref, u_ref = orc.linear_fwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), 32.0, r)
     tol = F16_TOL if act == torch.float16 else BF16_TOL
     ey, eu = rel_err(y.float().cpu().numpy(), y_ref), rel_err(u.cpu().numpy(), u_ref)
     _say(f"  rel err y {ey:.2e} u {eu:.2e}")
     assert ey <= tol and eu <= tol
+    _assert_fwd_within16(t, w_hat, 32.0, r, act, y, y_ref, u, u_ref)
 
 
 # Decode-sized forwards with blocks of 128 (the per-element constant path of
@@ -520,12 +540,13 @@ def test_decode_block128_long_contraction(orc, M, N, K, r, act, lora, dq):
     torch.cuda.synchronize()
     st = orc.quantize_nf4(host(t["W"]), double_quant=dq, block=128)
     np.testing.assert_array_equal(host(W.packed)[:st["packed"].size], st["packed"])
-    y_ref, u_ref = orc.linear_fwd(host(t["x"]), orc.dequantize(st).reshape(N, K), host(t["A"]),
-                                  host(t["B"]), 16.0, r)
+    w_hat = orc.dequantize(st).reshape(N, K)
+    y_ref, u_ref = orc.linear_fwd(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), 16.0, r)
     tol = F16_TOL if act == torch.float16 else BF16_TOL
     ey, eu = rel_err(y.float().cpu().numpy(), y_ref), rel_err(u.cpu().numpy(), u_ref)
     _say(f"  rel err y {ey:.2e} u {eu:.2e}")
     assert ey <= tol and eu <= tol
+    _assert_fwd_within16(t, w_hat, 16.0, r, act, y, y_ref, u, u_ref)
 
 
 @pytest.mark.parametrize("proj", ["gate", "down"])

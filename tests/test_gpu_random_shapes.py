@@ -18,7 +18,8 @@ import torch
 
 import qlora_fine_tuning_quantize_amd as q
 import synth_inputs as si
-from tests.helpers import BF16_TOL, F16_TOL, assert_f32_within, host, rel_err
+from tests.helpers import (BF16_TOL, F16_TOL, U_BF16, U_F16, assert_f32_within,
+                           assert_layer_within16, host, layer_bounds16, rel_err)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -101,3 +102,7 @@ def test_random_shape(orc, i):
     print("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for k, e in errs.items():
         assert e <= tol, (k, e)
+    if mult is None:  # the per-element bound (its bypass input is x itself)
+        s = float(np.float32(alpha) / np.float32(r))
+        b = layer_bounds16(host(t["x"]), w_hat, host(t["A"]), host(t["B"]), s, dy=host(t["dy"]))
+        assert_layer_within16(got, ref, b, U_F16 if act == torch.float16 else U_BF16)
