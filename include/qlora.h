@@ -349,7 +349,9 @@ const char *ql_strerror(int status);
  *        slices and u slices on every shape.
  *   107: qlora_linear_fwd_noalloc.
  *   108: the double-quantised nf4_quantize keeps 48 KiB of exact partial sums
- *        of the block constants in place of fp64 partials. */
+ *        of the block constants in place of fp64 partials.
+ *   109: the decode forward's plan takes longer runs per wave (fewer
+ *        contraction slices) on large weights. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

@@ -158,7 +158,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 108; }
+int ql_abi_version(void) { return 109; }
 
 const char *ql_strerror(int status) {
   switch (status) {

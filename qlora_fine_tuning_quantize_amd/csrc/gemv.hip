@@ -426,10 +426,12 @@ struct DecPlan {
 // so the contraction is split in S slices.  The kernel's register use
 // allows 3 resident workgroups of 4 waves per compute unit (256 units).
 // With double quantisation and K % 128 == 0, cpw is the largest power of
-// two up to 8 that still gives 3 workgroups per unit and keeps each wave's
-// 2 cpw codes inside one aligned 16-byte piece (K / 64 a multiple of 2 cpw,
-// N K / 64 of 16), so a wave loads the block constants of all its chunks at
-// once.  Otherwise cpw stays 1 while the tasks fill the resident
+// two up to 8 that still gives at least half of the resident workgroups (1.5
+// per unit: measured over cpw = 1..8 on weights from 4096x4096 to
+// 8192x28672, longer runs per wave beat a second, partial round of
+// workgroups) and keeps each wave's 2 cpw codes inside one aligned 16-byte
+// piece (K / 64 a multiple of 2 cpw, N K / 64 of 16), so a wave loads the
+// block constants of all its chunks at once.  Otherwise cpw stays 1 while the tasks fill the resident
 // workgroups; beyond that each wave takes several consecutive chunks.  In
 // both, a wave's loads of its next chunk are in flight while it multiplies
 // the current one.  u takes one workgroup per 4 chunks, at most 16.
@@ -444,7 +446,7 @@ static DecPlan dec_plan(int64_t N, int64_t K, bool dq, int shift) {
   if (p.ev && dq && (N * KB) % 16 == 0) {
     int c = 8;
     while (c > 1 && (KB % (2 * c) != 0 ||
-                     p.G * ((NC + kDecWaves * c - 1) / (kDecWaves * c)) < resident))
+                     p.G * ((NC + kDecWaves * c - 1) / (kDecWaves * c)) < resident / 2))
       c >>= 1;
     if (KB % (2 * c) == 0) {
       p.vc = true;

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 108
+    assert L.ql_abi_version() == 109
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -77,15 +77,16 @@ def test_workspace_sizes():
 def _decode_partial_floats(M, N, K, r):
     """The decode forward's fp32 partials: S contraction slices of y [M, N]
     and U slices of u [M, r], for the larger of its launch plans (runs of
-    cpw = 2^k <= 8 chunks for double-quantised weights with K % 128 == 0,
-    else one chunk per wave while 3 x 256 workgroups of 4 waves hold them;
+    cpw = 2^k <= 8 chunks for double-quantised weights with K % 128 == 0, the
+    longest that leaves at least 384 workgroups, else one chunk per wave
+    while 3 x 256 workgroups of 4 waves hold them;
     4 cpw chunks per workgroup; u slices of 4 chunks, at most 16)."""
     cdiv = lambda a, b: -(-a // b)
     G, NC, KB = cdiv(N, 64), cdiv(K, 128), K // 64
     S = []
     if K % 128 == 0 and (N * KB) % 16 == 0:
         c = 8
-        while c > 1 and (KB % (2 * c) != 0 or G * cdiv(NC, 4 * c) < 768):
+        while c > 1 and (KB % (2 * c) != 0 or G * cdiv(NC, 4 * c) < 384):
             c //= 2
         if KB % (2 * c) == 0:
             S.append(cdiv(NC, 4 * c))
