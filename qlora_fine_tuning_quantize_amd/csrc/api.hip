@@ -99,6 +99,9 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     const size_t gemv_end = w.rows + round_up(gemv_fwd_partial_floats(M, N, K, r) * 4);
     if (gemv_end > w.total) w.total = gemv_end;
   }
+  // a few-token forward's slice partials of y and u, in the same region
+  const size_t fused_end = w.rows + round_up(gemm_fwd_fused_partial_floats(M, N, K, r) * 4);
+  if (fused_end > w.total) w.total = fused_end;
   return w;
 }
 
@@ -264,6 +267,9 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   if (act_dtype != QL_F32 && !drop && gemv_fwd_preferred(M, N, K))
     return launch_gemv_fwd(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y,
                            u_save, s, rows_partial);
+  if (act_dtype != QL_F32 && !drop && gemm_fwd_fused_preferred(M))
+    return launch_gemm_fwd_fused(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r,
+                                 sc_lora, y, u_save, s, rows_partial);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
                            rows_partial, s, nullptr, drop);
   if (st) return st;

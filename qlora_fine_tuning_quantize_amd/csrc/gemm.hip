@@ -38,6 +38,7 @@
 // The rank-r bypass is accumulated first, before the main loop, so the loads
 // of its operands overlap the loads of the first tiles.
 #include "kernels.h"
+#include "upart.h"
 
 namespace qlora {
 
@@ -450,11 +451,19 @@ constexpr int kSmBM = 64;
 constexpr int kSmBN = 128;
 constexpr int kSmThreads = 256;
 
-template <typename AT, typename LT, bool DQ>
+//
+// FUSED: the launch also computes u and leaves the bypass to the launch that
+// sums its partials.  Workgroups past the G tiles (grid row 0 only; the
+// others return) each form one u slice tile -- token group, rank tile and
+// contraction slice -- from x and A; every tile workgroup writes its fp32
+// partial of x W^^T for its contraction slice (no bypass), and the next
+// launch forms y = RN(fmaf(s, sum_j u_j B_nj, sum of the slices)).
+template <typename AT, typename LT, bool DQ, bool FUSED>
 __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
     int64_t N, int64_t K, const float *__restrict__ u, const LT *__restrict__ B, int32_t r,
-    float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit) {
+    float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit,
+    const LT *__restrict__ A, float *__restrict__ upart, int uc, int MT) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kSmBM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wp[2][kSmBN * 32];
   __shared__ float wsc[2][kSmBN];
@@ -462,6 +471,16 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   __shared__ __attribute__((aligned(16))) uint8_t ls_b[kSmBN * kLoraStride];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
+  const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+  if (FUSED && (int64_t)blockIdx.x >= G) {
+    if (blockIdx.y == 0) {
+      const int JT = (r + 15) / 16;
+      const int b = (int)((int64_t)blockIdx.x - G);
+      u_slice_tile<AT, LT>(x, (int)M, K, A, r, upart, uc, b / (JT * MT), (b / MT) % JT, b % MT,
+                           reinterpret_cast<float *>(&xs[0][0]));
+    }
+    return;
+  }
   lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, nt;
@@ -522,7 +541,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   load_x(ks0, 0);
   load_x(ks0, 1);
   load_w(ks0);
-  if (split == 0) {
+  if (!FUSED && split == 0) {
     stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, 0, s, t);
     stage_lora<kSmBN, kSmThreads, AT>(ls_b, B, n0, N, r, 0, 1.0f, t);
   }
@@ -577,7 +596,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   }
 
   // LoRA bypass: acc += B (s u)^T, 16 ranks per MFMA step, first slice only
-  for (int j0 = 0; j0 < (split == 0 ? r : 0); j0 += 16) {
+  for (int j0 = 0; j0 < (!FUSED && split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
       stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, j0, s, t);
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     for (int i = 0; i < 2; ++i) acc[i][0] = mfma32<AT>(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
   }
   const int64_t col = n0 + 32 * wave;
-  if (nsplit > 1)
+  if (FUSED || nsplit > 1)
     store_tile_f32<2, 1>(part + (int64_t)split * M * N, N, M, N, m0, col, acc, lane);
   else if (n0 + kSmBN <= N && N % 8 == 0)  // per-wave slices of 32 rows in a dead staging buffer
     store_tile_lds<AT, 2, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
@@ -1009,9 +1028,9 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
     const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
     const int S = part ? fwd_split(M, N, K) : 1;
 #define QL_FWS(LT, DQV)                                                                          \
-  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV>), dim3((unsigned)G, (unsigned)S),           \
+  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, false>), dim3((unsigned)G, (unsigned)S),    \
                      dim3(kSmThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, \
-                     y, part, S)
+                     y, part, S, (const LT *)nullptr, (float *)nullptr, 0, 0)
     with_half(act_dtype, [&](auto *tag) {
       using AT = elem_of<decltype(tag)>;
       if (lora_dtype == QL_F32) {
@@ -1049,6 +1068,46 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
   QL_HIP_CHECK_LAUNCH();
   if (S > 1) return reduce_split(act_dtype, part, S, M * N, y, stream);
   return QL_OK;
+}
+
+// Up to 64 tokens the u slices and the slice sum with the bypass (two
+// launches) beat u in launches of its own plus a split-K sum; from 96 tokens
+// on the fp32 partials of every slice cost more than they save.
+bool gemm_fwd_fused_preferred(int64_t M) { return M > 16 && M <= 64; }
+
+size_t gemm_fwd_fused_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (!gemm_fwd_fused_preferred(M)) return 0;
+  return (size_t)fwd_split(M, N, K) * M * N + (size_t)u_slices(K).U * M * r;
+}
+
+int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
+                          BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
+                          int lora_dtype, int32_t r, float s, void *y, float *u_save,
+                          hipStream_t stream, float *part) {
+  const uint16_t *x = (const uint16_t *)xv;
+  const bool dq = sc.absmax == nullptr;
+  const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+  const int S = fwd_split(M, N, K);
+  const USlices us = u_slices(K);
+  const int MT = (int)((M + 15) / 16), JT = (r + 15) / 16;
+  float *upart = part + (size_t)S * M * N;
+  const dim3 grid((unsigned)(G + (int64_t)us.U * JT * MT), (unsigned)S);
+#define QL_FWF(LT, DQV)                                                                          \
+  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream,  \
+                     x, M, packed, sc, N, K, (const float *)nullptr, (const LT *)B, r, s,         \
+                     (uint16_t *)nullptr, part, S, (const LT *)A, upart, us.uc, MT)
+  with_half(act_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (lora_dtype == QL_F32) {
+      if (dq) QL_FWF(float, true); else QL_FWF(float, false);
+    } else {
+      if (dq) QL_FWF(AT, true); else QL_FWF(AT, false);
+    }
+  });
+#undef QL_FWF
+  QL_HIP_CHECK_LAUNCH();
+  return launch_fwd_finish(act_dtype, lora_dtype, part, S, upart, us.U, M, N, r, B, s, y, u_save,
+                           stream);
 }
 
 bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 == 0; }

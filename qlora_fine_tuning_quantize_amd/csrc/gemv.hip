@@ -43,6 +43,7 @@
 // zeroed (the first block) and once with that of 0-1 zeroed (the second).
 // The zeroed operands are built once per chunk and serve all 64 rows.
 #include "kernels.h"
+#include "upart.h"
 
 namespace qlora {
 
@@ -50,7 +51,6 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecRows = 64;   // weight rows per workgroup (4 groups of 16, every wave all of them)
 constexpr int kDecChunk = 128; // columns per chunk: 64 packed bytes per row
-constexpr int kDecUMaxSlices = 16;
 
 __device__ __forceinline__ float nf4_immediate(int i) {
   constexpr float cb[16] = QL_NF4_CODEBOOK_VALUES;
@@ -69,65 +69,6 @@ struct DecChunk {
   int cq[4][2];
   float cs[4][2];
 };
-
-// 8 16-bit values of a LoRA-A row as a matrix-core operand in format AT
-template <typename AT, typename LT>
-__device__ __forceinline__ u32x4 lora_op8(const LT *p) {
-  if constexpr (sizeof(LT) == 2) {
-    return *reinterpret_cast<const u32x4 *>(p);
-  } else {
-    const float4 a = reinterpret_cast<const float4 *>(p)[0];
-    const float4 b = reinterpret_cast<const float4 *>(p)[1];
-    return u32x4{Half<AT>::pack2(a.x, a.y), Half<AT>::pack2(a.z, a.w), Half<AT>::pack2(b.x, b.y),
-                 Half<AT>::pack2(b.z, b.w)};
-  }
-}
-
-// u = x A^T, rank tile jt (16 ranks) over the contraction chunks [su uc,
-// su uc + uc), summed over the workgroup's waves: upart[su][m][16 jt + j].
-// red: kDecWaves x 16 x 16 floats of LDS.
-template <typename AT, typename LT>
-__device__ __forceinline__ void dec_u_part(const uint16_t *__restrict__ x, int M, int64_t K,
-                                           const LT *__restrict__ A, int32_t r,
-                                           float *__restrict__ upart, int uc, int su, int jt,
-                                           float *red) {
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  const int nl = lane & 15, q = lane >> 4;
-  const int m = nl < M ? nl : M - 1;
-  const int64_t col0 = (int64_t)su * uc * kDecChunk;
-  const int64_t col1 = col0 + (int64_t)uc * kDecChunk < K ? col0 + (int64_t)uc * kDecChunk : K;
-  const int nsteps = (int)((col1 - col0) / 32);  // K % 64 == 0
-  const int j = 16 * jt + nl < r ? 16 * jt + nl : r - 1;
-  const uint16_t *xp = x + (int64_t)m * K + col0 + 8 * q;
-  const LT *ap = A + (int64_t)j * K + col0 + 8 * q;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // steps wave, wave + 4, ...: four at a time, all their loads issued
-  // before the first op (clamped to a valid step; extra ones not used)
-  for (int s0 = wave; s0 < nsteps; s0 += 4 * kDecWaves) {
-    u32x4 xo[4], ao[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int st = s0 + kDecWaves * i < nsteps ? s0 + kDecWaves * i : s0;
-      xo[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * st);
-      ao[i] = lora_op8<AT>(ap + 32 * st);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (s0 + kDecWaves * i < nsteps) acc = Half<AT>::mfma16(xo[i], ao[i], acc);
-  }
-  // acc[v] = partial u[4q + v][16 jt + nl]
-#pragma unroll
-  for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * q + v) * 16 + nl] = acc[v];
-  __syncthreads();
-  if (t < 16 * M) {
-    const int mo = t >> 4, jj = t & 15;
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) sum += red[(w * 16 + mo) * 16 + jj];
-    if (16 * jt + jj < r) upart[((int64_t)su * M + mo) * r + 16 * jt + jj] = sum;
-  }
-}
 
 // grid.x = U JT + G S (JT = ceil(r / 16)).  Workgroups [0, U JT): u, rank
 // tile b % JT over contraction slice b / JT of uc chunks, partial sums to
@@ -151,7 +92,8 @@ __global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
 
   const int JT = (r + 15) / 16;
   if ((int)blockIdx.x < U * JT) {
-    dec_u_part<AT, LT>(x, M, K, A, r, upart, uc, blockIdx.x / JT, blockIdx.x % JT, &red[0][0][0]);
+    u_slice_tile<AT, LT>(x, M, K, A, r, upart, uc, blockIdx.x / JT, blockIdx.x % JT, 0,
+                         &red[0][0][0]);
     return;
   }
 
@@ -334,8 +276,11 @@ __global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
 }
 
 // y[m][n] = RN(fmaf(s, sum_j u[m][j] B[n][j], sum over splits of x W^^T)),
-// u[m][j] = sum over the u slices in order.  Grid (ceil(N / 256), M): one
-// thread per output; the workgroups of the first column store u_save.
+// u[m][j] = sum over the u slices in order (both sums start from 0 and add in
+// slice order; the rank sum is a chain of fmaf in rank order).  Grid
+// (ceil(N / 256), M): one thread per output; the workgroups of the first
+// column store u_save.  Slices are read 8 at a time with all 8 loads in
+// flight (at clamped indices), so S slices cost ceil(S / 8) round trips.
 template <typename AT, typename LT>
 __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ part, int S,
                                                     const float *__restrict__ upart, int U, int M,
@@ -348,18 +293,22 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
   const int mo = blockIdx.y;
   const int64_t n = (int64_t)blockIdx.x * 256 + t;
   const int64_t nc = n < N ? n : N - 1;
-  // Every load of the thread is issued before the first sum: the first 8
-  // slice partials of y (and of u for threads t < r) at clamped indices, the
-  // row of B (at most 128 values: 16 pieces of 8); more than 8 slices are
-  // added by a tail loop.
+  // the first 8 slice partials of y, the first 8 of u (threads t < r) and
+  // the row of B (at most 128 values: 16 pieces of 8) are all issued before
+  // the first sum
   const int tj = t < r ? t : r - 1;
   float pv[8], uv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ii = i < S ? i : S - 1;
     pv[i] = part[((int64_t)ii * M + mo) * N + nc];
-    const int iu = i < U ? i : U - 1;
-    uv[i] = upart[((int64_t)iu * M + mo) * r + tj];
+  }
+  if (t < r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int iu = i < U ? i : U - 1;
+      uv[i] = upart[((int64_t)iu * M + mo) * r + tj];
+    }
   }
   const LT *bp = B + nc * r;
   u32x4 bw[16 * sizeof(LT) / 2];
@@ -376,13 +325,32 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
     }
   float base = 0.0f, su = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 8; ++i)
     if (i < S) base += pv[i];
-    if (i < U) su += uv[i];
+  for (int i0 = 8; i0 < S; i0 += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ii = i0 + i < S ? i0 + i : S - 1;
+      pv[i] = part[((int64_t)ii * M + mo) * N + nc];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i0 + i < S) base += pv[i];
   }
-  for (int i = 8; i < S; ++i) base += part[((int64_t)i * M + mo) * N + nc];
-  for (int i = 8; i < U; ++i) su += upart[((int64_t)i * M + mo) * r + tj];
   if (t < r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < U) su += uv[i];
+    for (int i0 = 8; i0 < U; i0 += 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int iu = i0 + i < U ? i0 + i : U - 1;
+        uv[i] = upart[((int64_t)iu * M + mo) * r + tj];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i0 + i < U) su += uv[i];
+    }
     us[t] = su;
     if (u_save && blockIdx.x == 0) u_save[(int64_t)mo * r + t] = su;
   }
@@ -407,6 +375,23 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
     for (int j = 0; j < r; ++j) l = __builtin_fmaf(us[j], load_as_f32(B, n * r + j), l);
   }
   y[(int64_t)mo * N + n] = Half<AT>::bits(__builtin_fmaf(s, l, base));
+}
+
+int launch_fwd_finish(int act_dtype, int lora_dtype, const float *part, int S,
+                      const float *upart, int U, int64_t M, int64_t N, int32_t r, const void *B,
+                      float s, void *y, float *u_save, hipStream_t stream) {
+  const dim3 fgrid((unsigned)((N + 255) / 256), (unsigned)M);
+  with_half(act_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (lora_dtype == QL_F32)
+      hipLaunchKernelGGL((k_dec_finish<AT, float>), fgrid, dim3(256), 0, stream, part, S, upart,
+                         U, (int)M, N, r, (const float *)B, s, (uint16_t *)y, u_save);
+    else
+      hipLaunchKernelGGL((k_dec_finish<AT, AT>), fgrid, dim3(256), 0, stream, part, S, upart, U,
+                         (int)M, N, r, (const AT *)B, s, (uint16_t *)y, u_save);
+  });
+  QL_HIP_CHECK_LAUNCH();
+  return QL_OK;
 }
 
 // Launch plan of a decode forward.
@@ -461,10 +446,9 @@ static DecPlan dec_plan(int64_t N, int64_t K, bool dq, int shift) {
     const int64_t cps = (NC + S - 1) / S;
     p.S = (int)((NC + cps - 1) / cps);
   }
-  int64_t U = (NC + 3) / 4;
-  if (U > kDecUMaxSlices) U = kDecUMaxSlices;
-  p.uc = (int)((NC + U - 1) / U);
-  p.U = (int)((NC + p.uc - 1) / p.uc);
+  const USlices us = u_slices(K);
+  p.U = us.U;
+  p.uc = us.uc;
   return p;
 }
 
@@ -487,7 +471,6 @@ int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
   const DecPlan p = dec_plan(N, K, dq, sc.shift);
   float *upart = part + (size_t)p.S * M * N;
   const dim3 grid((unsigned)(p.U * ((r + 15) / 16) + p.G * p.S));
-  const dim3 fgrid((unsigned)((N + 255) / 256), (unsigned)M);
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
     auto go = [&](auto *ltag) {
@@ -505,14 +488,14 @@ int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
       else if (dq) main(T{}, F{}, F{});
       else if (p.ev) main(F{}, T{}, F{});
       else main(F{}, F{}, F{});
-      hipLaunchKernelGGL((k_dec_finish<AT, LT>), fgrid, dim3(256), 0, stream, part, p.S, upart,
-                         p.U, (int)M, N, r, (const LT *)B, s, y, u_save);
+
     };
     if (lora_dtype == QL_F32) go((float *)nullptr);
     else go((AT *)nullptr);
   });
   QL_HIP_CHECK_LAUNCH();
-  return QL_OK;
+  return launch_fwd_finish(act_dtype, lora_dtype, part, p.S, upart, p.U, M, N, r, B, s, y, u_save,
+                           stream);
 }
 
 }  // namespace qlora

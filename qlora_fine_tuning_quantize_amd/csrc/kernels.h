@@ -73,6 +73,11 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
 // partials in part (gemv_fwd_partial_floats floats) and a second launch
 // that sums them.
 size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r);
+// y[m][n] = RN(fmaf(s, sum_j u_j B_nj, sum of S slices of part [S][M][N])),
+// u = sum of U slices of upart [U][M][r] (stored to u_save when non-null).
+int launch_fwd_finish(int act_dtype, int lora_dtype, const float *part, int S,
+                      const float *upart, int U, int64_t M, int64_t N, int32_t r, const void *B,
+                      float s, void *y, float *u_save, hipStream_t stream);
 int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *y, float *u_save,
@@ -83,6 +88,15 @@ int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *pack
 // part: fp32 workspace of gemm_*_partial_floats floats for split-K
 // launches, or NULL (no split).
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
+// Few-token forward (17..64 tokens, 16-bit activations, no dropout) in two
+// launches: the 64-token GEMM tiles plus u slice workgroups, then the slice
+// sum with the bypass (part: gemm_fwd_fused_partial_floats floats).
+bool gemm_fwd_fused_preferred(int64_t M);
+size_t gemm_fwd_fused_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r);
+int launch_gemm_fwd_fused(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
+                          BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
+                          int lora_dtype, int32_t r, float s, void *y, float *u_save,
+                          hipStream_t stream, float *part);
 size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K);
 int launch_gemm_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,

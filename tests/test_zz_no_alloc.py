@@ -41,6 +41,10 @@ def _both(t, W, alpha):
     # the matrix-core path (u, GEMM, split-K sum), then a decode-sized call
     ((300, 1024, 2048, 16, True, torch.bfloat16, torch.bfloat16),
      (5, 200, 640, 5, False, torch.float16, torch.float32)),
+    # few tokens: 64-token tiles and u slices in one launch, then the slice
+    # sum with the bypass; then fewer tokens, ragged, in fp16
+    ((48, 2048, 4096, 16, True, torch.bfloat16, torch.bfloat16),
+     (20, 200, 1024, 8, False, torch.float16, torch.float32)),
 ])
 def test_noalloc_matches_fwd_twice(first, second):
     for i, (M, N, K, r, dq, act, lora) in enumerate((first, second)):
