@@ -270,6 +270,8 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   if (act_dtype != QL_F32 && !drop && gemm_fwd_fused_preferred(M))
     return launch_gemm_fwd_fused(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r,
                                  sc_lora, y, u_save, s, rows_partial);
+  if (!drop && tiny_preferred(act_dtype, M, N, K, r))
+    return launch_tiny_fwd(x, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y, u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,
                            rows_partial, s, nullptr, drop);
   if (st) return st;
@@ -380,6 +382,9 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
+  if (!drop && tiny_preferred(act_dtype, M, N, K, r))
+    return launch_tiny_bwd(dy, x, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, u_saved,
+                           dx, dA, dB, accumulate, s);
   if (u_saved) {
     u = const_cast<float *>(u_saved);
   } else {

@@ -87,6 +87,16 @@ int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *pack
 // activations (act_dtype QL_BF16 or QL_F16; a 16-bit lora_dtype equals it).
 // part: fp32 workspace of gemm_*_partial_floats floats for split-K
 // launches, or NULL (no split).
+// tiny.hip: fp32 activations at small sizes (M <= 16, r <= 64, M N K <=
+// 2^22): each pass of the layer in one workgroup, no workspace.
+bool tiny_preferred(int act_dtype, int64_t M, int64_t N, int64_t K, int32_t r);
+int launch_tiny_fwd(const void *x, int64_t M, const uint8_t *packed, BlockScales sc, int64_t N,
+                    int64_t K, const void *A, const void *B, int lora_dtype, int32_t r, float s,
+                    void *y, float *u_save, hipStream_t stream);
+int launch_tiny_bwd(const void *dy, const void *x, int64_t M, const uint8_t *packed,
+                    BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
+                    int lora_dtype, int32_t r, float s, const float *u_saved, void *dx, float *dA,
+                    float *dB, bool accumulate, hipStream_t stream);
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
 // Few-token forward (17..64 tokens, 16-bit activations, no dropout) in two
 // launches: the 64-token GEMM tiles plus u slice workgroups, then the slice
