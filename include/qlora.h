@@ -351,7 +351,10 @@ const char *ql_strerror(int status);
  *   108: the double-quantised nf4_quantize keeps 48 KiB of exact partial sums
  *        of the block constants in place of fp64 partials.
  *   109: the decode forward's plan takes longer runs per wave (fewer
- *        contraction slices) on large weights. */
+ *        contraction slices) on large weights.
+ *   110: the LoRA products (u, g, dA, dB) cover several contraction chunks
+ *        per workgroup: fewer slices, smaller forward and backward
+ *        workspaces on large shapes. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

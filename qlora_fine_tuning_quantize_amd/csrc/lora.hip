@@ -76,14 +76,15 @@ __global__ __launch_bounds__(256) void k_lora_rows(const void *__restrict__ P, i
 // A = 16 rows of P x 32 contraction values (read straight from global, 16 B
 // per lane) and B = the LoRA factor slice staged in LDS in P's format [j][c].
 // Wave w of the workgroup owns rows 16w..16w+15 of a 64-row tile and all JT
-// 16-wide rank tiles; the workgroup covers one CS-wide slice of the
-// contraction in a single round trip, with every trip count fixed at
-// compile time: the factor loads are issued first (8 values per load along
-// the factor's contiguous dimension, or single values for ranks / shapes
-// that are not 8-aligned), then all CS/32 loads of P, then the factor is
-// written to LDS (only its loads are waited for), one barrier, the MFMAs,
-// and the fp32 partial sums of the slice.  Rows past M and contraction
-// positions past C load clamped addresses and use zeros instead.
+// 16-wide rank tiles; the workgroup covers nsub consecutive CS-wide chunks
+// of the contraction (one slice), chunk after chunk, with every per-chunk
+// trip count fixed at compile time: the factor loads are issued first (8
+// values per load along the factor's contiguous dimension, or single values
+// for ranks / shapes that are not 8-aligned), then all CS/32 loads of P, then
+// the factor is written to LDS (only its loads are waited for), one barrier,
+// the MFMAs; the slice's fp32 sums are written once at the end.  Rows past M
+// and contraction positions past C load clamped addresses and use zeros
+// instead.
 // Operand layout (gfx950): A lane l holds A[l % 16][8*(l/16) .. +8]; B lane l
 // holds B[8*(l/16) .. +8][l % 16]; result lane l holds D[4*(l/16) .. +4][l % 16].
 // ---------------------------------------------------------------------------
@@ -138,109 +139,126 @@ template <int CS, int JT, typename AT, typename QT, int QMODE, bool DROP>
 __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int64_t M,
                                                    int64_t C, const QT *__restrict__ Q,
                                                    int64_t ldq_j, int64_t ldq_c, int32_t r,
-                                                   float *__restrict__ partial, Dropout dr) {
+                                                   float *__restrict__ partial, Dropout dr,
+                                                   int nsub) {
   constexpr int QST = 2 * CS + 16;   // bytes per staged rank row
   constexpr int JW = JT * 16;
   __shared__ __attribute__((aligned(16))) uint8_t qs[JW * QST];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int li = lane & 15, q = lane >> 4;
-  const int64_t c0 = (int64_t)blockIdx.y * CS;
-
-  // ---- factor loads (issued first) ----
+  const int64_t cs0 = (int64_t)blockIdx.y * CS * nsub;
   constexpr int NV = JW * CS / 8 / 256;          // 8-value loads per lane
   constexpr int NE = (QMODE == kQElem) ? JW * CS / 256 : 1;
-  Vec8<QT> qv[QMODE == kQElem ? 1 : NV];
-  float qe[NE];
-  if constexpr (QMODE == kQRowJ) {
-#pragma unroll
-    for (int b = 0; b < NV; ++b) {
-      const int e = t + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
-      const int64_t c = c0 + 8 * c8;
-      const int jc = j < r ? j : r - 1;
-      const int64_t cc = c + 8 <= C ? c : C - 8;
-      qv[b].load(Q + (int64_t)jc * ldq_j + cc);
-    }
-  } else if constexpr (QMODE == kQRowC) {
-#pragma unroll
-    for (int b = 0; b < NV; ++b) {
-      const int e = t + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
-      const int64_t c = c0 + cc < C ? c0 + cc : C - 1;
-      const int jc = 8 * j8 + 8 <= r ? 8 * j8 : r - 8;
-      qv[b].load(Q + c * ldq_c + jc);
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < NE; ++b) {
-      const int e = t + 256 * b;
-      int j, cc;
-      if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
-      const int64_t c = c0 + cc;
-      qe[b] = (j < r && c < C) ? load_as_f32(Q, j * ldq_j + c * ldq_c) : 0.0f;
-    }
-  }
-
-  // ---- P loads: row mrow, contraction c0 + 32 i + 8 q ----
-  const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + li;
-  const AT *prow = P + (mrow < M ? mrow : M - 1) * C;
-  u32x4 a[CS / 32];
-#pragma unroll
-  for (int i = 0; i < CS / 32; ++i) {
-    const int64_t c = c0 + 32 * i + 8 * q;
-    a[i] = *reinterpret_cast<const u32x4 *>(prow + (c + 8 <= C ? c : C - 8));
-    if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
-#pragma unroll
-    for (int i = 0; i < CS / 32; ++i) {
-      const int64_t c = c0 + 32 * i + 8 * q;
-      if (c + 8 <= C) a[i] = dropout_mask8(dr, (uint64_t)mrow * C + c, a[i]);
-    }
-  }
-
-  // ---- factor slice to LDS, 16-bit [j][c] ----
-  if constexpr (QMODE == kQRowJ) {
-#pragma unroll
-    for (int b = 0; b < NV; ++b) {
-      const int e = t + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
-      const bool ok = j < r && c0 + 8 * c8 + 8 <= C;
-      *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) =
-          u32x4{Half<AT>::pack2(qv[b].get(0, ok), qv[b].get(1, ok)),
-                Half<AT>::pack2(qv[b].get(2, ok), qv[b].get(3, ok)),
-                Half<AT>::pack2(qv[b].get(4, ok), qv[b].get(5, ok)),
-                Half<AT>::pack2(qv[b].get(6, ok), qv[b].get(7, ok))};
-    }
-  } else if constexpr (QMODE == kQRowC) {
-#pragma unroll
-    for (int b = 0; b < NV; ++b) {
-      const int e = t + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
-      const bool ok = c0 + cc < C && 8 * j8 + 8 <= r;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        *reinterpret_cast<uint16_t *>(qs + (8 * j8 + jj) * QST + 2 * cc) =
-            Half<AT>::bits(qv[b].get(jj, ok));
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < NE; ++b) {
-      const int e = t + 256 * b;
-      int j, cc;
-      if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
-      *reinterpret_cast<uint16_t *>(qs + j * QST + 2 * cc) = Half<AT>::bits(qe[b]);
-    }
-  }
-  __syncthreads();
 
   f32x4 acc[JT];
 #pragma unroll
   for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One CS-wide chunk from c0 into acc.  Per-thread indices come from tt, a
+  // copy of the thread index the compiler may not assume constant across
+  // chunks, so addresses are recomputed per chunk rather than held in
+  // registers over the loop.
+  auto chunk = [&](int tt, int64_t c0, bool after) {
+    const int w = tt >> 6, l = tt & 63, lj = l & 15, lq = l >> 4;
+    // ---- factor loads (issued first) ----
+    Vec8<QT> qv[QMODE == kQElem ? 1 : NV];
+    float qe[NE];
+    if constexpr (QMODE == kQRowJ) {
 #pragma unroll
-  for (int i = 0; i < CS / 32; ++i) {
+      for (int b = 0; b < NV; ++b) {
+        const int e = tt + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
+        const int64_t c = c0 + 8 * c8;
+        const int jc = j < r ? j : r - 1;
+        const int64_t cc = c + 8 <= C ? c : C - 8;
+        qv[b].load(Q + (int64_t)jc * ldq_j + cc);
+      }
+    } else if constexpr (QMODE == kQRowC) {
 #pragma unroll
-    for (int jt = 0; jt < JT; ++jt) {
-      const u32x4 b = *reinterpret_cast<const u32x4 *>(qs + (16 * jt + li) * QST +
-                                                       2 * (32 * i + 8 * q));
-      acc[jt] = Half<AT>::mfma16(a[i], b, acc[jt]);
+      for (int b = 0; b < NV; ++b) {
+        const int e = tt + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
+        const int64_t c = c0 + cc < C ? c0 + cc : C - 1;
+        const int jc = 8 * j8 + 8 <= r ? 8 * j8 : r - 8;
+        qv[b].load(Q + c * ldq_c + jc);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NE; ++b) {
+        const int e = tt + 256 * b;
+        int j, cc;
+        if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
+        const int64_t c = c0 + cc;
+        qe[b] = (j < r && c < C) ? load_as_f32(Q, j * ldq_j + c * ldq_c) : 0.0f;
+      }
     }
+
+    // ---- P loads: row mrow, contraction c0 + 32 i + 8 lq ----
+    const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * w + lj;
+    const AT *prow = P + (mrow < M ? mrow : M - 1) * C;
+    u32x4 a[CS / 32];
+#pragma unroll
+    for (int i = 0; i < CS / 32; ++i) {
+      const int64_t c = c0 + 32 * i + 8 * lq;
+      a[i] = *reinterpret_cast<const u32x4 *>(prow + (c + 8 <= C ? c : C - 8));
+      if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
+#pragma unroll
+      for (int i = 0; i < CS / 32; ++i) {
+        const int64_t c = c0 + 32 * i + 8 * lq;
+        if (c + 8 <= C) a[i] = dropout_mask8(dr, (uint64_t)mrow * C + c, a[i]);
+      }
+    }
+
+    if (after) __syncthreads();  // the previous chunk's factor has been read
+    // ---- factor chunk to LDS, 16-bit [j][c] ----
+    if constexpr (QMODE == kQRowJ) {
+#pragma unroll
+      for (int b = 0; b < NV; ++b) {
+        const int e = tt + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
+        const bool ok = j < r && c0 + 8 * c8 + 8 <= C;
+        *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) =
+            u32x4{Half<AT>::pack2(qv[b].get(0, ok), qv[b].get(1, ok)),
+                  Half<AT>::pack2(qv[b].get(2, ok), qv[b].get(3, ok)),
+                  Half<AT>::pack2(qv[b].get(4, ok), qv[b].get(5, ok)),
+                  Half<AT>::pack2(qv[b].get(6, ok), qv[b].get(7, ok))};
+      }
+    } else if constexpr (QMODE == kQRowC) {
+#pragma unroll
+      for (int b = 0; b < NV; ++b) {
+        const int e = tt + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
+        const bool ok = c0 + cc < C && 8 * j8 + 8 <= r;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          *reinterpret_cast<uint16_t *>(qs + (8 * j8 + jj) * QST + 2 * cc) =
+              Half<AT>::bits(qv[b].get(jj, ok));
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NE; ++b) {
+        const int e = tt + 256 * b;
+        int j, cc;
+        if (ldq_c == 1) { j = e / CS; cc = e % CS; } else { cc = e / JW; j = e % JW; }
+        *reinterpret_cast<uint16_t *>(qs + j * QST + 2 * cc) = Half<AT>::bits(qe[b]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CS / 32; ++i) {
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(qs + (16 * jt + lj) * QST +
+                                                         2 * (32 * i + 8 * lq));
+        acc[jt] = Half<AT>::mfma16(a[i], b, acc[jt]);
+      }
+    }
+  };
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int64_t c0 = cs0 + (int64_t)sub * CS;
+    if (c0 >= C) break;  // uniform
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    chunk(tt, c0, sub > 0);
   }
   const int64_t mbase = (int64_t)blockIdx.x * kMRowsTile + 16 * wave + 4 * q;
 #pragma unroll
@@ -284,17 +302,31 @@ static int rows_slices(int64_t M, int64_t C) {
   return (int)s;
 }
 
-// Slices of the matrix-core rows kernel: one per CS-wide piece of the
-// contraction (the partial buffer is sized for the fp32-factor case, which
-// has the narrower slices).
-static int mrows_slices(int64_t C, int32_t r, int q_dtype) {
-  return (int)((C + rows_cs(r, q_dtype) - 1) / rows_cs(r, q_dtype));
+// Slices of the matrix-core rows kernel: runs of nsub CS-wide chunks of the
+// contraction, so that the workgroups (64-row tiles x slices) number about
+// 1024; fewer slices write fewer partials (M x r floats each).
+struct MRowsPlan {
+  int S, nsub;
+};
+static MRowsPlan mrows_plan(int64_t M, int64_t C, int32_t r, int q_dtype) {
+  const int64_t cs = rows_cs(r, q_dtype);
+  const int64_t chunks = (C + cs - 1) / cs;
+  const int64_t tiles = (M + kMRowsTile - 1) / kMRowsTile;
+  int64_t S = (1024 + tiles - 1) / tiles;
+  if (S > chunks) S = chunks;
+  if (S < 1) S = 1;
+  MRowsPlan p;
+  p.nsub = (int)((chunks + S - 1) / S);
+  p.S = (int)((chunks + p.nsub - 1) / p.nsub);
+  return p;
 }
 
 static bool rows_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
 
 size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r) {
-  const int64_t s1 = rows_slices(M, C), s2 = mrows_slices(C, r, QL_F32);
+  const int64_t s1 = rows_slices(M, C);
+  const int64_t sa = mrows_plan(M, C, r, QL_F32).S, sb = mrows_plan(M, C, r, QL_BF16).S;
+  const int64_t s2 = sa > sb ? sa : sb;
   return (size_t)(s1 > s2 ? s1 : s2) * (size_t)M * (size_t)r;
 }
 
@@ -308,7 +340,8 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     return QL_EUNSUPPORTED;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (rows_use_mfma(p_dtype, C)) {
-    S = mrows_slices(C, r, q_dtype);
+    const MRowsPlan mp = mrows_plan(M, C, r, q_dtype);
+    S = mp.S;
     const dim3 grid((unsigned)((M + kMRowsTile - 1) / kMRowsTile), (unsigned)S);
     const int jt = rows_jt(r);
     // 8-value loads need the loaded factor rows 8-aligned (the factor base
@@ -319,7 +352,7 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
 #define QL_ROWS_M(JTV, QT, MODEV, DRV)                                                           \
   hipLaunchKernelGGL((k_rows_mfma<rows_cs_of<QT>(JTV), JTV, AT, QT, MODEV, DRV>), grid,          \
                      dim3(256), 0, stream, (const AT *)P, M, C, (const QT *)Q, ldq_j, ldq_c, r,  \
-                     partial, dr)
+                     partial, dr, mp.nsub)
 #define QL_ROWS_Q(JTV, QT)                                                                       \
   do {                                                                                           \
     if (drop) QL_ROWS_M(JTV, QT, kQRowJ, true);                                                  \
@@ -460,7 +493,7 @@ template <int TM, int JT, typename AT, bool RVEC, bool DROP>
 __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
                                                    int32_t r, const AT *__restrict__ P,
                                                    int64_t C, float *__restrict__ partial,
-                                                   Dropout dr, ColsOut co) {
+                                                   Dropout dr, ColsOut co, int nsub) {
   constexpr int JW = JT * 16;
   constexpr int RST = 2 * TM + 16;  // bytes per staged rank row
   __shared__ __attribute__((aligned(16))) uint8_t ps[TM * 128];
@@ -468,87 +501,109 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int li = lane & 15, q = lane >> 4;
   const int64_t ct0 = (int64_t)blockIdx.x * kMColsTile;
-  const int64_t m0 = (int64_t)blockIdx.y * TM;
+  // the workgroup's token slice: nsub runs of TM tokens, one after another
+  // (the other resident workgroups of the CU cover a run's load latency)
+  const int64_t ms0 = (int64_t)blockIdx.y * TM * nsub;
 
-  // ---- R loads: rows m0 .. m0 + TM, ranks 0 .. JW ----
   constexpr int NR = RVEC ? TM * JW / 4 / 256 : TM * JW / 256;
-  f32x4 rv[RVEC ? NR : 1];
-  float re[RVEC ? 1 : NR];
-  if constexpr (RVEC) {
-#pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int e = t + 256 * b, mm = e / (JW / 4), j4 = e % (JW / 4);
-      const int64_t m = m0 + mm < M ? m0 + mm : M - 1;
-      const int jc = 4 * j4 + 4 <= r ? 4 * j4 : r - 4;
-      rv[b] = *reinterpret_cast<const f32x4 *>(R + m * r + jc);
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int e = t + 256 * b, mm = e / JW, j = e % JW;
-      re[b] = (m0 + mm < M && j < r) ? R[(m0 + mm) * r + j] : 0.0f;
-    }
-  }
-  // ---- P tile loads: rows (t >> 3) + 32 i, piece t & 7 ----
-  const int prow = t >> 3, ph = t & 7;
-  const int64_t pc = ct0 + 8 * ph;
-  const bool cok = pc + 8 <= C;
-  u32x4 pv[TM / 32];
-#pragma unroll
-  for (int i = 0; i < TM / 32; ++i) {
-    const int64_t m = m0 + prow + 32 * i;
-    pv[i] = *reinterpret_cast<const u32x4 *>(P + (m < M ? m : M - 1) * C + (cok ? pc : C - 8));
-    if (m >= M || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
-#pragma unroll
-    for (int i = 0; i < TM / 32; ++i) {
-      const int64_t m = m0 + prow + 32 * i;
-      if (m < M && cok) pv[i] = dropout_mask8(dr, (uint64_t)m * C + pc, pv[i]);
-    }
-  }
-  // ---- to LDS ----
-  if constexpr (RVEC) {
-#pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int e = t + 256 * b, mm = e / (JW / 4), j4 = e % (JW / 4);
-      const bool ok = m0 + mm < M && 4 * j4 + 4 <= r;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<uint16_t *>(rs + (4 * j4 + jj) * RST + 2 * mm) =
-            Half<AT>::bits(ok ? rv[b][jj] : 0.0f);
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int e = t + 256 * b, mm = e / JW, j = e % JW;
-      *reinterpret_cast<uint16_t *>(rs + j * RST + 2 * mm) = Half<AT>::bits(re[b]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TM / 32; ++i)
-    *reinterpret_cast<u32x4 *>(ps + ps_off(prow + 32 * i, ph)) = pv[i];
-  __syncthreads();
-
+  constexpr int RQ = RVEC ? JW / 4 : JW;  // threads per R row
+  constexpr int RROWS = 256 / RQ;
+  static_assert(256 % RQ == 0, "R rows split evenly over the threads");
   f32x4 acc[JT];
 #pragma unroll
   for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // transposing-read supplier address: rows 8q + (li >> 2) (+4), columns
-  // 16 wave + 4 (li & 3)
-  const int tr_col = 16 * wave + 4 * (li & 3);
-  const int tr_h = tr_col >> 3, tr_b = 2 * (tr_col & 7);
+
+  // One run of TM tokens from m0 into acc.  Every per-thread index is derived
+  // from tt, a copy of the thread index that the compiler may not assume
+  // constant across runs: addresses are recomputed per run instead of held
+  // in registers for the whole loop.
+  auto run = [&](int tt, int64_t m0, bool after) {
+    // R element of load b: rank column rl (4 wide for RVEC), run row
+    // rm0 + RROWS b; rows past M (and columns past r) read row M - 1 (column
+    // rj) and are zeroed when staged
+    const int rm0 = tt / RQ;
+    const int rl = RVEC ? 4 * (tt % RQ) : tt % RQ;
+    const bool rjok = RVEC ? rl + 4 <= r : rl < r;
+    const int rj = rjok || !RVEC ? rl : r - 4;
+    // P tile: rows prow + 32 i, 8-column piece ph
+    const int prow = tt >> 3, ph = tt & 7;
+    const int64_t pc = ct0 + 8 * ph;
+    const bool cok = pc + 8 <= C;
+    const bool full = m0 + TM <= M;  // uniform
+    f32x4 rv[RVEC ? NR : 1];
+    float re[RVEC ? 1 : NR];
+    u32x4 pv[TM / 32];
+    const float *rp = R + (m0 + rm0) * r + rj;
+    const AT *pp = P + (m0 + prow) * C + (cok ? pc : C - 8);
 #pragma unroll
-  for (int kk = 0; kk < TM; kk += 32) {
-    const int row = kk + 8 * q + (li >> 2);
-    const u32x2 lo = lds_tr16(ps + ps_off(row, tr_h) + tr_b);
-    const u32x2 hi = lds_tr16(ps + ps_off(row + 4, tr_h) + tr_b);
-    const u32x4 b = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) {
-      const u32x4 a =
-          *reinterpret_cast<const u32x4 *>(rs + (16 * jt + li) * RST + 2 * (kk + 8 * q));
-      acc[jt] = Half<AT>::mfma16(a, b, acc[jt]);
+    for (int b = 0; b < NR; ++b) {
+      const int64_t m = m0 + rm0 + RROWS * b;
+      if constexpr (RVEC) {
+        const float *src = full || m < M ? rp + (int64_t)RROWS * b * r : R + (M - 1) * r + rj;
+        rv[b] = *reinterpret_cast<const f32x4 *>(src);
+      } else {
+        re[b] = rjok && (full || m < M) ? rp[(int64_t)RROWS * b * r] : 0.0f;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i) {
+      const int64_t m = m0 + prow + 32 * i;
+      const AT *src =
+          full || m < M ? pp + (int64_t)32 * i * C : P + (M - 1) * C + (cok ? pc : C - 8);
+      pv[i] = *reinterpret_cast<const u32x4 *>(src);
+    }
+    if (after) __syncthreads();  // the previous run's operands have been read
+    // ---- to LDS (R and P rows past M and P pieces past C zeroed) ----
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i) {
+      const int64_t m = m0 + prow + 32 * i;
+      if (m >= M || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
+      else if constexpr (DROP)  // C % 8 == 0 on this path
+        pv[i] = dropout_mask8(dr, (uint64_t)m * C + pc, pv[i]);
+    }
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      const int mm = rm0 + RROWS * b;
+      const bool ok = m0 + mm < M && rjok;
+      if constexpr (RVEC) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<uint16_t *>(rs + (rl + jj) * RST + 2 * mm) =
+              Half<AT>::bits(ok ? rv[b][jj] : 0.0f);
+      } else {
+        *reinterpret_cast<uint16_t *>(rs + rl * RST + 2 * mm) = Half<AT>::bits(ok ? re[b] : 0.0f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i)
+      *reinterpret_cast<u32x4 *>(ps + ps_off(prow + 32 * i, ph)) = pv[i];
+    __syncthreads();
+    // ---- acc[jt] += R^T P over the run; transposing-read supplier address:
+    // rows 8 q + (li >> 2) (+4), columns 16 wave + 4 (li & 3) ----
+    const int w = tt >> 6, l = tt & 63, lj = l & 15, lq = l >> 4;
+    const int tr_col = 16 * w + 4 * (lj & 3);
+    const int tr_h = tr_col >> 3, tr_b = 2 * (tr_col & 7);
+#pragma unroll
+    for (int kk = 0; kk < TM; kk += 32) {
+      const int row = kk + 8 * lq + (lj >> 2);
+      const u32x2 lo = lds_tr16(ps + ps_off(row, tr_h) + tr_b);
+      const u32x2 hi = lds_tr16(ps + ps_off(row + 4, tr_h) + tr_b);
+      const u32x4 bb = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4 *>(rs + (16 * jt + lj) * RST + 2 * (kk + 8 * lq));
+        acc[jt] = Half<AT>::mfma16(a, bb, acc[jt]);
+      }
+    }
+  };
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int64_t m0 = ms0 + (int64_t)sub * TM;
+    if (m0 >= M) break;  // uniform
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    run(tt, m0, sub > 0);
   }
   const int64_t c = ct0 + 16 * wave + li;
   if (c < C) {
@@ -624,13 +679,29 @@ static int cols_slices(int64_t M, int64_t C) {
   return (int)s;
 }
 
-// Token slices of the matrix-core cols kernel: one per TM tokens.
-static int mcols_slices(int64_t M) { return (int)((M + kMColsTM - 1) / kMColsTM); }
+// Token slices of the matrix-core cols kernel: runs of TM tokens, nsub runs
+// per workgroup, so that the workgroups (column tiles x slices) number about
+// 1024: fewer slices write fewer partials (r x 64 floats per workgroup against
+// TM x 64 16-bit values read per run).
+struct MColsPlan {
+  int S, nsub;
+};
+static MColsPlan mcols_plan(int64_t M, int64_t C) {
+  const int64_t runs = (M + kMColsTM - 1) / kMColsTM;
+  const int64_t tiles = (C + kMColsTile - 1) / kMColsTile;
+  int64_t S = (1024 + tiles - 1) / tiles;
+  if (S > runs) S = runs;
+  if (S < 1) S = 1;
+  MColsPlan p;
+  p.nsub = (int)((runs + S - 1) / S);
+  p.S = (int)((runs + p.nsub - 1) / p.nsub);
+  return p;
+}
 
 static bool cols_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
 
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
-  const int64_t s1 = cols_slices(M, C), s2 = mcols_slices(M);
+  const int64_t s1 = cols_slices(M, C), s2 = mcols_plan(M, C).S;
   return (size_t)(s1 > s2 ? s1 : s2) * (size_t)r * (size_t)C;
 }
 
@@ -644,14 +715,15 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   if (drop && !cols_use_mfma(p_dtype, C)) return QL_EUNSUPPORTED;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (cols_use_mfma(p_dtype, C)) {
-    S = mcols_slices(M);
+    const MColsPlan mp = mcols_plan(M, C);
+    S = mp.S;
     const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
     // one token slice: the kernel writes the result, no reduction launch
     const ColsOut co{S == 1 ? out : nullptr, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0};
     const bool rvec = r % 4 == 0;
 #define QL_COLS_M(JTV, RV, DRV)                                                               \
   hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, AT, RV, DRV>), grid, dim3(256), 0, stream, R, \
-                     M, r, (const AT *)P, C, partial, dr, co)
+                     M, r, (const AT *)P, C, partial, dr, co, mp.nsub)
 #define QL_COLS_JT(JTV)                                                                          \
   do {                                                                                           \
     if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \

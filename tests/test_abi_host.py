@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 109
+    assert L.ql_abi_version() == 110
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
