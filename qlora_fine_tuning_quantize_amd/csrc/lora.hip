@@ -158,6 +158,20 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
   // copy of the thread index the compiler may not assume constant across
   // chunks, so addresses are recomputed per chunk rather than held in
   // registers over the loop.
+  // kQRowC (factor rows c contiguous in j, r % 8 == 0): a thread loads NV
+  // consecutive rows c of one 8-rank group and stages them transposed, as 8
+  // rank rows of NV 16-bit values (one 8- or 16-byte LDS store each).  Thread
+  // bits 0-2: low c block, bit 3: low rank group, the rest the high parts, so
+  // that one 16-lane store pass covers 16 distinct bank quads.
+  constexpr int NCB = CS / NV;                    // c blocks
+  static_assert(QMODE != kQRowC || (NCB % 8 == 0 && (JW / 8) % 2 == 0 &&
+                                    NCB * (JW / 8) == 256 && (NV == 4 || NV == 8)),
+                "factor blocks tile the chunk");
+  auto rowc_block = [&](int tt, int &cb, int &j8) {
+    const int hi = tt >> 4;
+    cb = (tt & 7) + 8 * (hi % (NCB / 8));
+    j8 = ((tt >> 3) & 1) + 2 * (hi / (NCB / 8));
+  };
   auto chunk = [&](int tt, int64_t c0, bool after) {
     const int w = tt >> 6, l = tt & 63, lj = l & 15, lq = l >> 4;
     // ---- factor loads (issued first) ----
@@ -173,12 +187,15 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
         qv[b].load(Q + (int64_t)jc * ldq_j + cc);
       }
     } else if constexpr (QMODE == kQRowC) {
+      int cb, j8;
+      rowc_block(tt, cb, j8);
+      const QT *qb = Q + c0 * ldq_c;  // uniform
+      const int jc = 8 * j8 + 8 <= r ? 8 * j8 : r - 8;
+      const int clast = (int)(C - 1 - c0);
 #pragma unroll
-      for (int b = 0; b < NV; ++b) {
-        const int e = tt + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
-        const int64_t c = c0 + cc < C ? c0 + cc : C - 1;
-        const int jc = 8 * j8 + 8 <= r ? 8 * j8 : r - 8;
-        qv[b].load(Q + c * ldq_c + jc);
+      for (int i = 0; i < NV; ++i) {
+        const int cr = NV * cb + i;
+        qv[i].load(qb + (int64_t)(cr < clast ? cr : clast) * ldq_c + jc);
       }
     } else {
 #pragma unroll
@@ -191,22 +208,19 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
       }
     }
 
-    // ---- P loads: row mrow, contraction c0 + 32 i + 8 lq ----
-    const int64_t mrow = (int64_t)blockIdx.x * kMRowsTile + 16 * w + lj;
-    const AT *prow = P + (mrow < M ? mrow : M - 1) * C;
+    // ---- P loads: row mrow, contraction c0 + 32 i + 8 lq (32-bit offsets
+    // from the tile's uniform base: 64 C < 2^31 on this path) ----
+    const int64_t mt0 = (int64_t)blockIdx.x * kMRowsTile;
+    const int mr = 16 * w + lj;
+    const int mrc = mt0 + mr < M ? mr : (int)(M - 1 - mt0);
+    const AT *pb = P + mt0 * C + c0;  // uniform
     u32x4 a[CS / 32];
 #pragma unroll
     for (int i = 0; i < CS / 32; ++i) {
       const int64_t c = c0 + 32 * i + 8 * lq;
-      a[i] = *reinterpret_cast<const u32x4 *>(prow + (c + 8 <= C ? c : C - 8));
-      if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (DROP) {  // after every load is out; C % 8 == 0 on this path
-#pragma unroll
-      for (int i = 0; i < CS / 32; ++i) {
-        const int64_t c = c0 + 32 * i + 8 * lq;
-        if (c + 8 <= C) a[i] = dropout_mask8(dr, (uint64_t)mrow * C + c, a[i]);
-      }
+      const int cl = c + 8 <= C ? 32 * i + 8 * lq : (int)(C - 8 - c0);
+      a[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(pb) +
+                                               (uint32_t)((mrc * (int)C + cl) * 2));
     }
 
     if (after) __syncthreads();  // the previous chunk's factor has been read
@@ -216,21 +230,44 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
       for (int b = 0; b < NV; ++b) {
         const int e = tt + 256 * b, j = e / (CS / 8), c8 = e % (CS / 8);
         const bool ok = j < r && c0 + 8 * c8 + 8 <= C;
-        *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) =
-            u32x4{Half<AT>::pack2(qv[b].get(0, ok), qv[b].get(1, ok)),
-                  Half<AT>::pack2(qv[b].get(2, ok), qv[b].get(3, ok)),
-                  Half<AT>::pack2(qv[b].get(4, ok), qv[b].get(5, ok)),
-                  Half<AT>::pack2(qv[b].get(6, ok), qv[b].get(7, ok))};
+        u32x4 v;
+        if constexpr (sizeof(QT) == 2) {  // the operands' own format: copied
+          v = ok ? qv[b].w : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          v = u32x4{Half<AT>::pack2(qv[b].get(0, ok), qv[b].get(1, ok)),
+                    Half<AT>::pack2(qv[b].get(2, ok), qv[b].get(3, ok)),
+                    Half<AT>::pack2(qv[b].get(4, ok), qv[b].get(5, ok)),
+                    Half<AT>::pack2(qv[b].get(6, ok), qv[b].get(7, ok))};
+        }
+        *reinterpret_cast<u32x4 *>(qs + j * QST + 16 * c8) = v;
       }
     } else if constexpr (QMODE == kQRowC) {
+      int cb, j8;
+      rowc_block(tt, cb, j8);
+      const bool jok = 8 * j8 + 8 <= r;
+      bool ok[NV];
 #pragma unroll
-      for (int b = 0; b < NV; ++b) {
-        const int e = tt + 256 * b, cc = e / (JW / 8), j8 = e % (JW / 8);
-        const bool ok = c0 + cc < C && 8 * j8 + 8 <= r;
+      for (int i = 0; i < NV; ++i) ok[i] = jok && c0 + NV * cb + i < C;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          *reinterpret_cast<uint16_t *>(qs + (8 * j8 + jj) * QST + 2 * cc) =
-              Half<AT>::bits(qv[b].get(jj, ok));
+      for (int jj = 0; jj < 8; ++jj) {
+        uint32_t o[NV / 2];
+#pragma unroll
+        for (int k = 0; k < NV / 2; ++k) {
+          if constexpr (sizeof(QT) == 2) {
+            // halves jj of rows 2k (low) and 2k + 1 (high), by byte select
+            const uint32_t lo = ok[2 * k] ? qv[2 * k].w[jj >> 1] : 0u;
+            const uint32_t hi = ok[2 * k + 1] ? qv[2 * k + 1].w[jj >> 1] : 0u;
+            o[k] = __builtin_amdgcn_perm(hi, lo, (jj & 1) ? 0x07060302u : 0x05040100u);
+          } else {
+            o[k] = Half<AT>::pack2(qv[2 * k].get(jj, ok[2 * k]),
+                                   qv[2 * k + 1].get(jj, ok[2 * k + 1]));
+          }
+        }
+        uint8_t *dst = qs + (8 * j8 + jj) * QST + 2 * NV * cb;
+        if constexpr (NV == 8)
+          *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+        else
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{o[0], o[1]};
       }
     } else {
 #pragma unroll
@@ -242,6 +279,15 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
       }
     }
     __syncthreads();
+    // P pieces past C zeroed, dropout applied: where the operands are used
+    // (no earlier wait on the P loads)
+#pragma unroll
+    for (int i = 0; i < CS / 32; ++i) {
+      const int64_t c = c0 + 32 * i + 8 * lq;
+      if (c + 8 > C) a[i] = u32x4{0u, 0u, 0u, 0u};
+      else if constexpr (DROP)  // C % 8 == 0 on this path
+        a[i] = dropout_mask8(dr, (uint64_t)(mt0 + mr) * C + c, a[i]);
+    }
 #pragma unroll
     for (int i = 0; i < CS / 32; ++i) {
 #pragma unroll
@@ -321,7 +367,10 @@ static MRowsPlan mrows_plan(int64_t M, int64_t C, int32_t r, int q_dtype) {
   return p;
 }
 
-static bool rows_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
+// 32-bit offsets within a 64-row tile: C < 2^24
+static bool rows_use_mfma(int p_dtype, int64_t C) {
+  return p_dtype != QL_F32 && C % 8 == 0 && C < ((int64_t)1 << 24);
+}
 
 size_t lora_rows_partial_floats(int64_t M, int64_t C, int32_t r) {
   const int64_t s1 = rows_slices(M, C);
@@ -505,79 +554,131 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
   // (the other resident workgroups of the CU cover a run's load latency)
   const int64_t ms0 = (int64_t)blockIdx.y * TM * nsub;
 
-  constexpr int NR = RVEC ? TM * JW / 4 / 256 : TM * JW / 256;
-  constexpr int RQ = RVEC ? JW / 4 : JW;  // threads per R row
+  // R with r % 4 == 0 (RVEC): load group g of a thread covers TG consecutive
+  // tokens x 4 ranks (TG loads of 16 bytes) and is staged as 4 rank rows of
+  // TG 16-bit values (one 8- or 16-byte LDS store each).  Group id
+  // gid = tt + 256 g splits as: bits 0-1 the low rank group, bits 2-3 the low
+  // token group, the rest (rank group high, token group high), so that the 16
+  // lanes of one store pass write 16 distinct bank quads and one load
+  // instruction reads whole 64-byte row pieces.  Other r: one value per load.
+  constexpr int RG = JW / 4;                      // 4-rank groups
+  constexpr int NRV = TM * JW / 4 / 256;          // 16-byte R loads per thread
+  constexpr int TG = NRV < 8 ? NRV : 8;           // tokens per load group
+  constexpr int NG = NRV / TG;                    // load groups per thread
+  static_assert(NG * TG == NRV && (TM / TG) * RG == 256 * NG && RG % 4 == 0,
+                "R load groups tile the run");
+  constexpr int NR = RVEC ? NRV : TM * JW / 256;
+  constexpr int RQ = JW;  // scalar path: threads per R row
   constexpr int RROWS = 256 / RQ;
   static_assert(256 % RQ == 0, "R rows split evenly over the threads");
   f32x4 acc[JT];
 #pragma unroll
   for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One run of TM tokens from m0 into acc.  Every per-thread index is derived
-  // from tt, a copy of the thread index that the compiler may not assume
-  // constant across runs: addresses are recomputed per run instead of held
-  // in registers for the whole loop.
-  auto run = [&](int tt, int64_t m0, bool after) {
-    // R element of load b: rank column rl (4 wide for RVEC), run row
-    // rm0 + RROWS b; rows past M (and columns past r) read row M - 1 (column
-    // rj) and are zeroed when staged
-    const int rm0 = tt / RQ;
-    const int rl = RVEC ? 4 * (tt % RQ) : tt % RQ;
-    const bool rjok = RVEC ? rl + 4 <= r : rl < r;
-    const int rj = rjok || !RVEC ? rl : r - 4;
+  // A run of TM tokens: load (R and P to registers), stage (to LDS), mma
+  // (into acc).  The next run's loads are issued right after a run is staged,
+  // so they are in flight during its matrix ops and barriers.  Per-thread
+  // indices come from tt, a copy of the thread index that the compiler may
+  // not assume constant across runs: addresses are recomputed per run instead
+  // of held in registers over the loop.  Offsets within a run are 32-bit
+  // (TM * C < 2^31 on this path).
+  f32x4 rv[RVEC ? NRV : 1];
+  float re[RVEC ? 1 : NR];
+  u32x4 pv[TM / 32];
+  auto load = [&](int tt, int64_t m0) {
+    const bool full = m0 + TM <= M;  // uniform
+    const int mlast = full ? TM - 1 : (int)(M - 1 - m0);  // last row of the run
+    const float *Rb = R + m0 * r;
     // P tile: rows prow + 32 i, 8-column piece ph
     const int prow = tt >> 3, ph = tt & 7;
     const int64_t pc = ct0 + 8 * ph;
     const bool cok = pc + 8 <= C;
+    const AT *Pb = P + m0 * C + ct0;  // uniform
+    const int pcl = cok ? 8 * ph : (int)(C - 8 - ct0);
+    if constexpr (RVEC) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int gid = tt + 256 * g, hi = gid >> 4;
+        const int rgi = (gid & 3) + 4 * (hi % (RG / 4));
+        const int tgi = ((gid >> 2) & 3) + 4 * (hi / (RG / 4));
+        const int col = 4 * rgi + 4 <= r ? 4 * rgi : r - 4;
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          const int row = TG * tgi + i;
+          rv[TG * g + i] = *reinterpret_cast<const f32x4 *>(
+              reinterpret_cast<const uint8_t *>(Rb) +
+              (uint32_t)(((row < mlast ? row : mlast) * r + col) * 4));
+        }
+      }
+    } else {
+      const int rm0 = tt / RQ, rl = tt % RQ;
+#pragma unroll
+      for (int b = 0; b < NR; ++b) {
+        const int row = rm0 + RROWS * b;
+        re[b] = rl < r && row <= mlast ? Rb[row * r + rl] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i) {
+      const int row = prow + 32 * i;
+      const int rc = row < mlast ? row : mlast;
+      pv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(Pb) +
+                                                (uint32_t)((rc * (int)C + pcl) * 2));
+    }
+  };
+  auto stage = [&](int tt, int64_t m0) {
     const bool full = m0 + TM <= M;  // uniform
-    f32x4 rv[RVEC ? NR : 1];
-    float re[RVEC ? 1 : NR];
-    u32x4 pv[TM / 32];
-    const float *rp = R + (m0 + rm0) * r + rj;
-    const AT *pp = P + (m0 + prow) * C + (cok ? pc : C - 8);
-#pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int64_t m = m0 + rm0 + RROWS * b;
-      if constexpr (RVEC) {
-        const float *src = full || m < M ? rp + (int64_t)RROWS * b * r : R + (M - 1) * r + rj;
-        rv[b] = *reinterpret_cast<const f32x4 *>(src);
-      } else {
-        re[b] = rjok && (full || m < M) ? rp[(int64_t)RROWS * b * r] : 0.0f;
-      }
-    }
+    const int mlast = full ? TM - 1 : (int)(M - 1 - m0);
+    const int prow = tt >> 3, ph = tt & 7;
+    const int64_t pc = ct0 + 8 * ph;
+    const bool cok = pc + 8 <= C;
+    // ---- to LDS (R and P rows past M, R ranks past r and P pieces past C
+    // zeroed) ----
 #pragma unroll
     for (int i = 0; i < TM / 32; ++i) {
-      const int64_t m = m0 + prow + 32 * i;
-      const AT *src =
-          full || m < M ? pp + (int64_t)32 * i * C : P + (M - 1) * C + (cok ? pc : C - 8);
-      pv[i] = *reinterpret_cast<const u32x4 *>(src);
-    }
-    if (after) __syncthreads();  // the previous run's operands have been read
-    // ---- to LDS (R and P rows past M and P pieces past C zeroed) ----
-#pragma unroll
-    for (int i = 0; i < TM / 32; ++i) {
-      const int64_t m = m0 + prow + 32 * i;
-      if (m >= M || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
+      const int row = prow + 32 * i;
+      if (row > mlast || !cok) pv[i] = u32x4{0u, 0u, 0u, 0u};
       else if constexpr (DROP)  // C % 8 == 0 on this path
-        pv[i] = dropout_mask8(dr, (uint64_t)m * C + pc, pv[i]);
+        pv[i] = dropout_mask8(dr, (uint64_t)(m0 + row) * C + pc, pv[i]);
     }
+    if constexpr (RVEC) {
 #pragma unroll
-    for (int b = 0; b < NR; ++b) {
-      const int mm = rm0 + RROWS * b;
-      const bool ok = m0 + mm < M && rjok;
-      if constexpr (RVEC) {
+      for (int g = 0; g < NG; ++g) {
+        const int gid = tt + 256 * g, hi = gid >> 4;
+        const int rgi = (gid & 3) + 4 * (hi % (RG / 4));
+        const int tgi = ((gid >> 2) & 3) + 4 * (hi / (RG / 4));
+        const bool rok = 4 * rgi + 4 <= r;
+        float v[TG][4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<uint16_t *>(rs + (rl + jj) * RST + 2 * mm) =
-              Half<AT>::bits(ok ? rv[b][jj] : 0.0f);
-      } else {
-        *reinterpret_cast<uint16_t *>(rs + rl * RST + 2 * mm) = Half<AT>::bits(ok ? re[b] : 0.0f);
+        for (int i = 0; i < TG; ++i) {
+          const bool ok = rok && TG * tgi + i <= mlast;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v[i][jj] = ok ? rv[TG * g + i][jj] : 0.0f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint8_t *dst = rs + (4 * rgi + jj) * RST + 2 * TG * tgi;
+          if constexpr (TG == 8)
+            *reinterpret_cast<u32x4 *>(dst) =
+                u32x4{Half<AT>::pack2(v[0][jj], v[1][jj]), Half<AT>::pack2(v[2][jj], v[3][jj]),
+                      Half<AT>::pack2(v[4][jj], v[5][jj]), Half<AT>::pack2(v[6][jj], v[7][jj])};
+          else
+            *reinterpret_cast<u32x2 *>(dst) =
+                u32x2{Half<AT>::pack2(v[0][jj], v[1][jj]), Half<AT>::pack2(v[2][jj], v[3][jj])};
+        }
       }
+    } else {
+      const int rm0 = tt / RQ, rl = tt % RQ;
+#pragma unroll
+      for (int b = 0; b < NR; ++b)
+        *reinterpret_cast<uint16_t *>(rs + rl * RST + 2 * (rm0 + RROWS * b)) =
+            Half<AT>::bits(re[b]);
     }
 #pragma unroll
     for (int i = 0; i < TM / 32; ++i)
       *reinterpret_cast<u32x4 *>(ps + ps_off(prow + 32 * i, ph)) = pv[i];
-    __syncthreads();
+  };
+  auto mma = [&](int tt) {
     // ---- acc[jt] += R^T P over the run; transposing-read supplier address:
     // rows 8 q + (li >> 2) (+4), columns 16 wave + 4 (li & 3) ----
     const int w = tt >> 6, l = tt & 63, lj = l & 15, lq = l >> 4;
@@ -597,13 +698,22 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
       }
     }
   };
-#pragma unroll 1
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int64_t m0 = ms0 + (int64_t)sub * TM;
-    if (m0 >= M) break;  // uniform
+  const int nrun = (int)((M - ms0 + TM - 1) / TM < nsub ? (M - ms0 + TM - 1) / TM : nsub);
+  {
     int tt = t;
     asm volatile("" : "+v"(tt));
-    run(tt, m0, sub > 0);
+    load(tt, ms0);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nrun; ++sub) {
+    const int64_t m0 = ms0 + (int64_t)sub * TM;
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    if (sub > 0) __syncthreads();  // the previous run's operands have been read
+    stage(tt, m0);
+    __syncthreads();
+    if (sub + 1 < nrun) load(tt, m0 + TM);
+    mma(tt);
   }
   const int64_t c = ct0 + 16 * wave + li;
   if (c < C) {
@@ -646,19 +756,72 @@ __device__ __forceinline__ void reduce_cols_one(const ColsReduce &jb, int64_t e)
     for (int b = 0; b < 8; ++b)
       if (i0 + b < jb.S) s += v[b];
   }
-  const int64_t j = e / jb.C, c = e % jb.C;
-  const int64_t o = jb.c_major ? c * jb.r + j : e;
-  jb.out[o] = jb.accumulate ? jb.out[o] + jb.scale * s : jb.scale * s;
+  jb.out[e] = jb.accumulate ? jb.out[e] + jb.scale * s : jb.scale * s;
+}
+
+// The transposed ([C][r]) result: a workgroup takes 64 columns x 32 ranks;
+// each thread sums 8 elements (as above, slices in increasing order, four
+// slices of all 8 elements loaded before they are added) into an LDS tile
+// [j][c], which is then written with j fastest (128-byte row pieces).
+constexpr int kRedTC = 64, kRedTJ = 32;
+__device__ __forceinline__ void reduce_cols_tile(const ColsReduce &jb, int64_t blk,
+                                                 float (*tile)[kRedTC + 1]) {
+#pragma clang fp contract(off)
+  constexpr int NE = kRedTC * kRedTJ / 256;
+  const int t = threadIdx.x, cl = t % kRedTC, jq = t / kRedTC;
+  const int64_t count = (int64_t)jb.r * jb.C;
+  const int64_t jtiles = (jb.r + kRedTJ - 1) / kRedTJ;
+  const int64_t c0 = blk / jtiles * kRedTC, c = c0 + cl;
+  const int j0 = (int)(blk % jtiles) * kRedTJ;
+  float s[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) s[k] = 0.0f;
+  for (int i0 = 0; i0 < jb.S; i0 += 4) {
+    float v[NE][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int j = j0 + jq + (256 / kRedTC) * k;
+        v[k][b] = i0 + b < jb.S && j < jb.r && c < jb.C
+                      ? jb.partial[(int64_t)(i0 + b) * count + (int64_t)j * jb.C + c]
+                      : 0.0f;
+      }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int k = 0; k < NE; ++k)
+        if (i0 + b < jb.S) s[k] += v[k][b];
+  }
+#pragma unroll
+  for (int k = 0; k < NE; ++k) tile[jq + (256 / kRedTC) * k][cl] = jb.scale * s[k];
+  __syncthreads();
+  const int ncol = (int)(jb.C - c0 < kRedTC ? jb.C - c0 : kRedTC);
+  const int nj = jb.r - j0 < kRedTJ ? jb.r - j0 : kRedTJ;
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int idx = t + 256 * k, cc = idx / kRedTJ, jj = idx % kRedTJ;
+    if (cc < ncol && jj < nj) {
+      const int64_t o = (c0 + cc) * jb.r + j0 + jj;
+      const float v = tile[jj][cc];
+      jb.out[o] = jb.accumulate ? jb.out[o] + v : v;
+    }
+  }
 }
 
 static int64_t reduce_cols_blocks(const ColsReduce &jb) {
-  return jb.S > 0 ? ((int64_t)jb.r * jb.C + 255) / 256 : 0;
+  if (jb.S <= 0) return 0;
+  return jb.c_major ? (jb.C + kRedTC - 1) / kRedTC * ((jb.r + kRedTJ - 1) / kRedTJ)
+                    : ((int64_t)jb.r * jb.C + 255) / 256;
 }
 
 __global__ __launch_bounds__(256) void k_reduce_cols(ColsReduce a, ColsReduce b, int64_t blocks_a) {
+  __shared__ float tile[kRedTJ][kRedTC + 1];
   const int64_t blk = blockIdx.x;
-  if (blk < blocks_a) reduce_cols_one(a, blk * 256 + threadIdx.x);
-  else reduce_cols_one(b, (blk - blocks_a) * 256 + threadIdx.x);
+  const ColsReduce &jb = blk < blocks_a ? a : b;
+  const int64_t bi = blk < blocks_a ? blk : blk - blocks_a;
+  if (jb.c_major) reduce_cols_tile(jb, bi, tile);  // uniform
+  else reduce_cols_one(jb, bi * 256 + threadIdx.x);
 }
 
 int launch_reduce_cols(const ColsReduce &a, const ColsReduce &b, hipStream_t stream) {
@@ -698,7 +861,10 @@ static MColsPlan mcols_plan(int64_t M, int64_t C) {
   return p;
 }
 
-static bool cols_use_mfma(int p_dtype, int64_t C) { return p_dtype != QL_F32 && C % 8 == 0; }
+// 32-bit offsets within a 256-token run: C < 2^22
+static bool cols_use_mfma(int p_dtype, int64_t C) {
+  return p_dtype != QL_F32 && C % 8 == 0 && C < ((int64_t)1 << 22);
+}
 
 size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
   const int64_t s1 = cols_slices(M, C), s2 = mcols_plan(M, C).S;
