@@ -608,6 +608,28 @@ def test_mlp70b_config_full_size_sampled(orc, proj):
         assert e <= BF16_TOL, (k, e)
 
 
+@pytest.mark.parametrize("M,N,K,r", [
+    (1000, 28608, 4096, 64),   # g: several factor chunks per workgroup, the last ragged;
+                               # dB: several token runs per workgroup, the last ragged
+    (1000, 4096, 28544, 64),   # u and dA: the same over the contraction K
+    (900, 22000, 1024, 18),    # dB with r % 4 != 0 (one value per R load), two runs
+])
+def test_lora_products_multi_chunk_ragged(orc, M, N, K, r):
+    """The LoRA products (u, g, dA, dB) where a workgroup covers several
+    contraction chunks or token runs and the last one is cut short: y and dx
+    on 32 sampled token rows, dA and dB in full, every output within its
+    per-element bound."""
+    rows = np.sort(np.random.default_rng(6).choice(M, 32, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    _say(f"lora multi-chunk M={M} N={N} K={K} r={r}")
+    got, ref = _layer_case(orc, M, N, K, r, True, torch.bfloat16, torch.bfloat16,
+                           alpha=16.0, rows=rows)
+    errs = {k: rel_err(got[k], ref[k]) for k in ("y", "u", "dx", "dA", "dB")}
+    _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= BF16_TOL, (k, e)
+
+
 @pytest.mark.parametrize("layer", [0, 31])
 def test_weightset_layer_bit_exact(orc, layer):
     """8B-shaped weight set (N(0, 0.02) with 0.1% outliers at 20 sigma): every
