@@ -154,10 +154,6 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
 #pragma unroll
   for (int i = 0; i < JT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One CS-wide chunk from c0 into acc.  Per-thread indices come from tt, a
-  // copy of the thread index the compiler may not assume constant across
-  // chunks, so addresses are recomputed per chunk rather than held in
-  // registers over the loop.
   // kQRowC (factor rows c contiguous in j, r % 8 == 0): a thread loads NV
   // consecutive rows c of one 8-rank group and stages them transposed, as 8
   // rank rows of NV 16-bit values (one 8- or 16-byte LDS store each).  Thread
@@ -172,6 +168,10 @@ __global__ __launch_bounds__(256) void k_rows_mfma(const AT *__restrict__ P, int
     cb = (tt & 7) + 8 * (hi % (NCB / 8));
     j8 = ((tt >> 3) & 1) + 2 * (hi / (NCB / 8));
   };
+  // One CS-wide chunk from c0 into acc.  Per-thread indices come from tt, a
+  // copy of the thread index the compiler may not assume constant across
+  // chunks, so addresses are recomputed per chunk rather than held in
+  // registers over the loop.
   auto chunk = [&](int tt, int64_t c0, bool after) {
     const int w = tt >> 6, l = tt & 63, lj = l & 15, lq = l >> 4;
     // ---- factor loads (issued first) ----
@@ -496,11 +496,12 @@ __global__ __launch_bounds__(256) void k_lora_cols(const float *__restrict__ R, 
 // ---------------------------------------------------------------------------
 // cols on the matrix cores (16-bit P): D[j][c] = sum_m R^T[j][m] P[m][c] with
 // v_mfma_f32_16x16x32_{bf16,f16}.  The workgroup owns 64 columns (wave w: columns
-// 16w..16w+15, all JT rank tiles) and one TM-token slice, in one round trip
-// with compile-time trip counts: the loads of R (fp32, 4 ranks per load when
-// r % 4 == 0) and of the P tile (16 bytes per lane) are all issued first,
-// then R^T is written to LDS in P's format [j][m] and the P tile as [m][c]
-// (128-byte rows), one barrier, the MFMAs, and the fp32 partial sums.  The
+// 16w..16w+15, all JT rank tiles) and one token slice of nsub runs of TM
+// tokens.  Per run, with compile-time trip counts: the loads of R (fp32, 4
+// ranks per load when r % 4 == 0) and of the P tile (16 bytes per lane) are
+// issued together, then R^T is written to LDS in P's format [j][m] and the P
+// tile as [m][c] (128-byte rows), one barrier, the next run's loads, the
+// MFMAs; the fp32 sums of the slice are written at the end.  The
 // B operand (8 consecutive tokens of one column) comes from gfx950's
 // transposing LDS read: for a group of 16 lanes naming rows m0..m0+3
 // (lanes 4e..4e+3 -> row m0+e, four columns each), output lane i receives
@@ -551,7 +552,6 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
   const int li = lane & 15, q = lane >> 4;
   const int64_t ct0 = (int64_t)blockIdx.x * kMColsTile;
   // the workgroup's token slice: nsub runs of TM tokens, one after another
-  // (the other resident workgroups of the CU cover a run's load latency)
   const int64_t ms0 = (int64_t)blockIdx.y * TM * nsub;
 
   // R with r % 4 == 0 (RVEC): load group g of a thread covers TG consecutive
