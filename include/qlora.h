@@ -295,8 +295,8 @@ int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const 
  *     dA = g^T xd,  dx = dy W^ + d .* (g A).
  * accumulate 0 overwrites dA and dB, 1 adds into them (as
  * qlora_linear_bwd_acc).  Workspace as qlora_linear_bwd.  dropout_p > 0
- * requires 16-bit activations and, when dx is wanted, N % 64 == 0 and
- * K % 128 == 0 (QL_EUNSUPPORTED otherwise).
+ * requires 16-bit activations and, when dx is wanted, N % 8 == 0
+ * (QL_EUNSUPPORTED otherwise).
  * Errors: as qlora_linear_bwd; QL_EINVAL for dropout_p outside [0, 1) or
  * accumulate not 0/1.
  */
@@ -354,7 +354,10 @@ const char *ql_strerror(int status);
  *        contraction slices) on large weights.
  *   110: the LoRA products (u, g, dA, dB) cover several contraction chunks
  *        per workgroup: fewer slices, smaller forward and backward
- *        workspaces on large shapes. */
+ *        workspaces on large shapes.
+ *   111: the matrix-core input gradient takes N % 8 == 0 and any K of the
+ *        layer (before: N % 64 == 0, K % 128 == 0), so more backward
+ *        workspaces hold its split-K partials. */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

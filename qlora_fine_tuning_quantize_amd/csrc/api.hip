@@ -161,7 +161,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 110; }
+int ql_abi_version(void) { return 111; }
 
 const char *ql_strerror(int status) {
   switch (status) {

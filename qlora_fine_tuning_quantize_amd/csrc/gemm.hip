@@ -193,14 +193,15 @@ __device__ __forceinline__ void stage_lora(uint8_t *dst, const T *__restrict__ s
 
 // ROWS x 16 slice of the transpose of a row-major [r, ld] factor: staged
 // row `row` holds src[(j0 + jj) * ld + col0 + row], jj = 0..15 (lanes walk
-// along a source row, so the loads are coalesced).
+// along a source row, so the loads are coalesced); columns past ld and
+// ranks past r are zero.
 template <int ROWS, int NT, typename AT, typename T>
 __device__ __forceinline__ void stage_lora_t(uint8_t *dst, const T *__restrict__ src, int64_t ld,
                                              int64_t col0, int32_t r, int j0, int t) {
   for (int e = t; e < ROWS * 16; e += NT) {
     const int jj = e / ROWS, row = e % ROWS;
     float v = 0.0f;
-    if (j0 + jj < r) v = load_as_f32(src, (int64_t)(j0 + jj) * ld + col0 + row);
+    if (j0 + jj < r && col0 + row < ld) v = load_as_f32(src, (int64_t)(j0 + jj) * ld + col0 + row);
     *reinterpret_cast<uint16_t *>(dst + row * kLoraStride + 2 * jj) = Half<AT>::bits(v);
   }
 }
@@ -689,9 +690,12 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
   if (t < 256) lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, kt;
-  tile_of((M + BM - 1) / BM, K / BX, mt, kt);
+  tile_of((M + BM - 1) / BM, (K + BX - 1) / BX, mt, kt);
   const int64_t m0 = mt * BM, k0 = kt * BX;
-  const int64_t NS = N / kDxBC;
+  // contraction steps of 64 outputs n; with N % 64 != 0 the last one is
+  // ragged (N % 8 == 0): its dy columns past N are staged as zeros and its
+  // weight rows past N repeat row N - 1 (finite values times zero)
+  const int64_t NS = (N + kDxBC - 1) / kDxBC;
   // contraction slice of this workgroup (split-K: grid row blockIdx.y)
   const int split = blockIdx.y;
   const int ks0 = (int)(split * NS / nsplit), ks1 = (int)((split + 1) * NS / nsplit);
@@ -703,8 +707,12 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
   uint32_t wr[NU];
   int wq;
   float wsig;
+  // columns past K (the last column tile when K % BX != 0, K % 64 == 0)
+  // load the row's last codes instead; they feed only unstored outputs
+  const int64_t wcol = k0 + wk + 8 * NU <= K ? k0 + wk : K - 8 * NU;
   auto load_w = [&](int step) {
-    const int64_t e = ((int64_t)step * kDxBC + wrow) * K + k0 + wk;
+    const int64_t n = (int64_t)step * kDxBC + wrow;
+    const int64_t e = (n < N ? n : N - 1) * K + wcol;
     if constexpr (NU == 2) {
       const u32x2 v = *reinterpret_cast<const u32x2 *>(packed + (e >> 1));
       wr[0] = v[0];
@@ -725,24 +733,30 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
       wsig = sc.absmax[b];
     }
   };
-  // token rows past M are clamped (their outputs are never stored)
+  // token rows past M are clamped (their outputs are never stored); a chunk
+  // past N loads the row's last chunk and is staged as zeros
   const uint16_t *dy_src[XC];
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
     const int id = t + NT * i;
     const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
-    dy_src[i] = dy + rr * N + 8 * (id & 7);
+    dy_src[i] = dy + rr * N;
   }
+  auto dy_col = [&](int step, int i) {
+    return (int64_t)step * kDxBC + 8 * ((t + NT * i) & 7);
+  };
   auto load_dy_chunk = [&](int step, int i) {
-    drv[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (int64_t)step * kDxBC);
+    const int64_t c = dy_col(step, i);
+    drv[i] = *reinterpret_cast<const u32x4 *>(dy_src[i] + (c < N ? c : N - 8));
   };
   // quarter q of one step's staging: the dy chunk(s) of that quarter, and
   // the weight words assigned to it (one word = 8 codes = one 16-byte chunk)
-  auto store_quarter = [&](int buf, int qq) {
+  auto store_quarter = [&](int buf, int qq, int step) {
     if (XC == 4 || (qq & 1) == 0) {
       const int ci = XC == 4 ? qq : qq >> 1;
       const int id = t + NT * ci;
-      *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) = drv[ci];
+      *reinterpret_cast<u32x4 *>(ds[buf] + swz(id >> 3, id & 7)) =
+          dy_col(step, ci) < N ? drv[ci] : u32x4{0u, 0u, 0u, 0u};
     }
     constexpr int every = 4 / NU;
     if (qq % every == 0) {
@@ -790,7 +804,7 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
     stage_lora_t<BX, NT, AT>(ls_a, A, K, k0, r, 0, t);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) store_quarter(0, i);
+  for (int i = 0; i < 4; ++i) store_quarter(0, i, ks0);
 #pragma unroll
   for (int i = 0; i < XC; ++i) load_dy_chunk(ks0 + 1 < ks1 ? ks0 + 1 : ks0, i);
   load_w(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
@@ -859,7 +873,7 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
         for (int j = 0; j < NJ; ++j) b[nb][j] = read_b(wb, kk + 1, j);
       }
       // each dy chunk is reloaded right after it was stored
-      store_quarter(cur ^ 1, kk);
+      store_quarter(cur ^ 1, kk, k + 1 < ks1 ? k + 1 : ks1 - 1);
       if (XC == 4) load_dy_chunk(pf, kk);
       else if ((kk & 1) == 0) load_dy_chunk(pf, kk >> 1);
       if (kk == 3) load_w(pf);
@@ -890,13 +904,14 @@ __global__ __launch_bounds__(DxShape<BM>::NT) void k_gemm_dx(const uint16_t *__r
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<AT>(ab[j], ga[i], acc[i][j]);
   }
-  // K % 128 == 0 here, so every tile is full in the column direction
   if (nsplit > 1)
     store_tile_f32<MI, NJ>(part + (int64_t)split * M * K, K, M, K, m0 + TM * wm, k0 + TX * wn,
                            acc, lane);
-  else  // per-wave slices of 32 rows in a dead staging buffer
+  else if (k0 + BX <= K)  // per-wave slices of 32 rows in a dead staging buffer
     store_tile_lds<AT, MI, NJ>(dx, K, M, m0 + TM * wm, k0 + TX * wn, acc,
                            (BM == 256 ? &ds[0][0] : &wt[0][0]) + wave * 32 * (2 * TX + 16), lane);
+  else  // the ragged last column tile (K % BX != 0)
+    store_tile_t<AT, MI, NJ>(dx, K, M, K, m0 + TM * wm, k0 + TX * wn, acc, lane);
 }
 
 // Split-K: a launch with fewer tiles than the chip runs at once (a few
@@ -990,8 +1005,9 @@ static int fwd_split(int64_t M, int64_t N, int64_t K) {
 constexpr int64_t kDxSmallM = 128;
 
 static int dx_split(int64_t M, int64_t N, int64_t K) {
-  if (M <= kDxSmallM) return split_count(((M + 63) / 64) * (K / 128), N / kDxBC, M, K, 512);
-  return plan_tiles(M, K, N / kDxBC, K % 256 == 0, true).S;
+  const int64_t steps = (N + kDxBC - 1) / kDxBC;
+  if (M <= kDxSmallM) return split_count(((M + 63) / 64) * ((K + 127) / 128), steps, M, K, 512);
+  return plan_tiles(M, K, steps, K % 256 == 0, true).S;
 }
 
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K) {
@@ -1110,7 +1126,8 @@ int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_
                            stream);
 }
 
-bool gemm_dx_supported(int64_t N, int64_t K) { return N % kDxBC == 0 && K % 128 == 0; }
+// 16-byte loads of dy rows and of 8-code words: N % 8 == 0 and K % 64 == 0
+bool gemm_dx_supported(int64_t N, int64_t K) { return N % 8 == 0 && N >= 8 && K % 64 == 0; }
 
 int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *packed,
                    BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
@@ -1122,9 +1139,10 @@ int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *pac
   const bool small = M <= kDxSmallM;
   const int bm = small ? 64 : kBM;
   const TilePlan pl = small ? TilePlan{128, part ? dx_split(M, N, K) : 1}
-                            : plan_tiles(M, K, N / kDxBC, K % 256 == 0, part != nullptr);
+                            : plan_tiles(M, K, (N + kDxBC - 1) / kDxBC, K % 256 == 0,
+                                         part != nullptr);
   const int bx = pl.bn, S = pl.S;
-  const int64_t G = ((M + bm - 1) / bm) * (K / bx);
+  const int64_t G = ((M + bm - 1) / bm) * ((K + bx - 1) / bx);
   const bool dq = sc.absmax == nullptr;
 #define QL_DX(BMV, BXV, LT, DQV, DRV)                                                            \
   hipLaunchKernelGGL((k_gemm_dx<BMV, BXV, AT, LT, DQV, DRV>), dim3((unsigned)G, (unsigned)S),   \

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 110
+    assert L.ql_abi_version() == 111
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -295,7 +295,7 @@ def test_dropout_entry_points_reject_bad_arguments():
     assert bwd(act=b.QL_F32) == b.QL_EUNSUPPORTED
     assert bwd(acc=2) == b.QL_EINVAL
     assert bwd(ws_bytes=1024) == b.QL_EWORKSPACE
-    # dx with dropout needs the matrix-core dx GEMM's shapes (N % 64, K % 128)
+    # dx with dropout needs the matrix-core dx GEMM's shapes (N % 8 == 0)
     assert bwd(desc=_desc(rows=100, cols=256)) == b.QL_EUNSUPPORTED
     assert L.ql_dropout_mask(0, 4, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
     assert L.ql_dropout_mask(4, -1, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL

@@ -79,6 +79,7 @@ DROP_CASES = [
     (512, 256, 640, 64, True, torch.float32, 0.05),   # r = 64, fp32 LoRA factors
     (77, 1024, 2048, 16, True, torch.bfloat16, 0.05), # split-K: fwd 4 slices, dx 2
     (130, 4096, 512, 16, True, torch.bfloat16, 0.2),  # split-K: dx 8 slices
+    (300, 200, 1088, 8, True, torch.bfloat16, 0.1),   # dx ragged in N and K
 ]
 
 

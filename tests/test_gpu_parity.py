@@ -263,7 +263,7 @@ BF16_CASES = [
     (5, 64, 14336, 64, True, torch.bfloat16),   # GEMV: 3.5 rounds, r = 64
     (17, 128, 128, 16, True, torch.bfloat16),   # smallest matrix-core GEMM
     (300, 384, 384, 16, True, torch.bfloat16),  # ragged M over two token tiles
-    (300, 200, 320, 8, False, torch.float32),   # ragged N: guarded fwd tile, tiled dx
+    (300, 200, 320, 8, False, torch.float32),   # ragged N: guarded fwd tile; dx ragged in N and K
     (512, 256, 640, 64, True, torch.bfloat16),  # r = 64
     (257, 128, 128, 128, True, torch.bfloat16), # r = 128
     (64, 64, 64, 5, True, torch.bfloat16),      # rank not a multiple of 8
@@ -273,6 +273,10 @@ BF16_CASES = [
     (200, 512, 4096, 8, True, torch.bfloat16),  # fwd 8 slices
     (130, 4096, 512, 16, True, torch.bfloat16), # dx 8 slices
     (7, 64, 512, 16, True, torch.bfloat16),     # GEMV: a round of 8 blocks
+    # matrix-core dx on ragged shapes (N % 64 != 0, K % 128 != 0)
+    (77, 200, 1088, 16, True, torch.bfloat16),  # 64-token dx tiles, last step and column tile ragged
+    (300, 456, 4416, 16, True, torch.bfloat16), # 256-token dx tiles, ragged N and K
+    (130, 2120, 576, 16, True, torch.bfloat16), # ragged dx with split-K
     (1, 200, 2048, 5, False, torch.bfloat16),   # GEMV: ragged N, rank 5, fp32 absmax
     # 64-token forward tiles (17..128 tokens)
     (100, 200, 320, 8, False, torch.float32),   # ragged M and N, fp32 absmax and factors
