@@ -264,12 +264,12 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
   hipStream_t s = (hipStream_t)stream;
   const float sc_lora = alpha / (float)r;
   const BlockScales sc = scales_of(W);
-  if (act_dtype != QL_F32 && !drop && gemv_fwd_preferred(M, N, K))
+  if (act_dtype != QL_F32 && gemv_fwd_preferred(M, N, K))
     return launch_gemv_fwd(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y,
-                           u_save, s, rows_partial);
-  if (act_dtype != QL_F32 && !drop && gemm_fwd_fused_preferred(M))
+                           u_save, s, rows_partial, drop, dscale);
+  if (act_dtype != QL_F32 && gemm_fwd_fused_preferred(M))
     return launch_gemm_fwd_fused(x, act_dtype, M, W->packed, sc, N, K, A, B, lora_dtype, r,
-                                 sc_lora, y, u_save, s, rows_partial);
+                                 sc_lora, y, u_save, s, rows_partial, drop, dscale);
   if (!drop && tiny_preferred(act_dtype, M, N, K, r))
     return launch_tiny_fwd(x, M, W->packed, sc, N, K, A, B, lora_dtype, r, sc_lora, y, u_save, s);
   st = launch_lora_rows_ws(x, act_dtype, M, K, A, lora_dtype, K, 1, r, drop ? dscale : 1.0f, u,

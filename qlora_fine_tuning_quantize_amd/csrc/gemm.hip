@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
     int64_t N, int64_t K, const float *__restrict__ u, const LT *__restrict__ B, int32_t r,
     float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit,
-    const LT *__restrict__ A, float *__restrict__ upart, int uc, int MT) {
+    const LT *__restrict__ A, float *__restrict__ upart, int uc, int MT, Dropout dr) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kSmBM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wp[2][kSmBN * 32];
   __shared__ float wsc[2][kSmBN];
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
       const int JT = (r + 15) / 16;
       const int b = (int)((int64_t)blockIdx.x - G);
       u_slice_tile<AT, LT>(x, (int)M, K, A, r, upart, uc, b / (JT * MT), (b / MT) % JT, b % MT,
-                           reinterpret_cast<float *>(&xs[0][0]));
+                           reinterpret_cast<float *>(&xs[0][0]), dr);
     }
     return;
   }
@@ -1046,7 +1046,7 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
 #define QL_FWS(LT, DQV)                                                                          \
   hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, false>), dim3((unsigned)G, (unsigned)S),    \
                      dim3(kSmThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, \
-                     y, part, S, (const LT *)nullptr, (float *)nullptr, 0, 0)
+                     y, part, S, (const LT *)nullptr, (float *)nullptr, 0, 0, Dropout{0u, 0u, 0u})
     with_half(act_dtype, [&](auto *tag) {
       using AT = elem_of<decltype(tag)>;
       if (lora_dtype == QL_F32) {
@@ -1099,8 +1099,9 @@ size_t gemm_fwd_fused_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r)
 int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
                           BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                           int lora_dtype, int32_t r, float s, void *y, float *u_save,
-                          hipStream_t stream, float *part) {
+                          hipStream_t stream, float *part, const Dropout *drop, float dscale) {
   const uint16_t *x = (const uint16_t *)xv;
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const bool dq = sc.absmax == nullptr;
   const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
   const int S = fwd_split(M, N, K);
@@ -1111,7 +1112,7 @@ int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_
 #define QL_FWF(LT, DQV)                                                                          \
   hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream,  \
                      x, M, packed, sc, N, K, (const float *)nullptr, (const LT *)B, r, s,         \
-                     (uint16_t *)nullptr, part, S, (const LT *)A, upart, us.uc, MT)
+                     (uint16_t *)nullptr, part, S, (const LT *)A, upart, us.uc, MT, dr)
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
     if (lora_dtype == QL_F32) {
@@ -1123,7 +1124,7 @@ int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_
 #undef QL_FWF
   QL_HIP_CHECK_LAUNCH();
   return launch_fwd_finish(act_dtype, lora_dtype, part, S, upart, us.U, M, N, r, B, s, y, u_save,
-                           stream);
+                           stream, drop ? dscale : 1.0f);
 }
 
 // 16-byte loads of dy rows and of 8-code words: N % 8 == 0 and K % 64 == 0

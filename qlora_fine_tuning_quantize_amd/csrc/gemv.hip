@@ -79,7 +79,7 @@ template <typename AT, typename LT, bool DQ, bool EV, bool VC>
 __global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ packed, BlockScales sc,
     int64_t N, int64_t K, const LT *__restrict__ A, int32_t r, float *__restrict__ part,
-    float *__restrict__ upart, int S, int U, int cpw, int uc) {
+    float *__restrict__ upart, int S, int U, int cpw, int uc, Dropout dr) {
   __shared__ uint32_t lut[256];
   __shared__ float red[kDecWaves][16][kDecRows];
   const int t = threadIdx.x;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
   const int JT = (r + 15) / 16;
   if ((int)blockIdx.x < U * JT) {
     u_slice_tile<AT, LT>(x, M, K, A, r, upart, uc, blockIdx.x / JT, blockIdx.x % JT, 0,
-                         &red[0][0][0]);
+                         &red[0][0][0], dr);
     return;
   }
 
@@ -276,8 +276,9 @@ __global__ __launch_bounds__(kDecThreads, 3) void k_dec_main(
 }
 
 // y[m][n] = RN(fmaf(s, sum_j u[m][j] B[n][j], sum over splits of x W^^T)),
-// u[m][j] = sum over the u slices in order (both sums start from 0 and add in
-// slice order; the rank sum is a chain of fmaf in rank order).  Grid
+// u[m][j] = uscale * (sum over the u slices in order) (both sums start from
+// 0 and add in slice order; the rank sum is a chain of fmaf in rank order;
+// uscale is 1, or 1 / (1 - p) under LoRA dropout).  Grid
 // (ceil(N / 256), M): one thread per output; the workgroups of the first
 // column store u_save.  Slices are read 8 at a time with all 8 loads in
 // flight (at clamped indices), so S slices cost ceil(S / 8) round trips.
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
                                                     int64_t N, int32_t r,
                                                     const LT *__restrict__ B, float s,
                                                     uint16_t *__restrict__ y,
-                                                    float *__restrict__ u_save) {
+                                                    float *__restrict__ u_save, float uscale) {
   __shared__ float us[128];
   const int t = threadIdx.x;
   const int mo = blockIdx.y;
@@ -351,6 +352,7 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
       for (int i = 0; i < 8; ++i)
         if (i0 + i < U) su += uv[i];
     }
+    su = uscale * su;
     us[t] = su;
     if (u_save && blockIdx.x == 0) u_save[(int64_t)mo * r + t] = su;
   }
@@ -379,16 +381,16 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float *__restrict__ pa
 
 int launch_fwd_finish(int act_dtype, int lora_dtype, const float *part, int S,
                       const float *upart, int U, int64_t M, int64_t N, int32_t r, const void *B,
-                      float s, void *y, float *u_save, hipStream_t stream) {
+                      float s, void *y, float *u_save, hipStream_t stream, float uscale) {
   const dim3 fgrid((unsigned)((N + 255) / 256), (unsigned)M);
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
     if (lora_dtype == QL_F32)
       hipLaunchKernelGGL((k_dec_finish<AT, float>), fgrid, dim3(256), 0, stream, part, S, upart,
-                         U, (int)M, N, r, (const float *)B, s, (uint16_t *)y, u_save);
+                         U, (int)M, N, r, (const float *)B, s, (uint16_t *)y, u_save, uscale);
     else
       hipLaunchKernelGGL((k_dec_finish<AT, AT>), fgrid, dim3(256), 0, stream, part, S, upart, U,
-                         (int)M, N, r, (const AT *)B, s, (uint16_t *)y, u_save);
+                         (int)M, N, r, (const AT *)B, s, (uint16_t *)y, u_save, uscale);
   });
   QL_HIP_CHECK_LAUNCH();
   return QL_OK;
@@ -464,7 +466,8 @@ size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r) {
 int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *yv, float *u_save,
-                    hipStream_t stream, float *part) {
+                    hipStream_t stream, float *part, const Dropout *drop, float dscale) {
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const uint16_t *x = (const uint16_t *)xv;
   uint16_t *y = (uint16_t *)yv;
   const bool dq = sc.absmax == nullptr;
@@ -479,7 +482,7 @@ int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
         hipLaunchKernelGGL((k_dec_main<AT, LT, decltype(dqt)::value, decltype(evt)::value,
                                        decltype(vct)::value>),
                            grid, dim3(kDecThreads), 0, stream, x, (int)M, packed, sc, N, K,
-                           (const LT *)A, r, part, upart, p.S, p.U, p.cpw, p.uc);
+                           (const LT *)A, r, part, upart, p.S, p.U, p.cpw, p.uc, dr);
       };
       using T = std::true_type;
       using F = std::false_type;
@@ -495,7 +498,7 @@ int launch_gemv_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
   });
   QL_HIP_CHECK_LAUNCH();
   return launch_fwd_finish(act_dtype, lora_dtype, part, p.S, upart, p.U, M, N, r, B, s, y, u_save,
-                           stream);
+                           stream, drop ? dscale : 1.0f);
 }
 
 }  // namespace qlora

@@ -74,14 +74,17 @@ int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *pa
 // that sums them.
 size_t gemv_fwd_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r);
 // y[m][n] = RN(fmaf(s, sum_j u_j B_nj, sum of S slices of part [S][M][N])),
-// u = sum of U slices of upart [U][M][r] (stored to u_save when non-null).
+// u = uscale * (sum of U slices of upart [U][M][r]) (stored to u_save when
+// non-null; uscale = 1 / (1 - p) under LoRA dropout, else 1).
 int launch_fwd_finish(int act_dtype, int lora_dtype, const float *part, int S,
                       const float *upart, int U, int64_t M, int64_t N, int32_t r, const void *B,
-                      float s, void *y, float *u_save, hipStream_t stream);
+                      float s, void *y, float *u_save, hipStream_t stream, float uscale = 1.0f);
+// drop: LoRA dropout of the bypass input (NULL for none), dscale = 1 / (1 - p).
 int launch_gemv_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                     int lora_dtype, int32_t r, float s, void *y, float *u_save,
-                    hipStream_t stream, float *part);
+                    hipStream_t stream, float *part, const Dropout *drop = nullptr,
+                    float dscale = 1.0f);
 
 // gemm.hip: matrix-core forward and input-gradient products for 16-bit
 // activations (act_dtype QL_BF16 or QL_F16; a 16-bit lora_dtype equals it).
@@ -98,15 +101,17 @@ int launch_tiny_bwd(const void *dy, const void *x, int64_t M, const uint8_t *pac
                     int lora_dtype, int32_t r, float s, const float *u_saved, void *dx, float *dA,
                     float *dB, bool accumulate, hipStream_t stream);
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
-// Few-token forward (17..64 tokens, 16-bit activations, no dropout) in two
-// launches: the 64-token GEMM tiles plus u slice workgroups, then the slice
-// sum with the bypass (part: gemm_fwd_fused_partial_floats floats).
+// Few-token forward (17..64 tokens, 16-bit activations) in two launches: the
+// 64-token GEMM tiles plus u slice workgroups, then the slice sum with the
+// bypass (part: gemm_fwd_fused_partial_floats floats); drop as for the
+// decode forward.
 bool gemm_fwd_fused_preferred(int64_t M);
 size_t gemm_fwd_fused_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r);
 int launch_gemm_fwd_fused(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                           BlockScales sc, int64_t N, int64_t K, const void *A, const void *B,
                           int lora_dtype, int32_t r, float s, void *y, float *u_save,
-                          hipStream_t stream, float *part);
+                          hipStream_t stream, float *part, const Dropout *drop = nullptr,
+                          float dscale = 1.0f);
 size_t gemm_dx_partial_floats(int64_t M, int64_t N, int64_t K);
 int launch_gemm_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *packed,
                     BlockScales sc, int64_t N, int64_t K, const float *u, const void *B,

@@ -27,12 +27,14 @@ __device__ __forceinline__ u32x4 lora_op8(const LT *p) {
 // over the contraction chunks [su uc, su uc + uc), summed over the
 // workgroup's 4 waves: upart[su][m][16 jt + j].  256 threads; red: 4 x 16 x
 // 16 floats of LDS.  K % 32 == 0.  Rows past M and ranks past r repeat the
-// last valid one and are not stored.
+// last valid one and are not stored.  With LoRA dropout (dr.thr != 0) the
+// dropped elements of x are zeroed as loaded; the 1 / (1 - p) scale is left
+// to the launch that sums the slices.
 template <typename AT, typename LT>
 __device__ __forceinline__ void u_slice_tile(const uint16_t *__restrict__ x, int M, int64_t K,
                                              const LT *__restrict__ A, int32_t r,
                                              float *__restrict__ upart, int uc, int su, int jt,
-                                             int tg, float *red) {
+                                             int tg, float *red, Dropout dr) {
   constexpr int kWaves = 4;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
@@ -54,6 +56,13 @@ __device__ __forceinline__ void u_slice_tile(const uint16_t *__restrict__ x, int
       const int st = s0 + kWaves * i < nsteps ? s0 + kWaves * i : s0;
       xo[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * st);
       ao[i] = lora_op8<AT>(ap + 32 * st);
+    }
+    if (dr.thr != 0u) {  // uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int st = s0 + kWaves * i < nsteps ? s0 + kWaves * i : s0;
+        xo[i] = dropout_mask8(dr, (uint64_t)m * K + col0 + 8 * q + 32 * st, xo[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)

@@ -71,7 +71,9 @@ def _drop_case(orc, M, N, K, r, dq, lora, p, seed, alpha=32.0, rows=None, cfg=95
 
 DROP_CASES = [
     # M, N, K, r, dq, lora dtype, p      (path exercised)
-    (3, 256, 256, 8, True, torch.bfloat16, 0.05),     # few tokens: GEMM, not the decode kernel
+    (3, 256, 256, 8, True, torch.bfloat16, 0.05),     # decode forward (u slices masked)
+    (16, 384, 4096, 16, True, torch.bfloat16, 0.1),   # decode forward, split contraction
+    (40, 256, 512, 8, True, torch.bfloat16, 0.05),    # few-token forward (u slices in its launch)
     (17, 128, 128, 16, True, torch.bfloat16, 0.1),    # smallest matrix-core GEMM
     (300, 384, 384, 16, True, torch.bfloat16, 0.05),  # ragged M over two token tiles
     (257, 128, 128, 128, True, torch.bfloat16, 0.3),  # r = 128 (8 rank chunks in dx)
@@ -90,7 +92,8 @@ def test_layer_dropout_parity(orc, M, N, K, r, dq, lora, p):
 
 
 @pytest.mark.parametrize("M,N,K,r,dq,lora,p", [
-    (3, 256, 256, 8, True, torch.float16, 0.05),      # few tokens: GEMM
+    (3, 256, 256, 8, True, torch.float16, 0.05),      # decode forward
+    (40, 256, 512, 8, True, torch.float16, 0.05),     # few-token forward
     (300, 384, 384, 16, True, torch.float16, 0.05),   # 256-token tiles, ragged M
     (64, 64, 128, 5, False, torch.float32, 0.5),      # 64-token tiles, fp32 factors
     (130, 4096, 512, 16, True, torch.float16, 0.2),   # split-K dx

@@ -22,6 +22,8 @@ DEV = torch.device("cuda:0")
     (300, 384, 640, 16, 0.1, 64, torch.float16),    # fp16 compute with dropout
     (8, 256, 512, 8, 0.0, 64, torch.float16),       # fp16 decode GEMV
     (4, 256, 8192, 16, 0.0, 64, torch.bfloat16),    # decode GEMV, contraction split in 2
+    (8, 256, 512, 8, 0.1, 64, torch.bfloat16),      # decode forward with LoRA dropout
+    (40, 256, 1024, 16, 0.1, 64, torch.bfloat16),   # few-token forward with LoRA dropout
 ])
 def test_graph_replay_matches_eager(M, N, K, r, dropout, block, act):
     print(f"graph replay M={M} N={N} K={K} r={r} dropout={dropout} block={block} act={act}",
