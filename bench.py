@@ -24,7 +24,8 @@ In the same run (reported beside the step):
                p10/p90; the oracle's GEMV on the host beside it; decode-sized
                calls on larger weights
   quantize     NF4 + double quantisation and full dequantisation of an
-               8B-shaped weight set, GB/s and bits/param; the oracle's
+               8B-shaped weight set, GB/s and bits/param (quantised one layer
+               per call, and one weight per call); the oracle's
                quantise + dequantise of layers 0 and 31 on the host beside it
   small_fp32   the fp32 256x256 layer (4 tokens, r=8) forward + backward,
                1000 calls, and the single-thread oracle beside it
@@ -704,11 +705,19 @@ def bench_quantize(q, si, dev, with_cpu=True):
             n_total += w.numel()
     maxn = max(w.numel() for w in ws_list)
     wsq = q.workspace(q.QL_OP_QUANTIZE, 0, 1, maxn, 0, dev)
+    per_layer = len(cfg["shapes"])
+    wsm = torch.empty(q.quantize_many_workspace_bytes([w.shape for w in ws_list[:per_layer]]),
+                      dtype=torch.uint8, device=dev)
     deq = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log(f"weight set ready: {n_total} params")
 
-    def quant_all():
+    def quant_all():  # one nf4_quantize_many call per layer (its 7 weights)
+        for i in range(0, len(ws_list), per_layer):
+            q.nf4_quantize_many(ws_list[i:i + per_layer], double_quant=True,
+                                out=q_list[i:i + per_layer], ws=wsm)
+
+    def quant_each():  # one nf4_quantize call per weight
         for w, qq in zip(ws_list, q_list):
             q.nf4_quantize(w, double_quant=True, out=qq, ws=wsq)
 
@@ -717,11 +726,12 @@ def bench_quantize(q, si, dev, with_cpu=True):
             q.nf4_dequantize(qq, out=deq[:qq.rows * qq.cols].view(qq.rows, qq.cols))
 
     qms_eager = timed(quant_all, 3, 1)
+    q1ms_eager = timed(quant_each, 3, 1)
     dms_eager = timed(dequant_all, 3, 1)
     # the same passes replayed from HIP graphs (no per-call host work: 224
     # launches of a few microseconds each would otherwise be host-bound)
     graphs = []
-    for fn in (quant_all, dequant_all):
+    for fn in (quant_all, dequant_all, quant_each):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -734,6 +744,7 @@ def bench_quantize(q, si, dev, with_cpu=True):
         graphs.append(g)
     qms = timed(graphs[0].replay, 5, 1)
     dms = timed(graphs[1].replay, 5, 1)
+    q1ms = timed(graphs[2].replay, 5, 1)
     del graphs
     stored = sum(qq.storage_bytes() for qq in q_list)
     q_bytes = 2 * n_total + stored
@@ -744,11 +755,17 @@ def bench_quantize(q, si, dev, with_cpu=True):
            "quantize_ms": round(qms, 3), "quantize_GBps": round(q_bytes / (qms * 1e-3) / 1e9, 1),
            "dequantize_ms": round(dms, 3),
            "dequantize_GBps": round(d_bytes / (dms * 1e-3) / 1e9, 1), "unit": "GB/s",
-           "launch": "HIP graph replay of each pass (224 calls)",
-           "quantize_ms_eager": round(qms_eager, 3), "dequantize_ms_eager": round(dms_eager, 3)}
+           "launch": "HIP graph replay of each pass: quantise as 32 nf4_quantize_many calls "
+                     "(one per layer, 64 launches), dequantise as 224 calls",
+           "quantize_per_tensor_ms": round(q1ms, 3),
+           "quantize_per_tensor_GBps": round(q_bytes / (q1ms * 1e-3) / 1e9, 1),
+           "quantize_ms_eager": round(qms_eager, 3),
+           "quantize_per_tensor_ms_eager": round(q1ms_eager, 3),
+           "dequantize_ms_eager": round(dms_eager, 3)}
     out["quantize_hbm_frac"] = round(out["quantize_GBps"] / PEAK_HBM_GBS, 4)
     out["dequantize_hbm_frac"] = round(out["dequantize_GBps"] / PEAK_HBM_GBS, 4)
-    log(f"quantize {qms:.2f} ms ({out['quantize_GBps']} GB/s), dequantize {dms:.2f} ms "
+    log(f"quantize {qms:.2f} ms ({out['quantize_GBps']} GB/s; one call per weight {q1ms:.2f} ms, "
+        f"{out['quantize_per_tensor_GBps']} GB/s), dequantize {dms:.2f} ms "
         f"({out['dequantize_GBps']} GB/s) in graphs; eager {qms_eager:.2f} / {dms_eager:.2f} ms; "
         f"{out['bits_per_param']} bits/param")
     del ws_list, q_list, deq

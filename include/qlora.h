@@ -159,6 +159,31 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
                  void *stream);
 
 /*
+ * NF4-quantise `count` weights at once (a model's tensors when it is loaded;
+ * Gemma lesson 09, sec. 9.2.1 and 9.2.2): the outputs of weight i are those
+ * of nf4_quantize(w[i], w_dtype, &q[i], ...), bit for bit, but up to eight
+ * weights share one launch (two with double quantisation), so small weights
+ * do not each pay a launch.
+ *   count     number of weights (0: nothing to do).
+ *   w         host array of count device pointers, each q[i].rows *
+ *             q[i].cols elements of w_dtype, 16-byte aligned.
+ *   q         host array of count structs as for nf4_quantize; all share
+ *             block and double_quant.  Outputs of different weights must not
+ *             overlap.
+ *   ws, ws_bytes  device workspace, 256-byte aligned, of at least the sum
+ *             over i of ql_workspace_bytes(QL_OP_QUANTIZE, 0, q[i].rows,
+ *             q[i].cols, 0) bytes, weight i using the part after those of
+ *             weights 0 .. i-1 (may be NULL/0 without double quant).
+ * Every argument is checked before anything is enqueued: on an error no
+ * weight has been touched.
+ * Errors: QL_EINVAL (count < 0, a NULL array or pointer, mixed block or
+ * double_quant, or an invalid struct), QL_EALIGN, QL_EUNSUPPORTED,
+ * QL_EWORKSPACE, QL_EHIP.
+ */
+int nf4_quantize_many(int32_t count, const void *const *w, int32_t w_dtype, const ql_nf4 *q,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Dequantise a whole NF4 weight to out (device, rows * cols elements of
  * out_dtype: fp32, or bf16 / fp16 as the round-to-nearest-even of the fp32
  * product)
@@ -357,7 +382,8 @@ const char *ql_strerror(int status);
  *        workspaces on large shapes.
  *   111: the matrix-core input gradient takes N % 8 == 0 and any K of the
  *        layer (before: N % 64 == 0, K % 128 == 0), so more backward
- *        workspaces hold its split-K partials. */
+ *        workspaces hold its split-K partials.
+ *   112: nf4_quantize_many (several weights per launch). */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

@@ -22,7 +22,8 @@ QL_OP_QUANTIZE, QL_OP_FWD, QL_OP_BWD = 0, 1, 2
 NF4_BLOCK, NF4_BLOCK_LARGE, DQ_BLOCK = 64, 128, 256
 
 # every extern "C" symbol declared in include/qlora.h
-EXPORTED = ("ql_nf4_sizes", "ql_nf4_sizes_block", "ql_workspace_bytes", "nf4_quantize", "nf4_dequantize",
+EXPORTED = ("ql_nf4_sizes", "ql_nf4_sizes_block", "ql_workspace_bytes", "nf4_quantize",
+            "nf4_quantize_many", "nf4_dequantize",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_fwd_u", "qlora_linear_bwd",
             "qlora_linear_bwd_acc",
             "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "ql_dropout_mask",
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.ql_workspace_bytes.restype = sz
     L.nf4_quantize.argtypes = [p, i32, sp, p, sz, p]
     L.nf4_quantize.restype = ctypes.c_int
+    L.nf4_quantize_many.argtypes = [i32, ctypes.POINTER(p), i32, sp, p, sz, p]
+    L.nf4_quantize_many.restype = ctypes.c_int
     L.nf4_dequantize.argtypes = [sp, p, i32, p]
     L.nf4_dequantize.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [p, i32, i64, sp, p, p, i32, i32, f32, p, p, p, sz, p]
@@ -204,6 +207,34 @@ def nf4_quantize(w: torch.Tensor, double_quant: bool = True, out: NF4Weight | No
                               0 if ws is None else ws.numel(), _stream(w.device)),
            "nf4_quantize")
     return q
+
+
+def quantize_many_workspace_bytes(shapes) -> int:
+    """Workspace of nf4_quantize_many with double quantisation: the sum of
+    the per-weight quantisation workspaces, in order."""
+    return sum(workspace_bytes(QL_OP_QUANTIZE, 0, N, K, 0) for N, K in shapes)
+
+
+def nf4_quantize_many(ws_in: list, double_quant: bool = True, out: list | None = None,
+                      ws: torch.Tensor | None = None, block: int = NF4_BLOCK) -> list:
+    """NF4-quantise several 2-D weights of one dtype (on one GPU) in as few
+    launches as the library can; each result equals nf4_quantize's."""
+    n = len(ws_in)
+    for w in ws_in:
+        assert w.dim() == 2 and w.is_contiguous() and w.is_cuda and w.dtype == ws_in[0].dtype
+    dev = ws_in[0].device if n else torch.device("cuda")
+    outs = out or [NF4Weight.empty(w.shape[0], w.shape[1], double_quant, w.device, block)
+                   for w in ws_in]
+    assert len(outs) == n
+    if ws is None and double_quant and n:
+        ws = torch.empty(max(256, quantize_many_workspace_bytes([w.shape for w in ws_in])),
+                         dtype=torch.uint8, device=dev)
+    structs = (QlNf4 * max(n, 1))(*[q.struct() for q in outs])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[w.data_ptr() for w in ws_in])
+    _check(lib().nf4_quantize_many(n, ptrs, _dtype_code(ws_in[0].dtype) if n else QL_BF16,
+                                   structs, _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(dev)), "nf4_quantize_many")
+    return outs
 
 
 def nf4_dequantize(q: NF4Weight, dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kernels.h"
@@ -161,7 +162,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 111; }
+int ql_abi_version(void) { return 112; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -232,6 +233,67 @@ int nf4_quantize(const void *w, int32_t w_dtype, const ql_nf4 *q, void *ws, size
   unsigned long long *partial = (unsigned long long *)(base + L.partial);
   return launch_nf4_quantize_dq(w, w_dtype, n, q->block, q->packed, absmax, partial, q->absmax_q,
                                 q->absmax_scale, q->absmax_mean, s);
+}
+
+int nf4_quantize_many(int32_t count, const void *const *w, int32_t w_dtype, const ql_nf4 *q,
+                      void *ws, size_t ws_bytes, void *stream) {
+  if (count < 0) return QL_EINVAL;
+  if (count == 0) return QL_OK;
+  if (!w || !q || check_dtype(w_dtype)) return QL_EINVAL;
+  // every check before the first launch: an error enqueues nothing
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    const int st = check_nf4(&q[i]);
+    if (st) return st;
+    if (q[i].block != q[0].block || q[i].double_quant != q[0].double_quant) return QL_EINVAL;
+    if (!w[i]) return QL_EINVAL;
+    if (!aligned16(w[i])) return QL_EALIGN;
+    if (q[i].double_quant) {
+      const int64_t n = q[i].rows * q[i].cols;
+      if ((n + q[i].block - 1) / q[i].block >= (int64_t(1) << 31)) return QL_EUNSUPPORTED;
+      need += quant_ws(n).total;
+    }
+  }
+  const bool dq = q[0].double_quant != 0;
+  if (dq) {
+    if (!ws || ws_bytes < need) return QL_EWORKSPACE;
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return QL_EALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *base = (uint8_t *)ws;
+  for (int i0 = 0; i0 < count; i0 += kQmMax) {
+    const int c = std::min(kQmMax, count - i0);
+    const void *wv[kQmMax];
+    int64_t nv[kQmMax];
+    uint8_t *pk[kQmMax];
+    float *am[kQmMax], *sg[kQmMax], *mu[kQmMax];
+    unsigned long long *pt[kQmMax];
+    int8_t *qc[kQmMax];
+    for (int j = 0; j < c; ++j) {
+      const ql_nf4 &Q = q[i0 + j];
+      wv[j] = w[i0 + j];
+      nv[j] = Q.rows * Q.cols;
+      pk[j] = Q.packed;
+      if (dq) {  // this weight's part of the workspace: constants, then partial sums
+        const QuantWs L = quant_ws(nv[j]);
+        am[j] = (float *)(base + L.absmax);
+        pt[j] = (unsigned long long *)(base + L.partial);
+        base += L.total;
+        qc[j] = Q.absmax_q;
+        sg[j] = Q.absmax_scale;
+        mu[j] = Q.absmax_mean;
+      } else {
+        am[j] = Q.absmax;
+        pt[j] = nullptr;
+        qc[j] = nullptr;
+        sg[j] = mu[j] = nullptr;
+      }
+    }
+    const int st = launch_nf4_quantize_many(c, wv, w_dtype, nv, q[0].block, dq, pk, am, pt, qc, sg,
+                                            mu, s);
+    if (st) return st;
+  }
+  return QL_OK;
 }
 
 int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) {

@@ -21,6 +21,15 @@ constexpr int kQdInfDigit = 10;
 int launch_nf4_quantize_dq(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
                            float *absmax, unsigned long long *partial, int8_t *q, float *sigma,
                            float *mean_out, hipStream_t stream);
+// Up to kQmMax weights of one dtype, block size and form in one launch (plus
+// one codes launch for the double-quantised form); each weight's outputs
+// are those of its own launch above.  partial, q, sigma and mean are read
+// only when dq.
+constexpr int kQmMax = 8;
+int launch_nf4_quantize_many(int count, const void *const *w, int w_dtype, const int64_t *n,
+                             int block, bool dq, uint8_t *const *packed, float *const *absmax,
+                             unsigned long long *const *partial, int8_t *const *q,
+                             float *const *sigma, float *const *mean, hipStream_t stream);
 int launch_nf4_dequantize(const uint8_t *packed, int64_t n, BlockScales sc, void *out,
                           int out_dtype, hipStream_t stream);
 

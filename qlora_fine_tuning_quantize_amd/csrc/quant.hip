@@ -222,15 +222,15 @@ __device__ __forceinline__ float quant_run(const T *__restrict__ w, int64_t n, i
   return m;
 }
 
-// Single-level form: a wave owns 2 runs; all loads are issued first.
+// Single-level form, one workgroup of 256 threads (number wg of its weight):
+// a wave owns 2 runs; all loads are issued first.
 template <typename T, int BLK>
-__global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, int64_t n,
-                                                      uint8_t *__restrict__ packed,
-                                                      float *__restrict__ absmax,
-                                                      NF4Thresholds th) {
-  __shared__ BucketEntry tab[kBuckets];
+__device__ __forceinline__ void quantize_wg(const T *__restrict__ w, int64_t n,
+                                            uint8_t *__restrict__ packed,
+                                            float *__restrict__ absmax, const NF4Thresholds &th,
+                                            BucketEntry *tab, int64_t wg) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t wave = wg * 4 + (threadIdx.x >> 6);
   constexpr int R = 2;
   RunRaw<T> raw[R];
 #pragma unroll
@@ -243,6 +243,15 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, i
     widen_run(raw[j], v);
     quant_run<T, BLK>(w, n, wave * (R * 512) + j * 512 + lane * 8, v, tab, lane, packed, absmax);
   }
+}
+
+template <typename T, int BLK>
+__global__ __launch_bounds__(256) void k_nf4_quantize(const T *__restrict__ w, int64_t n,
+                                                      uint8_t *__restrict__ packed,
+                                                      float *__restrict__ absmax,
+                                                      NF4Thresholds th) {
+  __shared__ BucketEntry tab[kBuckets];
+  quantize_wg<T, BLK>(w, n, packed, absmax, th, tab, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -308,21 +317,21 @@ __device__ __forceinline__ void lane_add(LaneSum &S, float m, unsigned long long
   S.acc += M << k;
 }
 
+// One workgroup (number wg of `groups` on this weight; tab and dig in LDS).
 template <typename T, int BLK>
-__global__ __launch_bounds__(kQdThreads, 8) void k_nf4_quantize_dq(const T *__restrict__ w, int64_t n,
-                                                                uint8_t *__restrict__ packed,
-                                                                float *__restrict__ absmax,
-                                                                NF4Thresholds th,
-                                                                unsigned long long *__restrict__ partial) {
-  __shared__ BucketEntry tab[kBuckets];
-  __shared__ unsigned long long dig[kQdDigits];
+__device__ __forceinline__ void quantize_dq_wg(const T *__restrict__ w, int64_t n,
+                                               uint8_t *__restrict__ packed,
+                                               float *__restrict__ absmax, const NF4Thresholds &th,
+                                               unsigned long long *__restrict__ partial,
+                                               BucketEntry *tab, unsigned long long *dig, int wg,
+                                               int groups) {
   const int lane = threadIdx.x & 63;
   constexpr int WPG = kQdThreads / 64;
   constexpr int R = kQdRuns;
-  const int64_t step = (int64_t)gridDim.x * WPG;
+  const int64_t step = (int64_t)groups * WPG;
   const int64_t full = n / (R * 512);  // steps wholly inside the weight
   // the wave's step index, wave-uniform (scalar) for the address math
-  int64_t c = (int64_t)blockIdx.x * WPG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t c = (int64_t)wg * WPG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   build_buckets(tab, th, threadIdx.x);
   if (threadIdx.x < kQdDigits) dig[threadIdx.x] = 0;
   __syncthreads();
@@ -360,9 +369,21 @@ __global__ __launch_bounds__(kQdThreads, 8) void k_nf4_quantize_dq(const T *__re
   }
   if (lsum.acc) add_shifted(dig, lsum.acc, lsum.base);
   __syncthreads();
-  // digit-major: partial[d * gridDim.x + workgroup]
-  if (threadIdx.x < kQdDigits) partial[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = dig[threadIdx.x];
+  // digit-major: partial[d * groups + wg]
+  if (threadIdx.x < kQdDigits) partial[(int64_t)threadIdx.x * groups + wg] = dig[threadIdx.x];
 }
+
+template <typename T, int BLK>
+__global__ __launch_bounds__(kQdThreads, 8) void k_nf4_quantize_dq(const T *__restrict__ w, int64_t n,
+                                                                uint8_t *__restrict__ packed,
+                                                                float *__restrict__ absmax,
+                                                                NF4Thresholds th,
+                                                                unsigned long long *__restrict__ partial) {
+  __shared__ BucketEntry tab[kBuckets];
+  __shared__ unsigned long long dig[kQdDigits];
+  quantize_dq_wg<T, BLK>(w, n, packed, absmax, th, partial, tab, dig, blockIdx.x, gridDim.x);
+}
+
 
 // ---------------------------------------------------------------------------
 // Double-quantised form, pass 2: every workgroup (16 waves) first adds the
@@ -442,18 +463,18 @@ constexpr int kDcThreads = 1024;
 static_assert(kDcThreads / 64 >= kQdDigits, "one wave per digit counter");
 static_assert(kQdMaxGroups % 64 == 0, "whole partials per lane");
 
-__global__ __launch_bounds__(kDcThreads) void k_dq_codes(const float *__restrict__ a, int64_t nb,
-                                                         const unsigned long long *__restrict__ partial,
-                                                         int n_partial, int8_t *__restrict__ q,
-                                                         float *__restrict__ sigma,
-                                                         float *__restrict__ mean_out) {
+// One workgroup (number wg of `groups` on this weight; tot and s_mu in LDS).
+__device__ __forceinline__ void dq_codes_wg(const float *__restrict__ a, int64_t nb,
+                                            const unsigned long long *__restrict__ partial,
+                                            int n_partial, int8_t *__restrict__ q,
+                                            float *__restrict__ sigma, float *__restrict__ mean_out,
+                                            unsigned long long *tot, float *s_mu, int wg,
+                                            int groups) {
   constexpr int WPG = kDcThreads / 64;
-  __shared__ unsigned long long tot[kQdDigits];
-  __shared__ float s_mu;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb2 = (nb + 255) / 256;
-  const int64_t step = (int64_t)gridDim.x * WPG;
-  int64_t b2 = (int64_t)blockIdx.x * WPG + wave;
+  const int64_t step = (int64_t)groups * WPG;
+  int64_t b2 = (int64_t)wg * WPG + wave;
   auto load4 = [&](int64_t blk, float (&av)[4]) {
     const int64_t j0 = blk * 256 + 4 * lane;
     if (j0 + 4 <= nb) {
@@ -486,11 +507,11 @@ __global__ __launch_bounds__(kDcThreads) void k_dq_codes(const float *__restrict
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    s_mu = exact_mean(tot, nb);
-    if (blockIdx.x == 0) mean_out[0] = s_mu;
+    *s_mu = exact_mean(tot, nb);
+    if (wg == 0) mean_out[0] = *s_mu;
   }
   __syncthreads();
-  const float mu = s_mu;
+  const float mu = *s_mu;
 
   for (; b2 < nb2; b2 += step) {
     const int64_t j0 = b2 * 256 + 4 * lane;
@@ -522,6 +543,88 @@ __global__ __launch_bounds__(kDcThreads) void k_dq_codes(const float *__restrict
     }
     if (lane == 0) sigma[b2] = sg;
   }
+}
+
+__global__ __launch_bounds__(kDcThreads) void k_dq_codes(const float *__restrict__ a, int64_t nb,
+                                                         const unsigned long long *__restrict__ partial,
+                                                         int n_partial, int8_t *__restrict__ q,
+                                                         float *__restrict__ sigma,
+                                                         float *__restrict__ mean_out) {
+  __shared__ unsigned long long tot[kQdDigits];
+  __shared__ float s_mu;
+  dq_codes_wg(a, nb, partial, n_partial, q, sigma, mean_out, tot, &s_mu, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Several weights per launch (a model's tensors quantised together when it
+// is loaded).  Workgroups [f[t], f[t + 1]) run weight t exactly as its own
+// launch would (the same workgroup count, numbering and partial layout), so
+// the results are those of one launch per weight; small weights no longer
+// pay a launch each, and their workgroups fill the chip beside the large
+// ones.  At most kQmMax weights per launch.
+// ---------------------------------------------------------------------------
+struct QuantBatch {
+  const void *w[kQmMax];
+  int64_t n[kQmMax];
+  uint8_t *packed[kQmMax];
+  float *absmax[kQmMax];
+  unsigned long long *partial[kQmMax];
+  int8_t *q[kQmMax];
+  float *sigma[kQmMax];
+  float *mean[kQmMax];
+  int g0[kQmMax + 1];  // first workgroup of each weight, quantisation launch
+  int h0[kQmMax + 1];  // first workgroup of each weight, codes launch
+  int count;
+};
+
+// Entry t of a kernel-argument array for a workgroup-uniform t: selects over
+// constant indices, so the array stays in scalar registers and is never
+// indexed in memory.
+template <typename P, int N>
+__device__ __forceinline__ P pick(const P (&a)[N], int t) {
+  P r = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = i == t ? a[i] : r;
+  return r;
+}
+
+// The weight that workgroup wg works on, from the first-workgroup offsets f.
+__device__ __forceinline__ int batch_member(const int (&f)[kQmMax + 1], int count, int wg) {
+  int t = 0;
+#pragma unroll
+  for (int i = 1; i < kQmMax; ++i) t += (i < count && wg >= f[i]) ? 1 : 0;
+  return t;
+}
+
+template <typename T, int BLK>
+__global__ __launch_bounds__(256) void k_nf4_quantize_many(QuantBatch b, NF4Thresholds th) {
+  __shared__ BucketEntry tab[kBuckets];
+  const int t = batch_member(b.g0, b.count, blockIdx.x);
+  quantize_wg<T, BLK>((const T *)pick(b.w, t), pick(b.n, t), pick(b.packed, t),
+                      pick(b.absmax, t), th, tab, (int64_t)blockIdx.x - pick(b.g0, t));
+}
+
+template <typename T, int BLK>
+__global__ __launch_bounds__(kQdThreads, 8) void k_nf4_quantize_dq_many(QuantBatch b,
+                                                                     NF4Thresholds th) {
+  __shared__ BucketEntry tab[kBuckets];
+  __shared__ unsigned long long dig[kQdDigits];
+  const int t = batch_member(b.g0, b.count, blockIdx.x);
+  const int f = pick(b.g0, t);
+  quantize_dq_wg<T, BLK>((const T *)pick(b.w, t), pick(b.n, t), pick(b.packed, t),
+                         pick(b.absmax, t), th, pick(b.partial, t), tab, dig,
+                         (int)blockIdx.x - f, pick(b.g0, t + 1) - f);
+}
+
+__global__ __launch_bounds__(kDcThreads) void k_dq_codes_many(QuantBatch b, int block) {
+  __shared__ unsigned long long tot[kQdDigits];
+  __shared__ float s_mu;
+  const int t = batch_member(b.h0, b.count, blockIdx.x);
+  const int f = pick(b.h0, t);
+  const int64_t nb = (pick(b.n, t) + block - 1) / block;
+  dq_codes_wg(pick(b.absmax, t), nb, pick(b.partial, t), pick(b.g0, t + 1) - pick(b.g0, t),
+              pick(b.q, t), pick(b.sigma, t), pick(b.mean, t), tot, &s_mu, (int)blockIdx.x - f,
+              pick(b.h0, t + 1) - f);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,12 +695,25 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t *__restric
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Workgroups of one weight's launch: single-level quantisation (one wave per
+// 1024 elements, 4 waves per workgroup), the double-quantised form (a
+// grid-stride loop over steps of 16 waves x 1024 elements, at most
+// kQdMaxGroups workgroups) and its codes (16 DQ blocks per workgroup and
+// step, at most 256 workgroups).
+static int64_t quant_groups(int64_t n) { return ((n + 1023) / 1024 + 3) / 4; }
+static int quant_dq_groups(int64_t n) {
+  const int64_t chunks = (n + kQdRuns * 512 - 1) / (kQdRuns * 512);
+  return (int)std::min<int64_t>(kQdMaxGroups, (chunks + kQdThreads / 64 - 1) / (kQdThreads / 64));
+}
+static int dq_code_groups(int64_t nb) {
+  const int64_t nb2 = (nb + 255) / 256;
+  return (int)std::min<int64_t>(256, (nb2 + 15) / 16);
+}
+
 int launch_nf4_quantize(const void *w, int w_dtype, int64_t n, int block, uint8_t *packed,
                         float *absmax, hipStream_t stream) {
   if (n <= 0) return QL_OK;
-  // one wave per 1024 elements (2 runs of 512)
-  const int64_t waves = (n + 1023) / 1024;
-  const dim3 grid((unsigned)((waves + 3) / 4));
+  const dim3 grid((unsigned)quant_groups(n));
   const NF4Thresholds th = nf4_thresholds();
 #define QL_QUANT(T, BLKV)                                                                        \
   hipLaunchKernelGGL((k_nf4_quantize<T, BLKV>), grid, dim3(256), 0, stream, (const T *)w, n,      \
@@ -620,8 +736,7 @@ int launch_nf4_quantize_dq(const void *w, int w_dtype, int64_t n, int block, uin
   if (n <= 0) return QL_OK;
   const int64_t nb = (n + block - 1) / block;
   if (nb >= (int64_t(1) << 31)) return QL_EUNSUPPORTED;  // keeps the 64-bit digit sums exact
-  const int64_t chunks = (n + kQdRuns * 512 - 1) / (kQdRuns * 512);
-  const int groups = (int)std::min<int64_t>(kQdMaxGroups, (chunks + kQdThreads / 64 - 1) / (kQdThreads / 64));
+  const int groups = quant_dq_groups(n);
   const NF4Thresholds th = nf4_thresholds();
 #define QL_QUANT(T, BLKV)                                                                        \
   hipLaunchKernelGGL((k_nf4_quantize_dq<T, BLKV>), dim3(groups), dim3(kQdThreads), 0, stream,     \
@@ -635,11 +750,71 @@ int launch_nf4_quantize_dq(const void *w, int w_dtype, int64_t n, int block, uin
   }
 #undef QL_QUANT
   QL_HIP_CHECK_LAUNCH();
-  const int64_t nb2 = (nb + 255) / 256;  // DQ blocks, one wave each per step
-  const int g2 = (int)std::min<int64_t>(256, (nb2 + 15) / 16);
-  hipLaunchKernelGGL(k_dq_codes, dim3(g2), dim3(kDcThreads), 0, stream, absmax, nb, partial, groups,
-                     q, sigma, mean_out);
+  hipLaunchKernelGGL(k_dq_codes, dim3(dq_code_groups(nb)), dim3(kDcThreads), 0, stream, absmax, nb,
+                     partial, groups, q, sigma, mean_out);
   QL_HIP_CHECK_LAUNCH();
+  return QL_OK;
+}
+
+int launch_nf4_quantize_many(int count, const void *const *w, int w_dtype, const int64_t *n,
+                             int block, bool dq, uint8_t *const *packed, float *const *absmax,
+                             unsigned long long *const *partial, int8_t *const *q,
+                             float *const *sigma, float *const *mean, hipStream_t stream) {
+  if (count <= 0) return QL_OK;
+  if (count > kQmMax) return QL_EINVAL;
+  const NF4Thresholds th = nf4_thresholds();
+  // a launch stays below 2^31 work-items: weights past that go to another one
+  const int64_t cap = (int64_t(1) << 31) / (dq ? kQdThreads : 256);
+  for (int i0 = 0; i0 < count;) {
+    QuantBatch b{};
+    int64_t g = 0;
+    int h = 0, j = 0;
+    for (; i0 + j < count && j < kQmMax; ++j) {
+      const int i = i0 + j;
+      const int64_t gi = dq ? quant_dq_groups(n[i]) : quant_groups(n[i]);
+      if (j > 0 && g + gi > cap) break;
+      b.w[j] = w[i];
+      b.n[j] = n[i];
+      b.packed[j] = packed[i];
+      b.absmax[j] = absmax[i];
+      b.g0[j] = (int)g;
+      b.h0[j] = h;
+      if (dq) {
+        b.partial[j] = partial[i];
+        b.q[j] = q[i];
+        b.sigma[j] = sigma[i];
+        b.mean[j] = mean[i];
+        h += dq_code_groups((n[i] + block - 1) / block);
+      }
+      g += gi;
+    }
+    b.count = j;
+    for (int k = j; k <= kQmMax; ++k) {
+      b.g0[k] = (int)g;
+      b.h0[k] = h;
+    }
+#define QL_QUANT(T, BLKV)                                                                         \
+  if (dq)                                                                                          \
+    hipLaunchKernelGGL((k_nf4_quantize_dq_many<T, BLKV>), dim3((unsigned)g), dim3(kQdThreads), 0, \
+                       stream, b, th);                                                             \
+  else                                                                                             \
+    hipLaunchKernelGGL((k_nf4_quantize_many<T, BLKV>), dim3((unsigned)g), dim3(256), 0, stream, b, \
+                       th)
+    if (w_dtype == QL_BF16) {
+      if (block == 128) QL_QUANT(uint16_t, 128); else QL_QUANT(uint16_t, 64);
+    } else if (w_dtype == QL_F16) {
+      if (block == 128) QL_QUANT(_Float16, 128); else QL_QUANT(_Float16, 64);
+    } else {
+      if (block == 128) QL_QUANT(float, 128); else QL_QUANT(float, 64);
+    }
+#undef QL_QUANT
+    QL_HIP_CHECK_LAUNCH();
+    if (dq) {
+      hipLaunchKernelGGL(k_dq_codes_many, dim3((unsigned)h), dim3(kDcThreads), 0, stream, b, block);
+      QL_HIP_CHECK_LAUNCH();
+    }
+    i0 += j;
+  }
   return QL_OK;
 }
 

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 111
+    assert L.ql_abi_version() == 112
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -160,6 +160,44 @@ def test_quantize_rejects_bad_buffers():
                           16, None) == b.QL_EWORKSPACE
     assert L.nf4_dequantize(ctypes.byref(d), ctypes.c_void_p(FAKE + 4), b.QL_F32,
                             None) == b.QL_EALIGN
+
+
+def _many(L, descs, ptrs=None, dtype=b.QL_BF16, ws=None, ws_bytes=0, count=None):
+    n = len(descs)
+    arr = (b.QlNf4 * max(n, 1))(*descs)
+    pv = (ctypes.c_void_p * max(n, 1))(*(ptrs if ptrs is not None else [FAKE] * n))
+    return L.nf4_quantize_many(n if count is None else count, pv, dtype, arr,
+                               ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+@no_gpu
+def test_quantize_many_rejects_bad_arguments():
+    """nf4_quantize_many checks every weight before enqueueing anything."""
+    L = q.lib()
+    ok = _desc()
+    assert _many(L, [ok], count=-1) == b.QL_EINVAL
+    assert L.nf4_quantize_many(1, None, b.QL_BF16, ctypes.byref(ok), None, 0, None) == b.QL_EINVAL
+    assert _many(L, [ok, ok], dtype=5) == b.QL_EINVAL
+    # an invalid descriptor anywhere in the list, with its own error code
+    assert _many(L, [ok, _desc(rows=0)]) == b.QL_EINVAL
+    assert _many(L, [ok, ok, _desc(block=96)]) == b.QL_EUNSUPPORTED
+    assert _many(L, [ok, _desc(packed=FAKE + 8)]) == b.QL_EALIGN
+    # mixed block size or form
+    assert _many(L, [ok, _desc(block=128)]) == b.QL_EINVAL
+    assert _many(L, [ok, _desc(dq=1)]) == b.QL_EINVAL
+    # a NULL or misaligned weight pointer
+    assert _many(L, [ok, ok], ptrs=[FAKE, 0]) == b.QL_EINVAL
+    assert _many(L, [ok, ok], ptrs=[FAKE, FAKE + 2]) == b.QL_EALIGN
+    # the double-quantised form needs the sum of the per-weight workspaces
+    d1, d2 = _desc(dq=1, rows=128), _desc(dq=1, rows=4096, cols=4096)
+    need = (q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 128, 64, 0)
+            + q.workspace_bytes(q.QL_OP_QUANTIZE, 0, 4096, 4096, 0))
+    assert q.quantize_many_workspace_bytes([(128, 64), (4096, 4096)]) == need
+    assert _many(L, [d1, d2]) == b.QL_EWORKSPACE
+    assert _many(L, [d1, d2], ws=FAKE, ws_bytes=need - 256) == b.QL_EWORKSPACE
+    assert _many(L, [d1, d2], ws=FAKE + 16, ws_bytes=need) == b.QL_EALIGN
+    # nothing to do
+    assert _many(L, [], count=0) == b.QL_OK
 
 
 def _fwd(L, M=16, r=8, act=b.QL_BF16, lora=b.QL_BF16, alpha=16.0, x=FAKE, y=FAKE, A=FAKE,
