@@ -305,8 +305,7 @@ int qlora_linear_bwd_acc(const void *dy, const void *x, int32_t act_dtype, int64
  * Forward with LoRA dropout:  u = xd A^T,  y = x W^^T + s u B^T.
  * Arguments as for qlora_linear_fwd (same workspace size).  u_save receives
  * the u of the dropped input, which is what qlora_linear_bwd_dropout's
- * u_saved expects.  dropout_p > 0 requires 16-bit activations (QL_EUNSUPPORTED
- * otherwise) and always takes the matrix-core GEMM, also for M <= 16.
+ * u_saved expects.  Every activation dtype and shape of qlora_linear_fwd.
  * Errors: as qlora_linear_fwd; QL_EINVAL for dropout_p outside [0, 1).
  */
 int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
@@ -319,9 +318,8 @@ int qlora_linear_fwd_dropout(const void *x, int32_t act_dtype, int64_t M, const 
  *     u = xd A^T (or u_saved),  g = s dy B,  dB = s dy^T u,
  *     dA = g^T xd,  dx = dy W^ + d .* (g A).
  * accumulate 0 overwrites dA and dB, 1 adds into them (as
- * qlora_linear_bwd_acc).  Workspace as qlora_linear_bwd.  dropout_p > 0
- * requires 16-bit activations and, when dx is wanted, N % 8 == 0
- * (QL_EUNSUPPORTED otherwise).
+ * qlora_linear_bwd_acc).  Workspace as qlora_linear_bwd.  Every activation
+ * dtype and shape of qlora_linear_bwd.
  * Errors: as qlora_linear_bwd; QL_EINVAL for dropout_p outside [0, 1) or
  * accumulate not 0/1.
  */
@@ -383,7 +381,9 @@ const char *ql_strerror(int status);
  *   111: the matrix-core input gradient takes N % 8 == 0 and any K of the
  *        layer (before: N % 64 == 0, K % 128 == 0), so more backward
  *        workspaces hold its split-K partials.
- *   112: nf4_quantize_many (several weights per launch). */
+ *   112: nf4_quantize_many (several weights per launch).
+ *   113: LoRA dropout with fp32 activations, and its backward for every
+ *        shape (before: 16-bit activations only, dx with N % 8 == 0). */
 int ql_abi_version(void);
 
 #ifdef __cplusplus

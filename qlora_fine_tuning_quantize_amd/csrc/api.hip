@@ -162,7 +162,7 @@ int dropout_of(double p, uint64_t seed, Dropout &d, float &scale) {
 
 extern "C" {
 
-int ql_abi_version(void) { return 112; }
+int ql_abi_version(void) { return 113; }
 
 const char *ql_strerror(int status) {
   switch (status) {
@@ -313,7 +313,6 @@ static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 
                       size_t ws_bytes, void *stream) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
-  if (drop && act_dtype == QL_F32) return QL_EUNSUPPORTED;
   if (!x || !y) return QL_EINVAL;
   if (!aligned16(x) || !aligned16(y) || (u_save && !aligned16(u_save))) return QL_EALIGN;
   const int64_t N = W->rows, K = W->cols;
@@ -425,8 +424,6 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
                       const Dropout *drop = nullptr, float dscale = 1.0f) {
   int st = check_linear_common(act_dtype, M, W, A, B, lora_dtype, r, alpha);
   if (st) return st;
-  if (drop && (act_dtype == QL_F32 || (dx && !gemm_dx_supported(W->rows, W->cols))))
-    return QL_EUNSUPPORTED;
   if (!dy || !x || !dA || !dB) return QL_EINVAL;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(dA) || !aligned16(dB) ||
       (dx && !aligned16(dx)) || (u_saved && !aligned16(u_saved)))
@@ -472,7 +469,8 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   if (act_dtype != QL_F32 && gemm_dx_supported(N, K))
     return launch_gemm_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s,
                           rows_partial, drop, dscale);
-  return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s);
+  return launch_simple_dx(dy, act_dtype, M, W->packed, sc, N, K, g, A, lora_dtype, r, dx, s, drop,
+                          dscale);
 }
 
 int qlora_linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t M,

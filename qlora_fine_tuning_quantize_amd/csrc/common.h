@@ -226,6 +226,11 @@ __device__ __forceinline__ uint32_t dropout_keep4(const Dropout &d, uint64_t e) 
          ((uint32_t)(w[2] >= d.thr) << 2) | ((uint32_t)(w[3] >= d.thr) << 3);
 }
 
+// keep bit of element e alone (the word e % 4 of its counter's draw)
+__device__ __forceinline__ bool dropout_keep1(const Dropout &d, uint64_t e) {
+  return (dropout_keep4(d, e) >> (e & 3u)) & 1u;
+}
+
 // 8 16-bit values (elements e .. e + 7 in order, e % 4 == 0) with the dropped
 // ones set to zero
 __device__ __forceinline__ u32x4 dropout_mask8(const Dropout &d, uint64_t e, u32x4 v) {

@@ -73,7 +73,8 @@ int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *pa
                       int lora_dtype, int32_t r, float s, void *y, hipStream_t stream);
 int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *packed,
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
-                     int lora_dtype, int32_t r, void *dx, hipStream_t stream);
+                     int lora_dtype, int32_t r, void *dx, hipStream_t stream,
+                     const Dropout *drop = nullptr, float dscale = 1.0f);
 
 // gemv.hip: decode-sized forward (M <= 16, 16-bit activations): computes
 // u = x A^T itself and writes it to u_save when non-null.  One launch, or,

@@ -23,11 +23,13 @@ __device__ __forceinline__ float ld(const void *p, int64_t i) {
 constexpr int kRowsTM = 32;
 constexpr int kRowsChunk = 64;
 
-template <typename PT, typename QT>
+// DROP: P is the activation x of the LoRA dropout; dropped elements are
+// staged as zeros (the reduction applies 1/(1-p)).
+template <typename PT, typename QT, bool DROP>
 __global__ __launch_bounds__(256) void k_lora_rows(const void *__restrict__ P, int64_t M, int64_t C,
                                                    const void *__restrict__ Q, int64_t ldq_j,
                                                    int64_t ldq_c, int32_t r, int64_t slice,
-                                                   float *__restrict__ partial) {
+                                                   float *__restrict__ partial, Dropout dr) {
   __shared__ float ps[kRowsTM][kRowsChunk + 1];
   __shared__ float qs[128][kRowsChunk + 1];
   const int t = threadIdx.x;
@@ -42,7 +44,9 @@ __global__ __launch_bounds__(256) void k_lora_rows(const void *__restrict__ P, i
     for (int e = t; e < kRowsTM * kRowsChunk; e += 256) {
       const int rr = e / kRowsChunk, cc = e % kRowsChunk;
       const int64_t m = m0 + rr, c = c0 + cc;
-      ps[rr][cc] = (m < M && c < c_end) ? ld<PT>(P, m * C + c) : 0.0f;
+      const bool in = m < M && c < c_end;
+      ps[rr][cc] = in && (!DROP || dropout_keep1(dr, (uint64_t)(m * C + c))) ? ld<PT>(P, m * C + c)
+                                                                             : 0.0f;
     }
     for (int e = t; e < r * kRowsChunk; e += 256) {
       const int jj = e / kRowsChunk, cc = e % kRowsChunk;
@@ -385,10 +389,9 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
                         const Dropout *drop) {
   if (M <= 0) return QL_OK;
   int S;
-  if (drop && (!rows_use_mfma(p_dtype, C) || ldq_c != 1 || ldq_j % 8 != 0 || C < 8))
-    return QL_EUNSUPPORTED;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
-  if (rows_use_mfma(p_dtype, C)) {
+  // the matrix-core kernel masks factor-row-major slices only
+  if (rows_use_mfma(p_dtype, C) && (!drop || (ldq_c == 1 && ldq_j % 8 == 0 && C >= 8))) {
     const MRowsPlan mp = mrows_plan(M, C, r, q_dtype);
     S = mp.S;
     const dim3 grid((unsigned)((M + kMRowsTile - 1) / kMRowsTile), (unsigned)S);
@@ -429,8 +432,14 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
     const dim3 grid((unsigned)((M + kRowsTM - 1) / kRowsTM), (unsigned)S);
     with_type(p_dtype, [&](auto *pt) {
       with_type(q_dtype, [&](auto *qt) {
-        hipLaunchKernelGGL((k_lora_rows<elem_of<decltype(pt)>, elem_of<decltype(qt)>>), grid,
-                           dim3(256), 0, stream, P, M, C, Q, ldq_j, ldq_c, r, slice, partial);
+        using PT = elem_of<decltype(pt)>;
+        using QT = elem_of<decltype(qt)>;
+        if (drop)
+          hipLaunchKernelGGL((k_lora_rows<PT, QT, true>), grid, dim3(256), 0, stream, P, M, C, Q,
+                             ldq_j, ldq_c, r, slice, partial, dr);
+        else
+          hipLaunchKernelGGL((k_lora_rows<PT, QT, false>), grid, dim3(256), 0, stream, P, M, C, Q,
+                             ldq_j, ldq_c, r, slice, partial, dr);
       });
     });
   }
@@ -452,11 +461,12 @@ int launch_lora_rows_ws(const void *P, int p_dtype, int64_t M, int64_t C, const 
 constexpr int kColsTC = 64;
 constexpr int kColsChunk = 64;
 
-template <typename PT>
+// DROP: as for k_lora_rows.
+template <typename PT, bool DROP>
 __global__ __launch_bounds__(256) void k_lora_cols(const float *__restrict__ R, int64_t M,
                                                    int32_t r, const void *__restrict__ P,
                                                    int64_t C, int64_t slice,
-                                                   float *__restrict__ partial) {
+                                                   float *__restrict__ partial, Dropout dr) {
   __shared__ float rs[kColsChunk][129];
   const int t = threadIdx.x;
   const int cl = t % kColsTC, j0 = t / kColsTC;
@@ -475,7 +485,8 @@ __global__ __launch_bounds__(256) void k_lora_cols(const float *__restrict__ R, 
     __syncthreads();
     const int n_in = (int)((m_end - mc) < kColsChunk ? (m_end - mc) : kColsChunk);
     for (int mm = 0; mm < n_in; ++mm) {
-      const float pv = (c < C) ? ld<PT>(P, (mc + mm) * C + c) : 0.0f;
+      const int64_t e = (mc + mm) * C + c;
+      const float pv = c < C && (!DROP || dropout_keep1(dr, (uint64_t)e)) ? ld<PT>(P, e) : 0.0f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int j = j0 + 4 * i;
@@ -878,7 +889,6 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   if (pending) pending->S = 0;
   if (C <= 0) return QL_OK;
   int S;
-  if (drop && !cols_use_mfma(p_dtype, C)) return QL_EUNSUPPORTED;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (cols_use_mfma(p_dtype, C)) {
     const MColsPlan mp = mcols_plan(M, C);
@@ -912,8 +922,13 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
     const int64_t slice = (M + S - 1) / S;
     const dim3 grid((unsigned)((C + kColsTC - 1) / kColsTC), (unsigned)S);
     with_type(p_dtype, [&](auto *pt) {
-      hipLaunchKernelGGL((k_lora_cols<elem_of<decltype(pt)>>), grid, dim3(256), 0, stream, R, M,
-                         r, P, C, slice, partial);
+      using PT = elem_of<decltype(pt)>;
+      if (drop)
+        hipLaunchKernelGGL((k_lora_cols<PT, true>), grid, dim3(256), 0, stream, R, M, r, P, C,
+                           slice, partial, dr);
+      else
+        hipLaunchKernelGGL((k_lora_cols<PT, false>), grid, dim3(256), 0, stream, R, M, r, P, C,
+                           slice, partial, dr);
     });
   }
   QL_HIP_CHECK_LAUNCH();

@@ -94,13 +94,17 @@ __global__ __launch_bounds__(256) void k_simple_fwd(const void *__restrict__ x, 
 // Input gradient.  Contraction over n in steps of 64; the weight tile holds
 // rows n0..n0+64 of W^ restricted to columns k0..k0+64 (one 64-element
 // chunk of each row, inside one NF4 block).
-template <typename AT, typename LT>
+// DROP: LoRA dropout on the bypass input; the bypass term of output (m, k)
+// is multiplied by keep(m, k) / (1 - p) (dscale) before the base product is
+// added to it.
+template <typename AT, typename LT, bool DROP>
 __global__ __launch_bounds__(256) void k_simple_dx(const void *__restrict__ dy, int64_t M,
                                                    const uint8_t *__restrict__ packed,
                                                    BlockScales sc, int64_t N, int64_t K,
                                                    const float *__restrict__ g,
                                                    const void *__restrict__ A, int32_t r,
-                                                   void *__restrict__ dx) {
+                                                   void *__restrict__ dx, Dropout dr,
+                                                   float dscale) {
   __shared__ float ds[kT][kT + 1];  // [m][n]
   __shared__ float ws[kT][kT + 1];  // [n][k]
   __shared__ float cb[16];
@@ -157,6 +161,7 @@ __global__ __launch_bounds__(256) void k_simple_dx(const void *__restrict__ dy, 
       const int64_t k = k0 + tk * 4 + j;
       float l = 0.0f;
       for (int jj = 0; jj < r; ++jj) l = __builtin_fmaf(g[m * r + jj], ldv<LT>(A, jj * K + k), l);
+      if constexpr (DROP) l = dropout_keep1(dr, (uint64_t)(m * K + k)) ? dscale * l : 0.0f;
       store_from_f32(reinterpret_cast<AT *>(dx), m * K + k, acc[i][j] + l);
     }
   }
@@ -178,12 +183,20 @@ int launch_simple_fwd(const void *x, int act_dtype, int64_t M, const uint8_t *pa
 
 int launch_simple_dx(const void *dy, int act_dtype, int64_t M, const uint8_t *packed,
                      BlockScales sc, int64_t N, int64_t K, const float *g, const void *A,
-                     int lora_dtype, int32_t r, void *dx, hipStream_t stream) {
+                     int lora_dtype, int32_t r, void *dx, hipStream_t stream,
+                     const Dropout *drop, float dscale) {
   const dim3 grid((unsigned)(K / kT), (unsigned)((M + kT - 1) / kT));
+  const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   with_type(act_dtype, [&](auto *at) {
     with_type(lora_dtype, [&](auto *lt) {
-      hipLaunchKernelGGL((k_simple_dx<elem_of<decltype(at)>, elem_of<decltype(lt)>>), grid,
-                         dim3(256), 0, stream, dy, M, packed, sc, N, K, g, A, r, dx);
+      using AT = elem_of<decltype(at)>;
+      using LT = elem_of<decltype(lt)>;
+      if (drop)
+        hipLaunchKernelGGL((k_simple_dx<AT, LT, true>), grid, dim3(256), 0, stream, dy, M, packed,
+                           sc, N, K, g, A, r, dx, dr, dscale);
+      else
+        hipLaunchKernelGGL((k_simple_dx<AT, LT, false>), grid, dim3(256), 0, stream, dy, M,
+                           packed, sc, N, K, g, A, r, dx, dr, 1.0f);
     });
   });
   QL_HIP_CHECK_LAUNCH();

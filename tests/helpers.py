@@ -58,6 +58,16 @@ def gamma_prob_f32(n: int, lam: float = F32_LAMBDA) -> float:
     return math.expm1(lam * math.sqrt(n) * u + n * u * u / (1.0 - u))
 
 
+def f32_chain(out, M, N, K, r):
+    """Roundings on the longest path to each fp32 output of the layer (sums of
+    n terms count n; scalings and the final additions one each; 4 spare for
+    partial sums scaled before their reduction, such as the dropout's
+    1/(1-p)): u = x A^T, y = x W^T + s u B^T, g = s dy B, dx = dy W + g A,
+    dA = g^T x, dB = s dy^T u."""
+    return {"u": K, "y": K + r + 2, "dx": N + r + 2, "dA": N + 1 + M,
+            "dB": K + M + 1}[out] + 4
+
+
 def assert_f32_within(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, n: int, what: str):
     bound = gamma_prob_f32(n) * np.asarray(mag, np.float64) + 2.0 ** -40 * np.abs(ref)
     excess = np.abs(np.asarray(got, np.float64) - ref) - bound

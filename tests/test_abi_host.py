@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ql_abi_version() == 112
+    assert L.ql_abi_version() == 113
 
 
 def test_nf4_sizes_and_bits_per_param(orc):
@@ -327,14 +327,14 @@ def test_dropout_entry_points_reject_bad_arguments():
         assert fwd(p=p) == b.QL_EINVAL
         assert bwd(p=p) == b.QL_EINVAL
         assert L.ql_dropout_mask(4, 4, p, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
-    assert fwd(act=b.QL_F32) == b.QL_EUNSUPPORTED   # dropout runs on the 16-bit paths only
     assert fwd(M=0) == b.QL_EINVAL
     assert fwd(ws_bytes=255) == b.QL_EWORKSPACE
-    assert bwd(act=b.QL_F32) == b.QL_EUNSUPPORTED
     assert bwd(acc=2) == b.QL_EINVAL
     assert bwd(ws_bytes=1024) == b.QL_EWORKSPACE
-    # dx with dropout needs the matrix-core dx GEMM's shapes (N % 8 == 0)
-    assert bwd(desc=_desc(rows=100, cols=256)) == b.QL_EUNSUPPORTED
+    # fp32 activations and any N are accepted: the checks after the dtype's run
+    assert fwd(act=b.QL_F32, ws_bytes=255) == b.QL_EWORKSPACE
+    assert bwd(act=b.QL_F32, ws_bytes=1024) == b.QL_EWORKSPACE
+    assert bwd(desc=_desc(rows=100, cols=256), ws_bytes=1024) == b.QL_EWORKSPACE
     assert L.ql_dropout_mask(0, 4, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
     assert L.ql_dropout_mask(4, -1, 0.1, 7, ctypes.c_void_p(FAKE), None) == b.QL_EINVAL
     assert L.ql_dropout_mask(4, 4, 0.1, 7, None, None) == b.QL_EINVAL

@@ -6,7 +6,7 @@ quantisation and LoRA dropout from fixed seeds, so that the kernel-choice
 boundaries (decode GEMV up to 16 tokens, the 64-token kernels up to 128,
 the 256-token GEMMs with their width / split-K plans, ragged N, the
 element-wise LoRA kernels for N not a multiple of 8, the fp32-path dx for N
-not a multiple of 64 or K not a multiple of 128) are crossed in combinations
+not a multiple of 8, dropout on each of them) are crossed in combinations
 the hand-picked cases do not list.  16-bit compute: the parity tests'
 tolerances.  fp32 compute: values here reach ~10, past what a fixed atol of
 1e-5 fits, so each element is held to the probabilistic fp32 rounding bound
@@ -18,21 +18,12 @@ import torch
 
 import qlora_fine_tuning_quantize_amd as q
 import synth_inputs as si
-from tests.helpers import (BF16_TOL, F16_TOL, U_BF16, U_F16, assert_f32_within,
+from tests.helpers import (BF16_TOL, F16_TOL, U_BF16, U_F16, assert_f32_within, f32_chain,
                            assert_layer_within16, host, layer_bounds16, rel_err)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 N_CASES = 48
-
-
-def f32_chain(out, M, N, K, r):
-    """Roundings on the longest path to each fp32 output (sums of n terms
-    count n; scalings and the final additions one each; 4 spare for partial
-    sums scaled before their reduction): u = x A^T, y = x W^T + s u B^T,
-    g = s dy B, dx = dy W + g A, dA = g^T x, dB = s dy^T u."""
-    return {"u": K, "y": K + r + 2, "dx": N + r + 2, "dA": N + 1 + M,
-            "dB": K + M + 1}[out] + 4
 
 
 def _draw(i):
@@ -50,9 +41,9 @@ def _draw(i):
     alpha = float(r * rng.choice([0.5, 1.0, 2.0]))
     dq = bool(rng.integers(0, 2))
     lora = torch.float32 if (act == torch.float32 or rng.integers(0, 3) == 0) else act
-    # dropout on the 16-bit paths, with dx shapes the matrix-core dx kernel takes
+    # dropout on every path and shape
     drop = 0.0
-    if act != torch.float32 and N % 64 == 0 and K % 128 == 0 and rng.integers(0, 3) == 0:
+    if rng.integers(0, 3) == 0:
         drop = float(rng.choice([0.05, 0.3]))
     return dict(M=M, N=N, K=K, r=r, alpha=alpha, act=act, lora=lora, block=block, dq=dq, drop=drop)
 
@@ -90,9 +81,10 @@ def test_random_shape(orc, i):
     if act == torch.float32:
         # magnitudes: the same expressions on absolute values (s > 0)
         ab = lambda a: np.abs(np.asarray(a, np.float64))
-        y_mag, u_mag = orc.linear_fwd(ab(t["x"]), ab(w_hat), ab(t["A"]), ab(t["B"]), alpha, r)
+        y_mag, u_mag = orc.linear_fwd(ab(t["x"]), ab(w_hat), ab(t["A"]), ab(t["B"]), alpha, r,
+                                      drop=mult)
         dx_mag, dA_mag, dB_mag = orc.linear_bwd(ab(t["x"]), ab(w_hat), ab(t["A"]), ab(t["B"]),
-                                                ab(t["dy"]), alpha, r)
+                                                ab(t["dy"]), alpha, r, drop=mult)
         mag = {"y": y_mag, "u": u_mag, "dx": dx_mag, "dA": dA_mag, "dB": dB_mag}
         for k in got:
             assert_f32_within(got[k], ref[k], mag[k], f32_chain(k, M, N, K, r), k)
