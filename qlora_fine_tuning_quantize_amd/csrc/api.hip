@@ -305,8 +305,8 @@ int nf4_dequantize(const ql_nf4 *q, void *out, int32_t out_dtype, void *stream) 
                                (hipStream_t)stream);
 }
 
-// drop: LoRA dropout of the bypass input (16-bit activations only), with
-// dscale = 1 / (1 - p); NULL for none.
+// drop: LoRA dropout of the bypass input, with dscale = 1 / (1 - p); NULL
+// for none.
 static int linear_fwd(const void *x, int32_t act_dtype, int64_t M, const ql_nf4 *W,
                       const void *A, const void *B, int32_t lora_dtype, int32_t r, float alpha,
                       const Dropout *drop, float dscale, void *y, float *u_save, void *ws,
