@@ -200,6 +200,7 @@ def nf4_quantize(w: torch.Tensor, double_quant: bool = True, out: NF4Weight | No
     assert w.dim() == 2 and w.is_contiguous() and w.is_cuda
     N, K = w.shape
     q = out or NF4Weight.empty(N, K, double_quant, w.device, block)
+    assert (q.rows, q.cols, q.double_quant, q.block) == (N, K, double_quant, block)
     if ws is None and double_quant:
         ws = workspace(QL_OP_QUANTIZE, 0, N, K, 0, w.device)
     st = q.struct()
@@ -226,6 +227,8 @@ def nf4_quantize_many(ws_in: list, double_quant: bool = True, out: list | None =
     outs = out or [NF4Weight.empty(w.shape[0], w.shape[1], double_quant, w.device, block)
                    for w in ws_in]
     assert len(outs) == n
+    for w, o in zip(ws_in, outs):
+        assert (o.rows, o.cols, o.double_quant, o.block) == (*w.shape, double_quant, block)
     if ws is None and double_quant and n:
         ws = torch.empty(max(256, quantize_many_workspace_bytes([w.shape for w in ws_in])),
                          dtype=torch.uint8, device=dev)
