@@ -434,13 +434,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 }
 
 // ===========================================================================
-// Forward for few tokens (up to a few hundred): 64 tokens x 128 outputs per
-// workgroup, 4 waves, wave w owning outputs 32 w .. 32 w + 31 for all 64
-// tokens.  A 256-token tile would run the matrix cores mostly on padding
-// rows, and with one wave per output row the weight tile needs no
+// Forward for few tokens (up to a few hundred): BM = 64 or 128 tokens x 128
+// outputs per workgroup, 4 waves, wave w owning outputs 32 w .. 32 w + 31
+// for all BM tokens.  A 256-token tile would run the matrix cores mostly on
+// padding rows, and with one wave per output row the weight tile needs no
 // dequantised copy in LDS: it is staged as packed codes (4 KB per step)
 // plus one block constant per row, and every wave dequantises its own rows
-// in registers right before its matrix ops.
+// in registers right before its matrix ops, once for all BM tokens (the
+// 128-token tile halves the weight reads and the dequantisation per token
+// of the 64-token one).
 //
 // The contraction order inside a step is permuted so that a lane's 16
 // packed bytes (32 consecutive codes of one row) feed all four 16-deep
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint16_t *__restric
 // k = 32 h + 8 kk + 0..7 in both operands (the weight from registers, the
 // activations from LDS chunk 4 h + kk of the token row).
 // ===========================================================================
-constexpr int kSmBM = 64;
+constexpr int kSmBM = 64;   // token tile of the fused form and of the smallest calls
 constexpr int kSmBN = 128;
 constexpr int kSmThreads = 256;
 
@@ -458,21 +460,26 @@ constexpr int kSmThreads = 256;
 // others return) each form one u slice tile -- token group, rank tile and
 // contraction slice -- from x and A; every tile workgroup writes its fp32
 // partial of x W^^T for its contraction slice (no bypass), and the next
-// launch forms y = RN(fmaf(s, sum_j u_j B_nj, sum of the slices)).
-template <typename AT, typename LT, bool DQ, bool FUSED>
+// launch forms y = RN(fmaf(s, sum_j u_j B_nj, sum of the slices)).  The
+// fused form runs with 64-token tiles only.
+template <int BM, typename AT, typename LT, bool DQ, bool FUSED>
 __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
     int64_t N, int64_t K, const float *__restrict__ u, const LT *__restrict__ B, int32_t r,
     float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit,
     const LT *__restrict__ A, float *__restrict__ upart, int uc, int MT, Dropout dr) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kSmBM * kRowBytes];
+  static_assert(BM == 64 || BM == 128, "token tiles of 64 or 128");
+  static_assert(!FUSED || BM == 64, "the fused form has 64-token tiles");
+  constexpr int MI = BM / 32;                // 32-token MFMA tiles per wave
+  constexpr int XR = BM * 8 / kSmThreads;    // 16-byte activation chunks per lane per step
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wp[2][kSmBN * 32];
   __shared__ float wsc[2][kSmBN];
-  __shared__ __attribute__((aligned(16))) uint8_t ls_u[kSmBM * kLoraStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ls_u[BM * kLoraStride];
   __shared__ __attribute__((aligned(16))) uint8_t ls_b[kSmBN * kLoraStride];
   __shared__ float2 lut[256];
   const int t = threadIdx.x;
-  const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+  const int64_t G = ((M + BM - 1) / BM) * ((N + kSmBN - 1) / kSmBN);
   if (FUSED && (int64_t)blockIdx.x >= G) {
     if (blockIdx.y == 0) {
       const int JT = (r + 15) / 16;
@@ -485,29 +492,29 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   lut[t] = make_float2(c_nf4[t >> 4], c_nf4[t & 15]);
 
   int64_t mt, nt;
-  tile_of((M + kSmBM - 1) / kSmBM, (N + kSmBN - 1) / kSmBN, mt, nt);
-  const int64_t m0 = mt * kSmBM, n0 = nt * kSmBN;
+  tile_of((M + BM - 1) / BM, (N + kSmBN - 1) / kSmBN, mt, nt);
+  const int64_t m0 = mt * BM, n0 = nt * kSmBN;
   const int64_t KB = K >> 6;
   const int split = blockIdx.y;
   const int ks0 = (int)(split * KB / nsplit), ks1 = (int)((split + 1) * KB / nsplit);
 
   // staging: lane t stages half t & 1 (16 bytes) of weight row t >> 1 and
-  // activation chunks t and t + 256 (token row (t >> 3) and 32 + (t >> 3));
-  // rows past N or M are clamped to the last valid row (their outputs are
-  // never stored)
+  // activation chunks t + 256 i, i < XR (token rows 32 i + (t >> 3)); rows
+  // past N or M are clamped to the last valid row (their outputs are never
+  // stored)
   const int w_row = t >> 1, w_half = t & 1;
   const int64_t w_n = n0 + w_row < N ? n0 + w_row : N - 1;
   const uint8_t *w_src = packed + ((w_n * K) >> 1) + 16 * w_half;
   const int64_t w_sc = w_n * KB;
   const float mu = DQ ? sc.mu[0] : 0.0f;
-  const uint16_t *x_src[2];
+  const uint16_t *x_src[XR];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < XR; ++i) {
     const int id = t + kSmThreads * i;
     const int64_t rr = m0 + (id >> 3) < M ? m0 + (id >> 3) : M - 1;
     x_src[i] = x + rr * K + 8 * (id & 7);
   }
-  u32x4 xr[2], wr;
+  u32x4 xr[XR], wr;
   int wq = 0;
   float wsig = 0.0f;
   auto load_x = [&](int step, int i) {
@@ -535,24 +542,24 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   const int wave = t >> 6, lane = t & 63;
   const int lr = lane & 31, lk = lane >> 5;
   const int my_row = 32 * wave + lr;  // this lane's weight row in the tile
-  f32x16 acc[2][1];
-  zero_acc(&acc[0][0], 2);
+  f32x16 acc[MI][1];
+  zero_acc(&acc[0][0], MI);
 
   __syncthreads();  // lut
-  load_x(ks0, 0);
-  load_x(ks0, 1);
+#pragma unroll
+  for (int i = 0; i < XR; ++i) load_x(ks0, i);
   load_w(ks0);
   if (!FUSED && split == 0) {
-    stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, 0, s, t);
+    stage_lora<BM, kSmThreads, AT>(ls_u, u, m0, M, r, 0, s, t);
     stage_lora<kSmBN, kSmThreads, AT>(ls_b, B, n0, N, r, 0, 1.0f, t);
   }
-  store_x(0, 0);
-  store_x(0, 1);
+#pragma unroll
+  for (int i = 0; i < XR; ++i) store_x(0, i);
   store_w(0);
   {
     const int nx = ks0 + 1 < ks1 ? ks0 + 1 : ks0;
-    load_x(nx, 0);
-    load_x(nx, 1);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) load_x(nx, i);
     load_w(nx);
   }
   __syncthreads();
@@ -562,16 +569,16 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint8_t *xb = xs[cur];
     const u32x4 wv = *reinterpret_cast<const u32x4 *>(wp[cur] + 32 * my_row + 16 * lk);
     const float wa = wsc[cur][my_row];
-    u32x4 xa[2][2];
+    u32x4 xa[2][MI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
       xa[0][i] = *reinterpret_cast<const u32x4 *>(xb + swz(32 * i + lr, 4 * lk));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cb = kk & 1, nb = cb ^ 1;
       if (kk < 3) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
           xa[nb][i] = *reinterpret_cast<const u32x4 *>(xb + swz(32 * i + lr, 4 * lk + kk + 1));
       }
       // the 8 codes of op kk: bytes 4 kk .. 4 kk + 3 of the lane's 16
@@ -583,15 +590,16 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
       }
       // staging of step k + 1 into the other buffer, one piece per op, each
       // register refilled for step k + 2 right after it was stored
-      if (kk < 2) {
+      if (kk < XR) {
         store_x(cur ^ 1, kk);
         load_x(pf, kk);
-      } else if (kk == 2) {
+      }
+      if (kk == 2) {
         store_w(cur ^ 1);
         load_w(pf);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i][0] = mfma32<AT>(wop, xa[cb][i], acc[i][0]);
+      for (int i = 0; i < MI; ++i) acc[i][0] = mfma32<AT>(wop, xa[cb][i], acc[i][0]);
     }
     __syncthreads();
   }
@@ -600,21 +608,21 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
   for (int j0 = 0; j0 < (!FUSED && split == 0 ? r : 0); j0 += 16) {
     if (j0 > 0) {
       __syncthreads();
-      stage_lora<kSmBM, kSmThreads, AT>(ls_u, u, m0, M, r, j0, s, t);
+      stage_lora<BM, kSmThreads, AT>(ls_u, u, m0, M, r, j0, s, t);
       stage_lora<kSmBN, kSmThreads, AT>(ls_b, B, n0, N, r, j0, 1.0f, t);
       __syncthreads();
     }
     const u32x4 bb = lora_frag(ls_b, my_row, lk);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = mfma32<AT>(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
+    for (int i = 0; i < MI; ++i) acc[i][0] = mfma32<AT>(bb, lora_frag(ls_u, 32 * i + lr, lk), acc[i][0]);
   }
   const int64_t col = n0 + 32 * wave;
   if (FUSED || nsplit > 1)
-    store_tile_f32<2, 1>(part + (int64_t)split * M * N, N, M, N, m0, col, acc, lane);
+    store_tile_f32<MI, 1>(part + (int64_t)split * M * N, N, M, N, m0, col, acc, lane);
   else if (n0 + kSmBN <= N && N % 8 == 0)  // per-wave slices of 32 rows in a dead staging buffer
-    store_tile_lds<AT, 2, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
+    store_tile_lds<AT, MI, 1>(y, N, M, m0, col, acc, &xs[0][0] + wave * 32 * (2 * 32 + 16), lane);
   else
-    store_tile_t<AT, 2, 1>(y, N, M, N, m0, col, acc, lane);
+    store_tile_t<AT, MI, 1>(y, N, M, N, m0, col, acc, lane);
 }
 
 // ===========================================================================
@@ -989,24 +997,35 @@ static TilePlan plan_tiles(int64_t M, int64_t cols, int64_t steps, bool wide_ok,
   return best;
 }
 
-// Forward tile: 64 tokens x 128 outputs (k_gemm_fwd_small) up to kFwdSmallM
-// tokens, else 256 tokens x the planned width (measured on the 8B MLP
-// shapes: the small tile is faster up to 128 tokens, slower at 256).
-constexpr int64_t kFwdSmallM = 128;
+// Forward tile (k_gemm_fwd_small): 64 tokens x 128 outputs up to 64 tokens,
+// 128 tokens x 128 outputs up to kFwdMidM tokens, else 256 tokens x the
+// planned width (k_gemm_fwd).  Measured on the 8B MLP's gate and down shapes
+// at 80-512 tokens: from 65 to 128 tokens the 128-token tile is 10-13 %
+// faster than two 64-token tiles; from 160 on it ties with the 256-token
+// tile or loses.
+constexpr int64_t kFwdMidM = 128;
+
+static int fwd_small_bm(int64_t M) { return M <= kSmBM ? 64 : (M <= kFwdMidM ? 128 : 0); }
 
 static int fwd_split(int64_t M, int64_t N, int64_t K) {
-  if (M <= kFwdSmallM)
-    return split_count(((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN), K >> 6, M, N, 512);
+  const int64_t bm = fwd_small_bm(M);
+  if (bm)
+    return split_count(((M + bm - 1) / bm) * ((N + kSmBN - 1) / kSmBN), K >> 6, M, N, 512);
   return plan_tiles(M, N, K >> 6, true, true).S;
 }
 
-// Input-gradient tile: 64 tokens x 128 columns up to kDxSmallM tokens, else
-// 256 tokens x the planned width (256 needs K % 256 == 0).
-constexpr int64_t kDxSmallM = 128;
+// Input-gradient tile: 64 tokens x 128 columns up to 64 tokens, 128 x 128 up
+// to kDxMidM tokens, else 256 tokens x the planned width (256 needs K % 256
+// == 0).  The same measurement as the forward's: the 128-token tile is 10-14
+// % faster from 65 to 128 tokens and 6-8 % slower from 160 on.
+constexpr int64_t kDxMidM = 128;
+
+static int dx_small_bm(int64_t M) { return M <= 64 ? 64 : (M <= kDxMidM ? 128 : 0); }
 
 static int dx_split(int64_t M, int64_t N, int64_t K) {
   const int64_t steps = (N + kDxBC - 1) / kDxBC;
-  if (M <= kDxSmallM) return split_count(((M + 63) / 64) * ((K + 127) / 128), steps, M, K, 512);
+  const int64_t bm = dx_small_bm(M);
+  if (bm) return split_count(((M + bm - 1) / bm) * ((K + 127) / 128), steps, M, K, 512);
   return plan_tiles(M, K, steps, K % 256 == 0, true).S;
 }
 
@@ -1040,21 +1059,24 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
   const uint16_t *x = (const uint16_t *)xv;
   uint16_t *y = (uint16_t *)yv;
   const bool dq = sc.absmax == nullptr;
-  if (M <= kFwdSmallM) {
-    const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+  if (const int bm = fwd_small_bm(M)) {
+    const int64_t G = ((M + bm - 1) / bm) * ((N + kSmBN - 1) / kSmBN);
     const int S = part ? fwd_split(M, N, K) : 1;
-#define QL_FWS(LT, DQV)                                                                          \
-  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, false>), dim3((unsigned)G, (unsigned)S),    \
+#define QL_FWS(BMV, LT, DQV)                                                                     \
+  hipLaunchKernelGGL((k_gemm_fwd_small<BMV, AT, LT, DQV, false>), dim3((unsigned)G, (unsigned)S), \
                      dim3(kSmThreads), 0, stream, x, M, packed, sc, N, K, u, (const LT *)B, r, s, \
                      y, part, S, (const LT *)nullptr, (float *)nullptr, 0, 0, Dropout{0u, 0u, 0u})
+#define QL_FWS_BM(LT, DQV) \
+  do { if (bm == 64) QL_FWS(64, LT, DQV); else QL_FWS(128, LT, DQV); } while (0)
     with_half(act_dtype, [&](auto *tag) {
       using AT = elem_of<decltype(tag)>;
       if (lora_dtype == QL_F32) {
-        if (dq) QL_FWS(float, true); else QL_FWS(float, false);
+        if (dq) QL_FWS_BM(float, true); else QL_FWS_BM(float, false);
       } else {
-        if (dq) QL_FWS(AT, true); else QL_FWS(AT, false);
+        if (dq) QL_FWS_BM(AT, true); else QL_FWS_BM(AT, false);
       }
     });
+#undef QL_FWS_BM
 #undef QL_FWS
     QL_HIP_CHECK_LAUNCH();
     if (S > 1) return reduce_split(act_dtype, part, S, M * N, y, stream);
@@ -1110,7 +1132,7 @@ int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_
   float *upart = part + (size_t)S * M * N;
   const dim3 grid((unsigned)(G + (int64_t)us.U * JT * MT), (unsigned)S);
 #define QL_FWF(LT, DQV)                                                                          \
-  hipLaunchKernelGGL((k_gemm_fwd_small<AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream,  \
+  hipLaunchKernelGGL((k_gemm_fwd_small<kSmBM, AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream, \
                      x, M, packed, sc, N, K, (const float *)nullptr, (const LT *)B, r, s,         \
                      (uint16_t *)nullptr, part, S, (const LT *)A, upart, us.uc, MT, dr)
   with_half(act_dtype, [&](auto *tag) {
@@ -1137,11 +1159,11 @@ int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *pac
   const uint16_t *dy = (const uint16_t *)dyv;
   uint16_t *dx = (uint16_t *)dxv;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
-  const bool small = M <= kDxSmallM;
-  const int bm = small ? 64 : kBM;
-  const TilePlan pl = small ? TilePlan{128, part ? dx_split(M, N, K) : 1}
-                            : plan_tiles(M, K, (N + kDxBC - 1) / kDxBC, K % 256 == 0,
-                                         part != nullptr);
+  const int sbm = dx_small_bm(M);
+  const int bm = sbm ? sbm : kBM;
+  const TilePlan pl = sbm ? TilePlan{128, part ? dx_split(M, N, K) : 1}
+                          : plan_tiles(M, K, (N + kDxBC - 1) / kDxBC, K % 256 == 0,
+                                       part != nullptr);
   const int bx = pl.bn, S = pl.S;
   const int64_t G = ((M + bm - 1) / bm) * ((K + bx - 1) / bx);
   const bool dq = sc.absmax == nullptr;
@@ -1157,7 +1179,8 @@ int launch_gemm_dx(const void *dyv, int act_dtype, int64_t M, const uint8_t *pac
   do { if (lora_dtype == QL_F32) QL_DX_DQ(BMV, BXV, float); else QL_DX_DQ(BMV, BXV, AT); } while (0)
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
-    if (small) QL_DX_LT(64, 128);
+    if (sbm == 64) QL_DX_LT(64, 128);
+    else if (sbm == 128) QL_DX_LT(128, 128);
     else if (bx == 256) QL_DX_LT(256, 256);
     else QL_DX_LT(256, 128);
   });

@@ -278,10 +278,13 @@ BF16_CASES = [
     (300, 456, 4416, 16, True, torch.bfloat16), # 256-token dx tiles, ragged N and K
     (130, 2120, 576, 16, True, torch.bfloat16), # ragged dx with split-K
     (1, 200, 2048, 5, False, torch.bfloat16),   # GEMV: ragged N, rank 5, fp32 absmax
-    # 64-token forward tiles (17..128 tokens)
+    # 64-token forward tiles (17..64 tokens), 128-token tiles (65..128)
     (100, 200, 320, 8, False, torch.float32),   # ragged M and N, fp32 absmax and factors
     (48, 256, 512, 128, True, torch.bfloat16),  # r = 128 (8 rank chunks), split
-    (128, 384, 4096, 16, True, torch.bfloat16), # two token tiles, split
+    (128, 384, 4096, 16, True, torch.bfloat16), # one full 128-token tile, split
+    (65, 256, 512, 16, True, torch.bfloat16),   # 128-token tiles with one row past 64
+    (127, 200, 1088, 16, False, torch.float32), # 128-token tiles, ragged N, dx ragged in N and K
+    (96, 1024, 4096, 64, True, torch.bfloat16), # 128-token tiles, r = 64, split-K forward and dx
 ]
 
 
@@ -300,6 +303,7 @@ BLOCK128_CASES = [
     (1, 256, 1024, 16, True, torch.bfloat16),   # decode GEMV
     (16, 200, 4352, 16, False, torch.bfloat16), # GEMV, second round, ragged N
     (64, 256, 512, 8, True, torch.bfloat16),    # 64-token forward tile, split
+    (120, 256, 1024, 16, True, torch.bfloat16), # 128-token forward and dx tiles
     (300, 384, 768, 16, True, torch.bfloat16),  # 256-token GEMM, ragged M
     (77, 1024, 2048, 16, False, torch.bfloat16),# split-K forward and dx
     (300, 200, 384, 8, True, torch.bfloat16),   # ragged N: guarded tile, tiled dx
@@ -363,7 +367,8 @@ F16_CASES = [
     (5, 64, 14336, 64, True, torch.float16, 64),    # GEMV: 3.5 rounds, r = 64
     (100, 200, 320, 8, False, torch.float32, 64),   # 64-token forward, ragged M and N
     (64, 256, 1024, 16, True, torch.float16, 64),   # 64-token forward with split-K, 64-token dx
-    (128, 384, 4096, 16, True, torch.float16, 64),  # two 64-token tiles, split-K
+    (128, 384, 4096, 16, True, torch.float16, 64),  # one 128-token tile, split-K
+    (90, 200, 1088, 8, False, torch.float32, 64),   # 128-token tiles, ragged N and K, fp32 factors
     (300, 384, 384, 16, True, torch.float16, 64),   # 256-token GEMM, ragged M
     (300, 200, 320, 8, False, torch.float32, 64),   # ragged N: guarded tile, fp32-path dx
     (512, 256, 640, 64, True, torch.float16, 64),   # r = 64
