@@ -460,8 +460,7 @@ constexpr int kSmThreads = 256;
 // others return) each form one u slice tile -- token group, rank tile and
 // contraction slice -- from x and A; every tile workgroup writes its fp32
 // partial of x W^^T for its contraction slice (no bypass), and the next
-// launch forms y = RN(fmaf(s, sum_j u_j B_nj, sum of the slices)).  The
-// fused form runs with 64-token tiles only.
+// launch forms y = RN(fmaf(s, sum_j u_j B_nj, sum of the slices)).
 template <int BM, typename AT, typename LT, bool DQ, bool FUSED>
 __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ packed, BlockScales sc,
@@ -469,7 +468,6 @@ __global__ __launch_bounds__(kSmThreads) void k_gemm_fwd_small(
     float s, uint16_t *__restrict__ y, float *__restrict__ part, int nsplit,
     const LT *__restrict__ A, float *__restrict__ upart, int uc, int MT, Dropout dr) {
   static_assert(BM == 64 || BM == 128, "token tiles of 64 or 128");
-  static_assert(!FUSED || BM == 64, "the fused form has 64-token tiles");
   constexpr int MI = BM / 32;                // 32-token MFMA tiles per wave
   constexpr int XR = BM * 8 / kSmThreads;    // 16-byte activation chunks per lane per step
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * kRowBytes];
@@ -1108,10 +1106,13 @@ int launch_gemm_fwd(const void *xv, int act_dtype, int64_t M, const uint8_t *pac
   return QL_OK;
 }
 
-// Up to 64 tokens the u slices and the slice sum with the bypass (two
-// launches) beat u in launches of its own plus a split-K sum; from 96 tokens
-// on the fp32 partials of every slice cost more than they save.
-bool gemm_fwd_fused_preferred(int64_t M) { return M > 16 && M <= 64; }
+// Up to 128 tokens (the few-token tiles) the u slices and the slice sum with
+// the bypass (two launches) beat u in launches of its own plus a split-K sum:
+// measured at 65-128 tokens with 128-token tiles, the fused form is 10-16 %
+// faster on the 8B MLP's down shape (4096x14336, the long contraction whose
+// u costs most) and within 2 % either way on the gate shape (14336x4096).
+constexpr int64_t kFusedMaxM = 128;
+bool gemm_fwd_fused_preferred(int64_t M) { return M > 16 && M <= kFusedMaxM; }
 
 size_t gemm_fwd_fused_partial_floats(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (!gemm_fwd_fused_preferred(M)) return 0;
@@ -1125,24 +1126,28 @@ int launch_gemm_fwd_fused(const void *xv, int act_dtype, int64_t M, const uint8_
   const uint16_t *x = (const uint16_t *)xv;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   const bool dq = sc.absmax == nullptr;
-  const int64_t G = ((M + kSmBM - 1) / kSmBM) * ((N + kSmBN - 1) / kSmBN);
+  const int bm = fwd_small_bm(M);
+  const int64_t G = ((M + bm - 1) / bm) * ((N + kSmBN - 1) / kSmBN);
   const int S = fwd_split(M, N, K);
   const USlices us = u_slices(K);
   const int MT = (int)((M + 15) / 16), JT = (r + 15) / 16;
   float *upart = part + (size_t)S * M * N;
   const dim3 grid((unsigned)(G + (int64_t)us.U * JT * MT), (unsigned)S);
-#define QL_FWF(LT, DQV)                                                                          \
-  hipLaunchKernelGGL((k_gemm_fwd_small<kSmBM, AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream, \
+#define QL_FWF(BMV, LT, DQV)                                                                     \
+  hipLaunchKernelGGL((k_gemm_fwd_small<BMV, AT, LT, DQV, true>), grid, dim3(kSmThreads), 0, stream, \
                      x, M, packed, sc, N, K, (const float *)nullptr, (const LT *)B, r, s,         \
                      (uint16_t *)nullptr, part, S, (const LT *)A, upart, us.uc, MT, dr)
+#define QL_FWF_BM(LT, DQV) \
+  do { if (bm == 64) QL_FWF(64, LT, DQV); else QL_FWF(128, LT, DQV); } while (0)
   with_half(act_dtype, [&](auto *tag) {
     using AT = elem_of<decltype(tag)>;
     if (lora_dtype == QL_F32) {
-      if (dq) QL_FWF(float, true); else QL_FWF(float, false);
+      if (dq) QL_FWF_BM(float, true); else QL_FWF_BM(float, false);
     } else {
-      if (dq) QL_FWF(AT, true); else QL_FWF(AT, false);
+      if (dq) QL_FWF_BM(AT, true); else QL_FWF_BM(AT, false);
     }
   });
+#undef QL_FWF_BM
 #undef QL_FWF
   QL_HIP_CHECK_LAUNCH();
   return launch_fwd_finish(act_dtype, lora_dtype, part, S, upart, us.U, M, N, r, B, s, y, u_save,

@@ -111,7 +111,7 @@ int launch_tiny_bwd(const void *dy, const void *x, int64_t M, const uint8_t *pac
                     int lora_dtype, int32_t r, float s, const float *u_saved, void *dx, float *dA,
                     float *dB, bool accumulate, hipStream_t stream);
 size_t gemm_fwd_partial_floats(int64_t M, int64_t N, int64_t K);
-// Few-token forward (17..64 tokens, 16-bit activations) in two launches: the
+// Few-token forward (17..128 tokens, 16-bit activations) in two launches: the
 // 64-token GEMM tiles plus u slice workgroups, then the slice sum with the
 // bypass (part: gemm_fwd_fused_partial_floats floats); drop as for the
 // decode forward.

@@ -18,6 +18,9 @@ from tests.helpers import (BF16_TOL, F16_TOL, U_BF16, U_F16, assert_f32_close,
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
+# a 16-bit forward of up to this many tokens computes u in workgroups of its
+# own launch and sums the slices of x W^^T with the bypass in a second one
+FUSED_MAX_M = 128
 
 
 def _say(*a):
@@ -209,13 +212,13 @@ def _layer_case(orc, M, N, K, r, dq, act, lora, alpha=32.0, seed_cfg=90, dy_ones
            "dx": dx.float().cpu().numpy()[sel], "dA": dA.cpu().numpy(), "dB": dB.cpu().numpy()}
     ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": dA_ref, "dB": dB_ref}
     # the saved-u backward is the same computation.  A 16-bit forward of up
-    # to 64 tokens (the decode forward, M <= 16, and the few-token forward)
+    # to 128 tokens (the decode forward, M <= 16, and the few-token forward)
     # computes u in workgroups of its own launch, in another fp32 summation
     # order than the backward's recomputation; the backward rounds u to 16
     # bits for its matrix ops, where the two orders can round to neighbouring
     # values: there the saved-u dA and dB are held to the oracle at the
     # layer's tolerance.  dx does not depend on u.
-    if act != torch.float32 and M <= 64:
+    if act != torch.float32 and M <= FUSED_MAX_M:
         tol = F16_TOL if act == torch.float16 else BF16_TOL
         assert rel_err(dA2.cpu().numpy(), dA_ref) <= tol
         assert rel_err(dB2.cpu().numpy(), dB_ref) <= tol
@@ -435,7 +438,7 @@ def test_fp16_tiny_weights_dequantise_to_subnormals(orc):
 def test_forward_given_u(orc, M, N, K, r, act, lora, fwd_splits):
     """qlora_linear_fwd_u with the u_save of qlora_linear_fwd reproduces its y
     (bit for bit where both run the same unsplit kernel; within rounding where
-    the forward splits the contraction or, up to 64 tokens, sums the slices
+    the forward splits the contraction or, up to 128 tokens, sums the slices
     of x W^^T and adds the bypass in a second launch) and the oracle's y."""
     _say(f"fwd_u M={M} N={N} K={K} r={r} act={act} lora={lora}")
     t = si.linear_inputs(91, M, N, K, r, act_dtype=act, w_dtype=act, lora_dtype=lora, sub=M + r)
@@ -445,7 +448,7 @@ def test_forward_given_u(orc, M, N, K, r, act, lora, fwd_splits):
     y = q.qlora_linear_fwd(d["x"], W, d["A"], d["B"], 32.0, u_save=u)
     y_u = q.qlora_linear_fwd_u(d["x"], W, u, d["B"], 32.0)
     torch.cuda.synchronize()
-    if (M > 64 and not fwd_splits) or act == torch.float32:
+    if (M > FUSED_MAX_M and not fwd_splits) or act == torch.float32:
         np.testing.assert_array_equal(y_u.float().cpu().numpy(), y.float().cpu().numpy())
     st = orc.quantize_nf4(host(t["W"]), double_quant=True)
     w_hat = orc.dequantize(st).reshape(N, K)
