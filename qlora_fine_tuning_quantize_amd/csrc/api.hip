@@ -454,15 +454,22 @@ static int linear_bwd(const void *dy, const void *x, int32_t act_dtype, int64_t 
   // g = s dy B: Q(j, c) = B[c][j]
   st = launch_lora_rows_ws(dy, act_dtype, M, N, B, lora_dtype, 1, r, r, sc_lora, g, rows_partial, s);
   if (st) return st;
-  // dB[n][j] = s sum_m dy[m][n] u[m][j]
+  // dB[n][j] = s sum_m dy[m][n] u[m][j] and dA[j][k] = sum_m g[m][j] x[m][k]
+  // (x after dropout: keep / (1 - p) times x); without dropout both in one
+  // launch
   ColsReduce red_dB, red_dA;
-  st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s, accumulate,
-                        nullptr, &red_dB);
-  if (st) return st;
-  // dA[j][k] = sum_m g[m][j] x[m][k] (x after dropout: keep / (1 - p) times x)
-  st = launch_lora_cols(g, M, r, x, act_dtype, K, drop ? dscale : 1.0f, false, dA, cols_partial2,
-                        s, accumulate, drop, &red_dA);
-  if (st) return st;
+  if (!drop) {
+    st = launch_lora_cols2(u, dy, N, sc_lora, true, dB, cols_partial, g, x, K, 1.0f, false, dA,
+                           cols_partial2, M, r, act_dtype, s, accumulate, &red_dB, &red_dA);
+    if (st) return st;
+  } else {
+    st = launch_lora_cols(u, M, r, dy, act_dtype, N, sc_lora, true, dB, cols_partial, s,
+                          accumulate, nullptr, &red_dB);
+    if (st) return st;
+    st = launch_lora_cols(g, M, r, x, act_dtype, K, dscale, false, dA, cols_partial2, s,
+                          accumulate, drop, &red_dA);
+    if (st) return st;
+  }
   st = launch_reduce_cols(red_dB, red_dA, s);
   if (st) return st;
   if (!dx) return QL_OK;

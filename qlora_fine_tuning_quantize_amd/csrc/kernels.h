@@ -64,6 +64,14 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
                      float scale, bool out_c_major, float *out, float *partial,
                      hipStream_t stream, bool accumulate = false,
                      const Dropout *drop = nullptr, ColsReduce *pending = nullptr);
+// Two such products over the same M tokens and rank r (no dropout), a and b,
+// in one launch when both take the matrix-core kernel (else one launch each);
+// their slice reductions are described in pending_a / pending_b.
+int launch_lora_cols2(const float *Ra, const void *Pa, int64_t Ca, float scale_a, bool cmaj_a,
+                      float *out_a, float *partial_a, const float *Rb, const void *Pb, int64_t Cb,
+                      float scale_b, bool cmaj_b, float *out_b, float *partial_b, int64_t M,
+                      int32_t r, int p_dtype, hipStream_t stream, bool accumulate,
+                      ColsReduce *pending_a, ColsReduce *pending_b);
 // one launch for up to two pending reductions (empty ones are skipped)
 int launch_reduce_cols(const ColsReduce &a, const ColsReduce &b, hipStream_t stream);
 

@@ -550,20 +550,44 @@ struct ColsOut {
   int c_major, accumulate;
 };
 
+// One product R^T P of a launch: its operands, output, token runs per
+// workgroup (nsub) and column tiles; its workgroups are tiles x slices, the
+// column tile fastest.
+struct ColsJob {
+  const float *R;
+  const void *P;
+  int64_t C;
+  float *partial;
+  ColsOut co;
+  int nsub;
+  int64_t tiles;
+};
+
+// grid.x = blocks_a + the workgroups of job b (none when b is empty): the
+// first blocks_a workgroups take job a, the rest job b.  Both jobs share M,
+// r and the dropout of the launch.
 template <int TM, int JT, typename AT, bool RVEC, bool DROP>
-__global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, int64_t M,
-                                                   int32_t r, const AT *__restrict__ P,
-                                                   int64_t C, float *__restrict__ partial,
-                                                   Dropout dr, ColsOut co, int nsub) {
+__global__ __launch_bounds__(256) void k_cols_mfma(ColsJob ja, ColsJob jb, int64_t blocks_a,
+                                                   int64_t M, int32_t r, Dropout dr) {
   constexpr int JW = JT * 16;
   constexpr int RST = 2 * TM + 16;  // bytes per staged rank row
   __shared__ __attribute__((aligned(16))) uint8_t ps[TM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t rs[JW * RST];
+  const bool second = (int64_t)blockIdx.x >= blocks_a;  // uniform
+  const ColsJob &job = second ? jb : ja;
+  const float *__restrict__ R = job.R;
+  const AT *__restrict__ P = static_cast<const AT *>(job.P);
+  const int64_t C = job.C;
+  float *__restrict__ partial = job.partial;
+  const ColsOut co = job.co;
+  const int nsub = job.nsub;
+  const int64_t blk = second ? (int64_t)blockIdx.x - blocks_a : (int64_t)blockIdx.x;
+  const int64_t bx = blk % job.tiles, by = blk / job.tiles;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int li = lane & 15, q = lane >> 4;
-  const int64_t ct0 = (int64_t)blockIdx.x * kMColsTile;
+  const int64_t ct0 = bx * kMColsTile;
   // the workgroup's token slice: nsub runs of TM tokens, one after another
-  const int64_t ms0 = (int64_t)blockIdx.y * TM * nsub;
+  const int64_t ms0 = by * TM * nsub;
 
   // R with r % 4 == 0 (RVEC): load group g of a thread covers TG consecutive
   // tokens x 4 ranks (TG loads of 16 bytes) and is staged as 4 rank rows of
@@ -740,7 +764,7 @@ __global__ __launch_bounds__(256) void k_cols_mfma(const float *__restrict__ R, 
           const int64_t o = co.c_major ? c * r + j : (int64_t)j * C + c;
           co.out[o] = co.accumulate ? co.out[o] + co.scale * sum : co.scale * sum;
         } else {
-          partial[((int64_t)blockIdx.y * r + j) * C + c] = acc[jt][v];
+          partial[(by * r + j) * C + c] = acc[jt][v];
         }
       }
     }
@@ -882,6 +906,42 @@ size_t lora_cols_partial_floats(int64_t M, int64_t C, int32_t r) {
   return (size_t)(s1 > s2 ? s1 : s2) * (size_t)r * (size_t)C;
 }
 
+// The matrix-core form of one product, as a job of a k_cols_mfma launch.
+static ColsJob mcols_job(const float *R, int64_t M, const void *P, int64_t C, float scale,
+                         bool out_c_major, float *out, float *partial, bool accumulate, int &S) {
+  const MColsPlan mp = mcols_plan(M, C);
+  S = mp.S;
+  // one token slice: the kernel writes the result, no reduction launch
+  const ColsOut co{S == 1 ? out : nullptr, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0};
+  return ColsJob{R, P, C, partial, co, mp.nsub, (C + kMColsTile - 1) / kMColsTile};
+}
+
+// One k_cols_mfma launch over jobs a and b (b.tiles == 0: a alone).
+static void launch_mcols(const ColsJob &a, int Sa, const ColsJob &b, int Sb, int64_t M, int32_t r,
+                         int p_dtype, const Dropout &dr, bool drop, hipStream_t stream) {
+  const int64_t blocks_a = a.tiles * Sa;
+  const dim3 grid((unsigned)(blocks_a + b.tiles * Sb));
+  const bool rvec = r % 4 == 0;
+#define QL_COLS_M(JTV, RV, DRV)                                                               \
+  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, AT, RV, DRV>), grid, dim3(256), 0, stream, a, \
+                     b, blocks_a, M, r, dr)
+#define QL_COLS_JT(JTV)                                                                          \
+  do {                                                                                           \
+    if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \
+    else { if (drop) QL_COLS_M(JTV, false, true); else QL_COLS_M(JTV, false, false); }           \
+  } while (0)
+  const int jt = rows_jt(r);
+  with_half(p_dtype, [&](auto *tag) {
+    using AT = elem_of<decltype(tag)>;
+    if (jt == 1) QL_COLS_JT(1);
+    else if (jt == 2) QL_COLS_JT(2);
+    else if (jt == 4) QL_COLS_JT(4);
+    else QL_COLS_JT(8);
+  });
+#undef QL_COLS_JT
+#undef QL_COLS_M
+}
+
 int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_dtype, int64_t C,
                      float scale, bool out_c_major, float *out, float *partial,
                      hipStream_t stream, bool accumulate, const Dropout *drop,
@@ -891,30 +951,9 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
   int S;
   const Dropout dr = drop ? *drop : Dropout{0u, 0u, 0u};
   if (cols_use_mfma(p_dtype, C)) {
-    const MColsPlan mp = mcols_plan(M, C);
-    S = mp.S;
-    const dim3 grid((unsigned)((C + kMColsTile - 1) / kMColsTile), (unsigned)S);
-    // one token slice: the kernel writes the result, no reduction launch
-    const ColsOut co{S == 1 ? out : nullptr, scale, out_c_major ? 1 : 0, accumulate ? 1 : 0};
-    const bool rvec = r % 4 == 0;
-#define QL_COLS_M(JTV, RV, DRV)                                                               \
-  hipLaunchKernelGGL((k_cols_mfma<kMColsTM, JTV, AT, RV, DRV>), grid, dim3(256), 0, stream, R, \
-                     M, r, (const AT *)P, C, partial, dr, co, mp.nsub)
-#define QL_COLS_JT(JTV)                                                                          \
-  do {                                                                                           \
-    if (rvec) { if (drop) QL_COLS_M(JTV, true, true); else QL_COLS_M(JTV, true, false); }        \
-    else { if (drop) QL_COLS_M(JTV, false, true); else QL_COLS_M(JTV, false, false); }           \
-  } while (0)
-    const int jt = rows_jt(r);
-    with_half(p_dtype, [&](auto *tag) {
-      using AT = elem_of<decltype(tag)>;
-      if (jt == 1) QL_COLS_JT(1);
-      else if (jt == 2) QL_COLS_JT(2);
-      else if (jt == 4) QL_COLS_JT(4);
-      else QL_COLS_JT(8);
-    });
-#undef QL_COLS_JT
-#undef QL_COLS_M
+    const ColsJob a = mcols_job(R, M, P, C, scale, out_c_major, out, partial, accumulate, S);
+    launch_mcols(a, S, ColsJob{nullptr, nullptr, 0, nullptr, ColsOut{nullptr, 0.0f, 0, 0}, 1, 0}, 0,
+                 M, r, p_dtype, dr, drop != nullptr, stream);
     QL_HIP_CHECK_LAUNCH();
     if (S == 1) return QL_OK;
   } else {
@@ -938,6 +977,32 @@ int launch_lora_cols(const float *R, int64_t M, int32_t r, const void *P, int p_
     return QL_OK;
   }
   return launch_reduce_cols(job, ColsReduce{nullptr, 0, 0, 0, 0.0f, 0, 0, nullptr}, stream);
+}
+
+int launch_lora_cols2(const float *Ra, const void *Pa, int64_t Ca, float scale_a, bool cmaj_a,
+                      float *out_a, float *partial_a, const float *Rb, const void *Pb, int64_t Cb,
+                      float scale_b, bool cmaj_b, float *out_b, float *partial_b, int64_t M,
+                      int32_t r, int p_dtype, hipStream_t stream, bool accumulate,
+                      ColsReduce *pending_a, ColsReduce *pending_b) {
+  if (!(cols_use_mfma(p_dtype, Ca) && cols_use_mfma(p_dtype, Cb) && Ca > 0 && Cb > 0)) {
+    int st = launch_lora_cols(Ra, M, r, Pa, p_dtype, Ca, scale_a, cmaj_a, out_a, partial_a, stream,
+                              accumulate, nullptr, pending_a);
+    if (st) return st;
+    return launch_lora_cols(Rb, M, r, Pb, p_dtype, Cb, scale_b, cmaj_b, out_b, partial_b, stream,
+                            accumulate, nullptr, pending_b);
+  }
+  int Sa, Sb;
+  const ColsJob a = mcols_job(Ra, M, Pa, Ca, scale_a, cmaj_a, out_a, partial_a, accumulate, Sa);
+  const ColsJob b = mcols_job(Rb, M, Pb, Cb, scale_b, cmaj_b, out_b, partial_b, accumulate, Sb);
+  launch_mcols(a, Sa, b, Sb, M, r, p_dtype, Dropout{0u, 0u, 0u}, false, stream);
+  QL_HIP_CHECK_LAUNCH();
+  *pending_a = Sa == 1 ? ColsReduce{nullptr, 0, 0, 0, 0.0f, 0, 0, nullptr}
+                       : ColsReduce{partial_a, Sa, r, Ca, scale_a, cmaj_a ? 1 : 0,
+                                    accumulate ? 1 : 0, out_a};
+  *pending_b = Sb == 1 ? ColsReduce{nullptr, 0, 0, 0, 0.0f, 0, 0, nullptr}
+                       : ColsReduce{partial_b, Sb, r, Cb, scale_b, cmaj_b ? 1 : 0,
+                                    accumulate ? 1 : 0, out_b};
+  return QL_OK;
 }
 
 }  // namespace qlora
