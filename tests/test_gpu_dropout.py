@@ -125,6 +125,7 @@ def test_layer_dropout_parity(orc, M, N, K, r, dq, lora, p):
 @pytest.mark.parametrize("M,N,K,r,dq,lora,p", [
     (3, 256, 256, 8, True, torch.float16, 0.05),      # decode forward
     (40, 256, 512, 8, True, torch.float16, 0.05),     # few-token forward
+    (100, 256, 1024, 16, True, torch.float16, 0.1),   # 128-token fused forward and dx tiles
     (300, 384, 384, 16, True, torch.float16, 0.05),   # 256-token tiles, ragged M
     (64, 64, 128, 5, False, torch.float32, 0.5),      # 64-token tiles, fp32 factors
     (130, 4096, 512, 16, True, torch.float16, 0.2),   # split-K dx

@@ -45,6 +45,10 @@ def _both(t, W, alpha):
     # sum with the bypass; then fewer tokens, ragged, in fp16
     ((48, 2048, 4096, 16, True, torch.bfloat16, torch.bfloat16),
      (20, 200, 1024, 8, False, torch.float16, torch.float32)),
+    # 128-token tiles with u slices in the same launch (65..128 tokens), then
+    # a decode-sized call
+    ((96, 1024, 4096, 16, True, torch.bfloat16, torch.bfloat16),
+     (3, 256, 512, 8, True, torch.bfloat16, torch.bfloat16)),
 ])
 def test_noalloc_matches_fwd_twice(first, second):
     for i, (M, N, K, r, dq, act, lora) in enumerate((first, second)):
