@@ -66,8 +66,8 @@ def layer_flops(M, N, K, r):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
-        with open(os.path.join(ROOT, "qlora_fine_tuning_quantize_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/gemm.hip", "csrc/common.h", "build.py"):
+        with open(os.path.join(ROOT, "qlora_fine_tuning_quantize_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
