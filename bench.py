@@ -13,7 +13,7 @@ In the same run (reported beside the step):
   rows         each step row per projection, timed through the entry points
   mlp_8b       the same step on an 8B-shaped MLP (gate/up 14336x4096, down
                4096x14336, 2048 tokens, r=16, alpha=32)
-  few_tokens   the 8B gate projection at 17 .. 512 tokens, forward and backward
+  few_tokens   the 8B gate (and down) projection at 17 .. 512 tokens, forward and backward
   dropout      the 8B gate projection with LoRA dropout 0.05 against without
   formats      the 8B gate projection in each storage variant (blocks of 64
                or 128, with or without double quantisation)
@@ -395,36 +395,41 @@ def bench_mlp8b(q, si, dev, steps, warmup):
 
 def bench_few_tokens(q, si, dev, token_counts=(17, 64, 128, 256, 512)):
     """The gate projection (14336x4096, NF4 + double quant, r=16) with few
-    tokens: forward (u + y) and backward (g, dA, dB, dx) per call, eager."""
+    tokens: forward (u + y) and backward (g, dA, dB, dx) per call, eager;
+    the down projection (4096x14336, the long contraction) under "down"."""
     c = si.MLP_8B
-    N, K = c["projs"]["gate"]
     r, alpha = c["r"], c["alpha"]
-    W = None
     out = {"workload": "gate projection 14336x4096 NF4 + double quant, r=16, alpha=32, bf16, "
-                       "forward and backward per call (eager, every launch of the call)",
+                       "forward and backward per call (eager, every launch of the call); "
+                       "down: the down projection 4096x14336, the same calls",
            "unit": "us"}
-    for M in token_counts:
-        t = si.linear_inputs(c["config"], M, N, K, r, device=dev)
-        if W is None:
-            W = q.nf4_quantize(t["W"], double_quant=True)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        u = torch.empty((M, r), dtype=torch.float32, device=dev)
-        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        dA = torch.empty((r, K), dtype=torch.float32, device=dev)
-        dB = torch.empty((N, r), dtype=torch.float32, device=dev)
-        wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
-        wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, dev)
-        tf = timed(lambda: q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], alpha, y=y, u_save=u,
-                                              ws=wsf), 30, 3)
-        tb = timed(lambda: q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], alpha,
-                                              u_saved=u, dx=dx, dA=dA, dB=dB, ws=wsb), 30, 3)
-        fl = layer_flops(M, N, K, r)
-        out[f"M{M}"] = {"fwd_us": round(tf * 1e3, 2), "bwd_us": round(tb * 1e3, 2),
-                        "fwd_bwd_TFLOPs": round(fl / ((tf + tb) * 1e-3) / 1e12, 1),
-                        "fwd_packed_weight_GBps": round(W.storage_bytes() / (tf * 1e-3) / 1e9, 1)}
-        log(f"few tokens M={M}: fwd {tf * 1e3:.1f} us, bwd {tb * 1e3:.1f} us")
-        del t, y, u, dx, dA, dB, wsf, wsb
-    del W
+    for proj in ("gate", "down"):
+        N, K = c["projs"][proj]
+        dst = out if proj == "gate" else out.setdefault("down", {})
+        W = None
+        for M in token_counts:
+            t = si.linear_inputs(c["config"], M, N, K, r, device=dev)
+            if W is None:
+                W = q.nf4_quantize(t["W"], double_quant=True)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            u = torch.empty((M, r), dtype=torch.float32, device=dev)
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+            dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+            wsf = q.workspace(q.QL_OP_FWD, M, N, K, r, dev)
+            wsb = q.workspace(q.QL_OP_BWD, M, N, K, r, dev)
+            tf = timed(lambda: q.qlora_linear_fwd(t["x"], W, t["A"], t["B"], alpha, y=y, u_save=u,
+                                                  ws=wsf), 30, 3)
+            tb = timed(lambda: q.qlora_linear_bwd(t["dy"], t["x"], W, t["A"], t["B"], alpha,
+                                                  u_saved=u, dx=dx, dA=dA, dB=dB, ws=wsb), 30, 3)
+            fl = layer_flops(M, N, K, r)
+            dst[f"M{M}"] = {"fwd_us": round(tf * 1e3, 2), "bwd_us": round(tb * 1e3, 2),
+                            "fwd_bwd_TFLOPs": round(fl / ((tf + tb) * 1e-3) / 1e12, 1),
+                            "fwd_packed_weight_GBps": round(W.storage_bytes() / (tf * 1e-3) / 1e9,
+                                                            1)}
+            log(f"few tokens {proj} M={M}: fwd {tf * 1e3:.1f} us, bwd {tb * 1e3:.1f} us")
+            del t, y, u, dx, dA, dB, wsf, wsb
+        del W
     torch.cuda.empty_cache()
     return out
 
